@@ -1,0 +1,168 @@
+"""fp64 CPU oracle of the sparse-MoE layer forward (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
+package; the product path never imports it.  The arithmetic lives in
+``moe_oracle.c`` (plain loops, fp64, OpenMP across independent tokens) and
+this module only marshals numpy arrays to it.  ``build()`` compiles it with
+gcc (no fast-math: sums are never reassociated).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+ACT = {"gelu": 0, "relu": 1}
+DTYPE = {"f32": 0, "bf16": 1}
+
+
+class _Cfg(C.Structure):
+    _fields_ = [("T", C.c_int64), ("d", C.c_int32), ("F", C.c_int32), ("E", C.c_int32),
+                ("k", C.c_int32), ("act", C.c_int32), ("dtype", C.c_int32),
+                ("capacity", C.c_int32), ("renormalize", C.c_int32), ("Fs", C.c_int32)]
+
+
+def build() -> str:
+    """Compile liboracle.so from moe_oracle.c (always recompiles)."""
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+           "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = C.CDLL(_LIB)
+        P = C.c_void_p
+        lib.orc_route.argtypes = [C.POINTER(_Cfg), P, P, P, P, P, P, P, P, P, P, P]
+        lib.orc_dispatch.argtypes = [C.POINTER(_Cfg), P, P, P, P, P, P]
+        lib.orc_experts.argtypes = [C.POINTER(_Cfg)] + [P] * 13 + [C.c_int64, P]
+        lib.orc_expert_row.argtypes = [C.POINTER(_Cfg)] + [P] * 9 + [C.c_int64, C.c_int32,
+                                                                     C.c_double, P]
+        for f in (lib.orc_route, lib.orc_dispatch, lib.orc_experts, lib.orc_expert_row):
+            f.restype = C.c_int
+        _lib = lib
+    return _lib
+
+
+def _cfg(shape, T: Optional[int] = None) -> _Cfg:
+    return _Cfg(shape.T if T is None else T, shape.d, shape.F, shape.E, shape.k,
+                ACT[shape.act], DTYPE[shape.dtype], shape.capacity, shape.renormalize,
+                shape.Fs)
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def route(shape, inp, *, with_probs: bool = True) -> dict:
+    """Routing, capacity and statistics for every token of ``inp``."""
+    lib = _load()
+    T, E, k = shape.T, shape.E, shape.k
+    r = dict(topk_idx=np.zeros((T, k), np.int32), topk_w=np.zeros((T, k), np.float64),
+             probs=np.zeros((T, E), np.float64) if with_probs else None,
+             counts=np.zeros(E, np.int32), kept=np.zeros(E, np.int32),
+             keep=np.zeros((T, k), np.int32), mean_prob=np.zeros(E, np.float64),
+             balance=np.zeros(1, np.float64))
+    c = _cfg(shape)
+    rc = lib.orc_route(C.byref(c), _p(inp["x"]), _p(inp["Wg"]), _p(inp["bg"]),
+                       _p(r["topk_idx"]), _p(r["topk_w"]), _p(r["probs"]), _p(r["counts"]),
+                       _p(r["kept"]), _p(r["keep"]), _p(r["mean_prob"]), _p(r["balance"]))
+    if rc != 0:
+        raise ValueError("orc_route failed")
+    r["balance"] = float(r["balance"][0])
+    return r
+
+
+def dispatch(shape, topk_idx: np.ndarray, keep: np.ndarray) -> dict:
+    """Expert-major, token-ascending grouping implied by the routing."""
+    lib = _load()
+    T, E, k = shape.T, shape.E, shape.k
+    nrows = T * k + (T if shape.Fs else 0)
+    d = dict(offsets=np.zeros(E + 2, np.int32), row_token=np.full(max(nrows, 1), -1, np.int32),
+             row_slot=np.full(max(nrows, 1), -1, np.int32), inv=np.zeros((T, k), np.int32))
+    c = _cfg(shape)
+    ti = np.ascontiguousarray(topk_idx, np.int32)
+    kp = np.ascontiguousarray(keep, np.int32)
+    if lib.orc_dispatch(C.byref(c), _p(ti), _p(kp), _p(d["offsets"]), _p(d["row_token"]),
+                        _p(d["row_slot"]), _p(d["inv"])) != 0:
+        raise ValueError("orc_dispatch failed")
+    n = int(d["offsets"][E + 1])
+    d["row_token"], d["row_slot"] = d["row_token"][:n], d["row_slot"][:n]
+    return d
+
+
+def experts(shape, inp, rt: dict, tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Layer output rows y[len(tokens), d] in fp64 (all tokens when None)."""
+    lib = _load()
+    toks = np.arange(shape.T, dtype=np.int64) if tokens is None else \
+        np.ascontiguousarray(tokens, dtype=np.int64)
+    y = np.zeros((len(toks), shape.d), np.float64)
+    c = _cfg(shape)
+    tw = np.ascontiguousarray(rt["topk_w"], np.float64)
+    rc = lib.orc_experts(C.byref(c), _p(inp["x"]), _p(inp["W1"]), _p(inp["b1"]), _p(inp["W2"]),
+                         _p(inp["b2"]), _p(inp.get("Ws1")), _p(inp.get("bs1")),
+                         _p(inp.get("Ws2")), _p(inp.get("bs2")),
+                         _p(np.ascontiguousarray(rt["topk_idx"], np.int32)), _p(tw),
+                         _p(np.ascontiguousarray(rt["keep"], np.int32)), _p(toks),
+                         len(toks), _p(y))
+    if rc != 0:
+        raise ValueError("orc_experts failed")
+    return y
+
+
+def expert_row(shape, inp, t: int, e: int, g: float) -> np.ndarray:
+    """g * E_e(x_t) for one token (e = -1: the shared expert)."""
+    lib = _load()
+    out = np.zeros(shape.d, np.float64)
+    c = _cfg(shape)
+    rc = lib.orc_expert_row(C.byref(c), _p(inp["x"]), _p(inp["W1"]), _p(inp["b1"]),
+                            _p(inp["W2"]), _p(inp["b2"]), _p(inp.get("Ws1")),
+                            _p(inp.get("bs1")), _p(inp.get("Ws2")), _p(inp.get("bs2")),
+                            int(t), int(e), float(g), _p(out))
+    if rc != 0:
+        raise ValueError("orc_expert_row failed")
+    return out
+
+
+def forward(shape, inp, tokens=None) -> dict:
+    """Whole layer: routing for all tokens, outputs for ``tokens`` (all if None)."""
+    rt = route(shape, inp)
+    rt["y"] = experts(shape, inp, rt, tokens)
+    return rt
+
+
+def combine(shape, y_rows: np.ndarray, inv: np.ndarray, offsets: np.ndarray) -> np.ndarray:
+    """Gather-combine of expert rows in fp64: y[t] = sum_i y_rows[inv[t,i]] (+ shared row).
+
+    Plain loops over slots in ascending order, then the shared row (rows start
+    at offsets[E]).  Small numpy helper; tokens independent."""
+    T, k, E = shape.T, shape.k, shape.E
+    y = np.zeros((T, shape.d), np.float64)
+    yr = y_rows.astype(np.float64)
+    for i in range(k):
+        r = inv[:, i]
+        m = r >= 0
+        y[m] += yr[r[m]]
+    if shape.Fs:
+        base = int(offsets[E])
+        y += yr[base:base + T]
+    return y
