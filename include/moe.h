@@ -1,0 +1,167 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer forward.
+ *
+ * The layer (pages: botmartz "Mixture of Experts (MoE) and Mixtral", sections
+ * "MoE Architecture" and "Expert Routing"; roadtointelligence "Mixture of
+ * Experts", router formula and output equation; matteuscruz "Mixture of
+ * Experts", "Architecture: router + experts" and "Load balancing"):
+ *
+ *   l = x W_g^T + b_g                          router scores, fp32
+ *   p = softmax(l); top-k of p                 slots in descending order,
+ *                                              lowest expert index on ties
+ *   g_i = p_{e_i} / sum_j p_{e_j}              renormalised gates
+ *   capacity: per expert the first C (token, slot) pairs in token order are
+ *             kept, the rest dropped (they contribute zero)
+ *   E_e(x) = W2[e] act(W1[e] x + b1[e]) + b2[e]   act = exact GELU or ReLU
+ *   y = sum_{kept i} g_i E_{e_i}(x)  (+ S(x), an always-on shared expert)
+ *
+ * Conventions for every entry point:
+ *  - All array arguments are DEVICE pointers, row-major and contiguous, owned
+ *    by the caller.  The library allocates and frees nothing, keeps no state
+ *    between calls and is re-entrant; two calls that share a workspace or an
+ *    output buffer on different streams race.
+ *  - Expert weights use the nn.Linear layout [out, in]: W1 [E, d_ff, d_model],
+ *    W2 [E, d_model, d_ff]; b1 [E, d_ff], b2 [E, d_model].  They, x and y are
+ *    fp32 (MOE_F32) or bf16 (MOE_BF16, raw 16-bit patterns) as cfg->dtype
+ *    says.  Router weight W_g [E, d_model] and bias b_g [E] are always fp32.
+ *    Every bias pointer may be NULL (zero bias).
+ *  - Expert indices are 0-based.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *    enqueued: no call synchronises, reads device memory on the host or
+ *    allocates, so a sequence of calls can be captured in a HIP graph.
+ *  - Arguments are validated before anything is enqueued; a failed check
+ *    returns a negative moe_status and enqueues nothing.  A failed launch
+ *    returns MOE_ERR_HIP (hipGetLastError has the detail).  Nothing is printed.
+ *  - Workspace: ws must be 256-byte aligned device memory of at least
+ *    moe_workspace_bytes(cfg) bytes (one size serves every entry point).  Its
+ *    contents need no initialisation and are garbage after the call.
+ *  - Limits: 1 <= n_experts <= 1024, 1 <= top_k <= min(n_experts, 32),
+ *    d_model, d_ff and shared_d_ff multiples of 8, T * (top_k + 1) < 2^31,
+ *    x / weight / y pointers 16-byte aligned.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null required pointer, bad size, misalignment */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but outside the limits above */
+  MOE_ERR_WORKSPACE = -3,   /* ws NULL, misaligned or smaller than needed */
+  MOE_ERR_HIP = -4          /* a HIP launch failed */
+} moe_status;
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+enum { MOE_ACT_GELU = 0 /* 0.5 z (1 + erf(z / sqrt 2)) */, MOE_ACT_RELU = 1 };
+
+typedef struct {
+  int64_t T;           /* tokens (batch * seq_len, flattened) */
+  int32_t d_model;     /* d */
+  int32_t d_ff;        /* routed expert hidden size F */
+  int32_t n_experts;   /* E */
+  int32_t top_k;       /* k */
+  int32_t act;         /* MOE_ACT_GELU or MOE_ACT_RELU */
+  int32_t dtype;       /* MOE_F32 or MOE_BF16 */
+  int32_t capacity;    /* < 0: unlimited; else max kept rows per routed expert */
+  int32_t renormalize; /* 1: g_i = p_i / sum p over the top-k; 0: g_i = p_i */
+  int32_t shared_d_ff; /* hidden size of the always-on shared expert, 0 = none */
+} moe_config;
+
+typedef struct {
+  const float *Wg, *bg;                /* [E, d] fp32, [E] fp32 or NULL */
+  const void *W1, *b1, *W2, *b2;       /* routed experts, see layout above */
+  const void *Ws1, *bs1, *Ws2, *bs2;   /* shared expert [Fs, d], [Fs], [d, Fs], [d] */
+} moe_weights;
+
+/* Optional per-call outputs of moe_forward; every member may be NULL. */
+typedef struct {
+  int32_t *topk_idx; /* [T, k] chosen experts */
+  float *topk_w;     /* [T, k] gates */
+  int32_t *counts;   /* [E] routed (token, slot) pairs per expert */
+  int32_t *kept;     /* [E] pairs that survived the capacity limit */
+  float *mean_prob;  /* [E] mean router probability over tokens (NaN if T = 0) */
+  float *balance;    /* [1] unbiased variance of mean_prob over experts (NaN if E = 1) */
+} moe_stats;
+
+/* Workspace bytes that every entry point below accepts for this config
+ * (0 on an invalid config). */
+size_t moe_workspace_bytes(const moe_config *cfg);
+
+/*
+ * Router and gating: scores, softmax, top-k, renormalise (botmartz "Expert
+ * Routing"; roadtointelligence router formula, "Tiny example").
+ *   x [T, d] (cfg->dtype); Wg [E, d] fp32; bg [E] fp32 or NULL
+ *   topk_idx [T, k] int32 out; topk_w [T, k] fp32 out
+ *   probs [T, E] fp32 out or NULL: the full softmax
+ *   mean_prob [E] and balance [1] fp32 out or NULL: load statistics
+ *     (botmartz "Load Balancing": mean of the probabilities over tokens and
+ *     the square of their standard deviation over experts)
+ */
+moe_status moe_route(const moe_config *cfg, const void *x, const float *Wg, const float *bg,
+                     int32_t *topk_idx, float *topk_w, float *probs, float *mean_prob,
+                     float *balance, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Dispatch: group (token, slot) pairs by expert under the capacity limit
+ * (matteuscruz "Load balancing", expert capacity buffer; roadtointelligence
+ * "Keeping the experts busy": overflow tokens are dropped).
+ *   topk_idx [T, k] int32 in, values in [0, E).  An out-of-range id is
+ *     dropped (inv = -1); the grouping of the other pairs is then unspecified,
+ *     but nothing is written outside the arrays described here.
+ *   counts [E], kept [E] int32 out
+ *   offsets [E + 2] int32 out: rows of expert e are offsets[e] .. offsets[e+1]-1,
+ *     offsets[E] = routed rows R, offsets[E+1] = R + (shared_d_ff ? T : 0)
+ *   row_token, row_slot [T*k + (shared_d_ff ? T : 0)] int32 out: token and slot
+ *     of each row; rows are expert-major and token-ascending inside an expert;
+ *     the shared expert's rows R + t have token t and slot -1
+ *   inv [T, k] int32 out: row of each (token, slot), -1 if dropped
+ */
+moe_status moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, int32_t *counts,
+                        int32_t *kept, int32_t *offsets, int32_t *row_token, int32_t *row_slot,
+                        int32_t *inv, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Expert MLPs over the grouped rows (botmartz "Expert Routing" expert
+ * networks; codingnowai "Code"; roadtointelligence shared expert):
+ *   y_rows[r, :] = gate_r * (W2[e] act(W1[e] x[row_token[r]] + b1[e]) + b2[e])
+ * with gate_r = topk_w[row_token[r], row_slot[r]] for routed rows and 1 for
+ * shared rows (which use Ws1, bs1, Ws2, bs2).
+ *   x [T, d]; offsets, row_token, row_slot as produced by moe_dispatch;
+ *   topk_w [T, k] fp32; y_rows [T*k + (shared_d_ff ? T : 0), d] fp32 out (only
+ *   the first offsets[E+1] rows are written).
+ */
+moe_status moe_expert_ffn(const moe_config *cfg, const void *x, const moe_weights *w,
+                          const int32_t *offsets, const int32_t *row_token,
+                          const int32_t *row_slot, const float *topk_w, float *y_rows, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/*
+ * Combine: y[t] = sum over slots i = 0..k-1 with inv[t,i] >= 0 of
+ * y_rows[inv[t,i]], then + y_rows[offsets[E] + t] if there is a shared expert,
+ * summed in that order in fp32, no atomics (roadtointelligence output
+ * equation; botmartz "Expert Routing" accumulation into zeros_like(x)).
+ *   y [T, d] out in cfg->dtype.  Needs no workspace.
+ */
+moe_status moe_combine(const moe_config *cfg, const float *y_rows, const int32_t *inv,
+                       const int32_t *offsets, void *y, void *stream);
+
+/*
+ * The whole layer: route, dispatch, expert MLPs, combine.  y [T, d] out in
+ * cfg->dtype; stats may be NULL or have NULL members.
+ */
+moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
+                       moe_stats *stats, void *ws, size_t ws_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -251,3 +251,22 @@ def make_inputs(shape: LayerShape, seed: int, *, margin: float = MARGIN,
     else:
         out.update(Ws1=None, bs1=None, Ws2=None, bs2=None)
     return out
+
+
+def to_device(inp: dict, device="cuda") -> dict:
+    """Copy the arrays of ``make_inputs`` to torch tensors on ``device``.
+
+    bf16 bit patterns become torch.bfloat16 tensors with the same bits; fp32
+    stays fp32; None stays None."""
+    import torch
+
+    out = {}
+    for key in ("x", "Wg", "bg", "W1", "b1", "W2", "b2", "Ws1", "bs1", "Ws2", "bs2"):
+        a = inp.get(key)
+        if a is None:
+            out[key] = None
+        elif a.dtype == np.uint16:
+            out[key] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        else:
+            out[key] = torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return out

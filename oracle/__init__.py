@@ -56,8 +56,15 @@ def _load():
                                                                      C.c_double, P]
         for f in (lib.orc_route, lib.orc_dispatch, lib.orc_experts, lib.orc_expert_row):
             f.restype = C.c_int
+        lib.orc_threads.argtypes = []
+        lib.orc_threads.restype = C.c_int
         _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().orc_threads())
 
 
 def _cfg(shape, T: Optional[int] = None) -> _Cfg:

@@ -48,6 +48,7 @@
  * that reduce to torch CPU library routines.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -340,3 +341,6 @@ int orc_expert_row(const orc_config *c, const void *x, const void *W1, const voi
   free(h);
   return 0;
 }
+
+/* Threads the parallel loops above use. */
+int orc_threads(void) { return omp_get_max_threads(); }

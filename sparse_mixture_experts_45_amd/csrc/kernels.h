@@ -1,0 +1,56 @@
+// Launch plans and entry points of the HIP kernels (internal to the library).
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+
+struct RoutePlan {
+  int64_t T;
+  int d, E, k, renorm;
+  int S, kchunk;  // router score split over d: S chunks of kchunk columns
+  int lpt, vpl;   // gate: lanes per token, values per lane
+  int nb;         // gate blocks = ceil(T / kGateTokens)
+};
+
+// Row-tile shapes of the grouped GEMM.  Chosen on the host from the shape only.
+enum GemmShape { kGemmF32 = 0, kGemmBf16Large = 1, kGemmBf16Mid = 2, kGemmBf16Small = 3 };
+
+struct GemmPlan {
+  int shape;        // GemmShape
+  int BM, BN_up, BN_down;
+  int64_t tiles_max;  // upper bound on row tiles over all groups
+};
+
+struct FfnArgs {
+  int64_t T;
+  int d, F, E, k, Fs, act, dtype;
+  const void* x;
+  const void *W1, *b1, *W2, *b2, *Ws1, *bs1, *Ws2, *bs2;
+  const int32_t *offsets, *row_token, *row_slot;
+  const float* topk_w;
+  void* H;           // [rows_max, max(F, Fs)] in dtype
+  float* y_rows;     // [rows_max, d]
+  RowTile* tiles;    // [tiles_max]
+  int32_t* ntiles;   // [1]
+};
+
+hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const float* Wg,
+                         const float* bg, float* part, int32_t* topk_idx, float* topk_w,
+                         float* probs, double* stat_part, int32_t* hist, float* mean_prob,
+                         float* balance, hipStream_t st);
+
+hipError_t launch_dispatch(int64_t T, int E, int k, int capacity, int shared, int nb,
+                           const int32_t* topk_idx, bool need_hist, int32_t* hist, int32_t* base,
+                           int32_t* counts, int32_t* kept, int32_t* offsets, int32_t* row_token,
+                           int32_t* row_slot, int32_t* inv, hipStream_t st);
+
+hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& a, hipStream_t st);
+
+hipError_t launch_combine(int64_t T, int d, int E, int k, int shared, int dtype,
+                          const float* y_rows, const int32_t* inv, const int32_t* offsets,
+                          void* y, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,293 @@
+// C ABI of the MoE layer: argument checks, workspace carve-up, launch order.
+// Nothing here allocates, synchronises or reads device memory.
+#include <string.h>
+
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+struct Layout {
+  RoutePlan rp;
+  GemmPlan gp;
+  int64_t rows_max;  // T*k + (Fs ? T : 0)
+  size_t part, stat, hist, base, topk_idx, topk_w, counts, kept, offsets, row_token, row_slot,
+      inv, tiles, ntiles, H, y_rows, total;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->d_model < 8 || c->d_ff < 8 || c->n_experts < 1 || c->top_k < 1 ||
+      c->shared_d_ff < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->d_model % 8 || c->d_ff % 8 || c->shared_d_ff % 8) return MOE_ERR_INVALID_ARG;
+  if (c->act != MOE_ACT_GELU && c->act != MOE_ACT_RELU) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (c->top_k > c->n_experts) return MOE_ERR_INVALID_ARG;
+  if (c->n_experts + (c->shared_d_ff > 0 ? 1 : 0) > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (c->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (c->T * (c->top_k + 1) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+GemmPlan gemm_plan(const moe_config* c) {
+  GemmPlan g{};
+  const int64_t pairs = c->T * c->top_k;
+  const int64_t rmax = c->capacity >= 0 ? std::min<int64_t>(pairs, int64_t(c->n_experts) * c->capacity)
+                                        : pairs;
+  const int64_t avg = rmax / c->n_experts;
+  if (c->dtype == MOE_F32) {
+    g.shape = kGemmF32;
+    g.BM = 64;
+  } else if (avg >= 128) {
+    g.shape = kGemmBf16Large;
+    g.BM = 128;
+  } else if (avg >= 48) {
+    g.shape = kGemmBf16Mid;
+    g.BM = 64;
+  } else {
+    g.shape = kGemmBf16Small;
+    g.BM = 32;
+  }
+  // sum_e ceil(r_e / BM) <= ceil(R / BM) + (number of non-empty experts)
+  g.tiles_max = ceil_div(rmax, g.BM) + std::min<int64_t>(c->n_experts, rmax) +
+                (c->shared_d_ff > 0 ? ceil_div(c->T, g.BM) : 0);
+  return g;
+}
+
+RoutePlan route_plan(const moe_config* c) {
+  RoutePlan p{};
+  p.T = c->T;
+  p.d = c->d_model;
+  p.E = c->n_experts;
+  p.k = c->top_k;
+  p.renorm = c->renormalize;
+  p.nb = static_cast<int>(ceil_div(c->T, kGateTokens));
+  // split d so the score kernel has >= ~512 blocks, chunks >= 128 columns
+  const int64_t base_blocks = ceil_div(c->T, 64) * ceil_div(c->n_experts, 64);
+  int S = static_cast<int>(std::max<int64_t>(1, ceil_div(512, std::max<int64_t>(1, base_blocks))));
+  S = std::min(S, std::max(1, c->d_model / 128));
+  S = std::min(S, 16);
+  p.kchunk = static_cast<int>(align_up(ceil_div(c->d_model, S), 32));
+  p.S = static_cast<int>(ceil_div(c->d_model, p.kchunk));
+  int lpt = 1;
+  while (lpt < c->n_experts && lpt < 64) lpt <<= 1;
+  p.lpt = lpt;
+  const int need = static_cast<int>(ceil_div(c->n_experts, lpt));
+  int vpl = 1;
+  while (vpl < need) vpl <<= 1;
+  p.vpl = vpl;
+  return p;
+}
+
+Layout layout(const moe_config* c) {
+  Layout L{};
+  L.rp = route_plan(c);
+  L.gp = gemm_plan(c);
+  const int64_t T = c->T, E = c->n_experts, k = c->top_k;
+  L.rows_max = T * k + (c->shared_d_ff > 0 ? T : 0);
+  const size_t elt = c->dtype == MOE_BF16 ? 2 : 4;
+  const int64_t ldh = std::max(c->d_ff, c->shared_d_ff);
+  const int64_t nb = L.rp.nb;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + std::max<size_t>(bytes, 1), kAlign);
+    return at;
+  };
+  L.part = take(sizeof(float) * L.rp.S * T * E);
+  L.stat = take(sizeof(double) * nb * E);
+  L.hist = take(sizeof(int32_t) * nb * E);
+  L.base = take(sizeof(int32_t) * nb * E);
+  L.topk_idx = take(sizeof(int32_t) * T * k);
+  L.topk_w = take(sizeof(float) * T * k);
+  L.counts = take(sizeof(int32_t) * E);
+  L.kept = take(sizeof(int32_t) * E);
+  L.offsets = take(sizeof(int32_t) * (E + 2));
+  L.row_token = take(sizeof(int32_t) * L.rows_max);
+  L.row_slot = take(sizeof(int32_t) * L.rows_max);
+  L.inv = take(sizeof(int32_t) * T * k);
+  L.tiles = take(sizeof(RowTile) * L.gp.tiles_max);
+  L.ntiles = take(sizeof(int32_t));
+  L.H = take(elt * L.rows_max * ldh);
+  L.y_rows = take(sizeof(float) * L.rows_max * c->d_model);
+  L.total = o;
+  return L;
+}
+
+inline char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+moe_status check_ws(const Layout& L, void* ws, size_t ws_bytes) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) || ws_bytes < L.total)
+    return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status check_weights(const moe_config* c, const moe_weights* w) {
+  if (!w || !w->Wg || !w->W1 || !w->W2) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w->W1) || !aligned16(w->W2)) return MOE_ERR_INVALID_ARG;
+  if (c->shared_d_ff > 0) {
+    if (!w->Ws1 || !w->Ws2 || !aligned16(w->Ws1) || !aligned16(w->Ws2)) return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+moe_status run_ffn(const moe_config* c, const Layout& L, const void* x, const moe_weights* w,
+                   const int32_t* offsets, const int32_t* row_token, const int32_t* row_slot,
+                   const float* topk_w, float* y_rows, void* ws, hipStream_t st) {
+  FfnArgs f{};
+  f.T = c->T;
+  f.d = c->d_model;
+  f.F = c->d_ff;
+  f.E = c->n_experts;
+  f.k = c->top_k;
+  f.Fs = c->shared_d_ff;
+  f.act = c->act;
+  f.dtype = c->dtype;
+  f.x = x;
+  f.W1 = w->W1;
+  f.b1 = w->b1;
+  f.W2 = w->W2;
+  f.b2 = w->b2;
+  f.Ws1 = w->Ws1;
+  f.bs1 = w->bs1;
+  f.Ws2 = w->Ws2;
+  f.bs2 = w->bs2;
+  f.offsets = offsets;
+  f.row_token = row_token;
+  f.row_slot = row_slot;
+  f.topk_w = topk_w;
+  f.H = at(ws, L.H);
+  f.y_rows = y_rows;
+  f.tiles = reinterpret_cast<RowTile*>(at(ws, L.tiles));
+  f.ntiles = reinterpret_cast<int32_t*>(at(ws, L.ntiles));
+  return hip_status(launch_ffn(L.gp, f, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return layout(cfg).total;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const float* Wg, const float* bg,
+                     int32_t* topk_idx, float* topk_w, float* probs, float* mean_prob,
+                     float* balance, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T > 0 && (!x || !Wg || !topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(cfg);
+  if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(launch_router(L.rp, x, cfg->dtype, Wg, bg, reinterpret_cast<float*>(at(ws, L.part)),
+                                  topk_idx, topk_w, probs, reinterpret_cast<double*>(at(ws, L.stat)),
+                                  reinterpret_cast<int32_t*>(at(ws, L.hist)), mean_prob, balance, st));
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t* counts,
+                        int32_t* kept, int32_t* offsets, int32_t* row_token, int32_t* row_slot,
+                        int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!counts || !kept || !offsets) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!topk_idx || !row_token || !row_slot || !inv)) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(cfg);
+  if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
+  return hip_status(launch_dispatch(cfg->T, cfg->n_experts, cfg->top_k, cfg->capacity,
+                                    cfg->shared_d_ff > 0, L.rp.nb, topk_idx, true,
+                                    reinterpret_cast<int32_t*>(at(ws, L.hist)),
+                                    reinterpret_cast<int32_t*>(at(ws, L.base)), counts, kept,
+                                    offsets, row_token, row_slot, inv,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const moe_weights* w,
+                          const int32_t* offsets, const int32_t* row_token,
+                          const int32_t* row_slot, const float* topk_w, float* y_rows, void* ws,
+                          size_t ws_bytes, void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(cfg, w)) != MOE_OK) return s;
+  if (!offsets || (cfg->T > 0 && (!x || !row_token || !row_slot || !topk_w || !y_rows)))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && !aligned16(x)) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(cfg);
+  if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
+  if (cfg->T == 0) return MOE_OK;
+  return run_ffn(cfg, L, x, w, offsets, row_token, row_slot, topk_w, y_rows, ws,
+                 static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_config* cfg, const float* y_rows, const int32_t* inv,
+                       const int32_t* offsets, void* y, void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T > 0 && (!y_rows || !inv || !offsets || !y)) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!aligned16(y_rows) || !aligned16(y))) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(cfg->T, cfg->d_model, cfg->n_experts, cfg->top_k,
+                                   cfg->shared_d_ff > 0, cfg->dtype, y_rows, inv, offsets, y,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* y,
+                       moe_stats* stats, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(cfg, w)) != MOE_OK) return s;
+  if (cfg->T > 0 && (!x || !y || !aligned16(x) || !aligned16(y))) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(cfg);
+  if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  moe_stats none{};
+  const moe_stats& o = stats ? *stats : none;
+
+  int32_t* topk_idx = o.topk_idx ? o.topk_idx : reinterpret_cast<int32_t*>(at(ws, L.topk_idx));
+  float* topk_w = o.topk_w ? o.topk_w : reinterpret_cast<float*>(at(ws, L.topk_w));
+  int32_t* counts = o.counts ? o.counts : reinterpret_cast<int32_t*>(at(ws, L.counts));
+  int32_t* kept = o.kept ? o.kept : reinterpret_cast<int32_t*>(at(ws, L.kept));
+  int32_t* offsets = reinterpret_cast<int32_t*>(at(ws, L.offsets));
+  int32_t* row_token = reinterpret_cast<int32_t*>(at(ws, L.row_token));
+  int32_t* row_slot = reinterpret_cast<int32_t*>(at(ws, L.row_slot));
+  int32_t* inv = reinterpret_cast<int32_t*>(at(ws, L.inv));
+  int32_t* hist = reinterpret_cast<int32_t*>(at(ws, L.hist));
+  float* y_rows = reinterpret_cast<float*>(at(ws, L.y_rows));
+
+  if ((s = hip_status(launch_router(L.rp, x, cfg->dtype, w->Wg, w->bg,
+                                    reinterpret_cast<float*>(at(ws, L.part)), topk_idx, topk_w,
+                                    nullptr, reinterpret_cast<double*>(at(ws, L.stat)), hist,
+                                    o.mean_prob, o.balance, st))) != MOE_OK)
+    return s;
+  // the gate kernel already wrote the per-block expert histogram
+  if ((s = hip_status(launch_dispatch(cfg->T, cfg->n_experts, cfg->top_k, cfg->capacity,
+                                      cfg->shared_d_ff > 0, L.rp.nb, topk_idx, false, hist,
+                                      reinterpret_cast<int32_t*>(at(ws, L.base)), counts, kept,
+                                      offsets, row_token, row_slot, inv, st))) != MOE_OK)
+    return s;
+  if (cfg->T == 0) return MOE_OK;
+  if ((s = run_ffn(cfg, L, x, w, offsets, row_token, row_slot, topk_w, y_rows, ws, st)) != MOE_OK)
+    return s;
+  return hip_status(launch_combine(cfg->T, cfg->d_model, cfg->n_experts, cfg->top_k,
+                                   cfg->shared_d_ff > 0, cfg->dtype, y_rows, inv, offsets, y, st));
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+"""Helpers shared by the GPU tests: run the C-ABI on generated inputs and
+compare with the oracle under the stated tolerances."""
+import sys
+
+import numpy as np
+import torch
+
+import sparse_mixture_experts_45_amd as moe
+from moe_synth import bf16_bits_to_f32, to_device
+
+# tolerances (routing indices, counts and grouping are compared exactly)
+TOPK_W_ABS = 1e-6
+PROBS_ABS = 1e-6
+MEAN_PROB_REL = 1e-5
+BALANCE_REL, BALANCE_ABS = 1e-4, 1e-9
+Y_F32_REL_L2, Y_F32_MAX_ABS = 1e-5, 1e-4
+Y_BF16_REL_L2 = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(shape):
+    return torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+
+
+def cfg_of(shape, T=None):
+    return moe.config(shape.T if T is None else T, shape.d, shape.F, shape.E, shape.k,
+                      act=shape.act, dtype=torch_dtype(shape), capacity=shape.capacity,
+                      renormalize=bool(shape.renormalize), shared_d_ff=shape.Fs)
+
+
+def gpu_forward(shape, dev, ws=None):
+    """moe_forward with every statistic requested; returns numpy outputs."""
+    T, k, E = shape.T, shape.k, shape.E
+    c = cfg_of(shape)
+    ws = moe.workspace(c) if ws is None else ws
+    y = torch.empty((T, shape.d), dtype=torch_dtype(shape), device="cuda")
+    st = dict(topk_idx=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+              topk_w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+              counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+              kept=torch.empty(E, dtype=torch.int32, device="cuda"),
+              mean_prob=torch.empty(E, dtype=torch.float32, device="cuda"),
+              balance=torch.empty(1, dtype=torch.float32, device="cuda"))
+    moe.moe_forward(c, dev, dev["x"], y, st, ws)
+    torch.cuda.synchronize()
+    out = {key: v.cpu().numpy() for key, v in st.items()}
+    out["balance"] = float(out["balance"][0])
+    out["y"] = y.float().cpu().numpy().astype(np.float64)
+    out["y_raw"] = y
+    return out
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def check_y(shape, got, ref, what="y"):
+    if ref.size == 0:
+        return
+    r = rel_l2(got, ref)
+    if shape.dtype == "f32":
+        m = float(np.max(np.abs(got - ref)))
+        assert r <= Y_F32_REL_L2 and m <= Y_F32_MAX_ABS, (what, r, m)
+    else:
+        assert r <= Y_BF16_REL_L2, (what, r)
+    return r
+
+
+def check_routing(shape, g, ref):
+    assert np.array_equal(g["topk_idx"], ref["topk_idx"])
+    if shape.T:
+        err = float(np.max(np.abs(g["topk_w"] - ref["topk_w"])))
+        assert err <= TOPK_W_ABS, err
+    assert np.array_equal(g["counts"], ref["counts"])
+    assert np.array_equal(g["kept"], ref["kept"])
+    if shape.T == 0:
+        assert np.all(np.isnan(g["mean_prob"]))
+        return
+    mp_ref = ref["mean_prob"]
+    rel = np.abs(g["mean_prob"] - mp_ref) / np.abs(mp_ref)
+    assert float(np.max(rel)) <= MEAN_PROB_REL, float(np.max(rel))
+    if shape.E == 1:
+        assert np.isnan(g["balance"])
+    else:
+        b, br = g["balance"], ref["balance"]
+        assert abs(b - br) <= max(BALANCE_ABS, BALANCE_REL * abs(br)), (b, br)
+
+
+def device_inputs(inp):
+    return to_device(inp, "cuda")
+
+
+def widen(a, shape):
+    return bf16_bits_to_f32(a) if shape.dtype == "bf16" else a

@@ -1,0 +1,77 @@
+"""GPU parity at the five full workload sizes, in the launch configuration the
+benchmark times (moe_forward with the library's own tile choice).
+
+Routing, counts, kept counts and the load statistics are checked for every
+token; the grouping arrays are checked in full through moe_dispatch fed the
+oracle's routing; layer outputs are checked on a sample of tokens the oracle
+computes one by one (spread over the batch, plus, with a capacity limit,
+dropped tokens and the last tokens kept by the fullest expert).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_45_amd as moe
+from moe_synth import WORKLOAD_ORDER, make_inputs, workload
+from gpu_common import cfg_of, check_routing, check_y, device_inputs, gpu_forward, say
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = {"tiny_f32": None, "page1_b4s512": 96, "mixtral_t4096": 24,
+           "switch_e64_top1_cap": 64, "deepseek_e256_top8": 32}
+
+
+def sample_tokens(shape, ref, n):
+    if n is None:
+        return np.arange(shape.T)
+    toks = set(np.linspace(0, shape.T - 1, n).astype(int).tolist())
+    if shape.capacity >= 0:
+        dropped = np.nonzero(ref["keep"].min(axis=1) == 0)[0]
+        toks.update(dropped[:8].tolist())
+        e0 = int(np.argmax(ref["counts"]))
+        kept_e0 = [t for t in range(shape.T) for i in range(shape.k)
+                   if ref["topk_idx"][t, i] == e0 and ref["keep"][t, i]]
+        toks.update(kept_e0[-4:])
+    return np.array(sorted(toks))
+
+
+@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+def test_workload_parity(name):
+    shape = workload(name)
+    say("workload", shape)
+    inp = make_inputs(shape, 0)
+    ref = oracle.route(shape, inp)
+    dev = device_inputs(inp)
+    g = gpu_forward(shape, dev)
+    check_routing(shape, g, ref)
+    toks = sample_tokens(shape, ref, SAMPLES[name])
+    y_ref = oracle.experts(shape, inp, ref, toks)
+    r = check_y(shape, g["y"][toks], y_ref)
+    say("  rel-L2 on %d tokens: %.3g" % (len(toks), r))
+    if shape.capacity >= 0:
+        dropped_all = np.nonzero(ref["keep"].max(axis=1) == 0)[0]
+        if shape.Fs == 0 and len(dropped_all):
+            assert np.all(g["y"][dropped_all] == 0.0)
+
+    # grouping arrays in full, from the oracle's routing
+    d = oracle.dispatch(shape, ref["topk_idx"], ref["keep"])
+    T, k, E = shape.T, shape.k, shape.E
+    nrows = T * k + (T if shape.Fs else 0)
+    c = cfg_of(shape)
+    ws = moe.workspace(c)
+    outs = [torch.empty(E, dtype=torch.int32, device="cuda"),
+            torch.empty(E, dtype=torch.int32, device="cuda"),
+            torch.empty(E + 2, dtype=torch.int32, device="cuda"),
+            torch.empty(nrows, dtype=torch.int32, device="cuda"),
+            torch.empty(nrows, dtype=torch.int32, device="cuda"),
+            torch.empty((T, k), dtype=torch.int32, device="cuda")]
+    moe.moe_dispatch(c, torch.from_numpy(ref["topk_idx"]).cuda(), *outs, ws)
+    torch.cuda.synchronize()
+    n = int(d["offsets"][E + 1])
+    assert np.array_equal(outs[2].cpu().numpy(), d["offsets"])
+    assert np.array_equal(outs[3].cpu().numpy()[:n], d["row_token"])
+    assert np.array_equal(outs[4].cpu().numpy()[:n], d["row_slot"])
+    assert np.array_equal(outs[5].cpu().numpy(), d["inv"])
+    del dev, inp
+    torch.cuda.empty_cache()
