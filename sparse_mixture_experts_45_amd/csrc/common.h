@@ -56,9 +56,10 @@ __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { re
 __host__ __device__ constexpr inline size_t align_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
 // One row tile of the grouped GEMM: group (expert, or E for the shared expert),
-// first row, number of rows.
+// first row, number of rows, and the index of the group's first row tile and
+// the group's number of row tiles.
 struct RowTile {
-  int32_t group, row0, rows, pad;
+  int32_t group, row0, rows, first, count, pad0, pad1, pad2;
 };
 
 }  // namespace moe

@@ -15,12 +15,21 @@
 // Work list: row tiles (group, first row, rows) built on the device from the
 // dispatch offsets, times N tiles.  The grid is sized from an upper bound on
 // the row-tile count known on the host; blocks past the real count exit.
+//
+// Tile order.  Workgroup i is dispatched to XCD i % 8, and each XCD has its own
+// L2.  Block ids are remapped so each XCD walks a contiguous range of the
+// tile list, and the list is ordered group by group, in bands of kBand N tiles
+// with the group's row tiles fastest: the blocks that run together on one XCD
+// share the same weight columns and the same token rows.
 #include "kernels.h"
 
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kXcd = 8;
+constexpr int kBand = 8;
 
 template <typename T>
 struct Mfma;
@@ -76,6 +85,29 @@ struct GemmArgs {
   int act;
 };
 
+// Block id -> (row tile, n tile), or false if the block has no work.
+__device__ __forceinline__ bool decode_tile(const GemmArgs& a, int* rt, int* nt) {
+  const int NT = a.n_tiles_n;
+  const int total = *a.ntiles * NT;
+  const int pid = blockIdx.x;
+  if (pid >= total) return false;
+  const int q = total / kXcd, r = total % kXcd;
+  const int x = pid % kXcd, local = pid / kXcd;
+  const int v = x * q + min(x, r) + local;  // bijection onto [0, total)
+  const RowTile& t = a.tiles[v / NT];
+  const int m = t.count;
+  const int ve = v - t.first * NT;           // index inside the group
+  const int band = ve / (m * kBand);
+  const int rem = ve - band * m * kBand;
+  *nt = band * kBand + rem / m;
+  *rt = t.first + rem % m;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Generic kernel: any K that is a multiple of 8 (bf16) or 4 (fp32); tiles are
+// staged through registers with zero fill beyond K and beyond the tile rows.
+// ---------------------------------------------------------------------------
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool UP>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
   using M = Mfma<T>;
@@ -94,10 +126,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
   __shared__ __align__(16) T Bs[BN * LDK];
   __shared__ float gate_s[BM];
 
-  const int bid = blockIdx.x;
-  const int rt = bid / a.n_tiles_n;
-  const int nt = bid - rt * a.n_tiles_n;
-  if (rt >= *a.ntiles) return;
+  int rt, nt;
+  if (!decode_tile(a, &rt, &nt)) return;
   const RowTile tile = a.tiles[rt];
   const int g = tile.group;
   const bool sh = (g == a.E);
@@ -124,7 +154,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
     }
   }
 
-  // per-thread 16-byte chunks of the A and B tiles
   const T* asrc[ACH];
   int aoff[ACH], akc[ACH];
 #pragma unroll
@@ -223,12 +252,163 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel for K a multiple of 64.  Tiles go from global memory straight
+// into LDS with global_load_lds_dwordx4 (no register staging), two stages,
+// one barrier per 64-wide K step.  LDS rows are 128 bytes (eight 16-byte
+// chunks) with the chunk index XORed with (row % 8), so the eight rows an MFMA
+// fragment read touches per chunk land in eight different bank groups.  Each
+// wave instruction fills 8 consecutive tile rows (1 KB of LDS); lane L writes
+// chunk slot L % 8 of row L / 8 and fetches the global chunk that belongs
+// there.  Rows past the tile (or past N) are fetched from a clamped valid row
+// and their results are never stored.
+// ---------------------------------------------------------------------------
+constexpr int kDmaBK = 64;
+constexpr int kRowBytes = kDmaBK * 2;  // 128
+
+// 16 bytes from global memory to LDS; the wave's 64 lanes fill 1 KB starting at
+// the wave-uniform address `lds` (lane L at lds + 16 L).
+__device__ __forceinline__ void lds_dma16(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, bool UP>
+__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs a) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MI = WTM / 32, NI = WTN / 32;
+  constexpr int ROWS = BM + BN;            // A rows then B rows
+  constexpr int JPW = ROWS / 8 / NW;       // load instructions per wave per stage
+  constexpr int STAGE = ROWS * kRowBytes;  // bytes
+  static_assert(ROWS % (8 * NW) == 0 && MI >= 1 && NI >= 1, "tile shape");
+
+  extern __shared__ __align__(16) char smem[];
+  __shared__ float gate_s[BM];
+
+  int rt, nt;
+  if (!decode_tile(a, &rt, &nt)) return;
+  const RowTile tile = a.tiles[rt];
+  const int g = tile.group;
+  const bool sh = (g == a.E);
+  const int N = sh ? a.Ns : a.N;
+  const int K = sh ? a.Ks : a.K;
+  const int n0 = nt * BN;
+  if (n0 >= N) return;
+  const bf16* Bw =
+      static_cast<const bf16*>(sh ? a.Wsh : a.W) + (sh ? 0 : static_cast<int64_t>(g) * N * K);
+  const bf16* bias = static_cast<const bf16*>(sh ? a.bias_sh : a.bias);
+  if (bias && !sh) bias += static_cast<int64_t>(g) * N;
+  const int row0 = tile.row0, rows = tile.rows;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  if (!UP) {
+    for (int m = tid; m < BM; m += NW * 64) {
+      float gv = 0.f;
+      if (m < rows) {
+        const int r = row0 + m;
+        gv = sh ? 1.0f : a.topk_w[static_cast<int64_t>(a.row_token[r]) * a.k + a.row_slot[r]];
+      }
+      gate_s[m] = gv;
+    }
+  }
+
+  // global source of this lane's chunk for each of its load instructions
+  const char* src[JPW];
+  const int swz = lane >> 3;  // tile row % 8 of this lane's row
+#pragma unroll
+  for (int j = 0; j < JPW; ++j) {
+    const int r = (wave + j * NW) * 8 + swz;  // combined tile row
+    const int chunk = (lane & 7) ^ swz;
+    const char* base;
+    if (r < BM) {
+      const int rr = min(r, rows - 1);
+      const int64_t arow = UP ? static_cast<int64_t>(a.row_token[row0 + rr]) : (row0 + rr);
+      base = reinterpret_cast<const char*>(static_cast<const bf16*>(a.A) + arow * a.lda);
+    } else {
+      const int nn = min(n0 + r - BM, N - 1);
+      base = reinterpret_cast<const char*>(Bw + static_cast<int64_t>(nn) * K);
+    }
+    src[j] = base + chunk * 16;
+  }
+  auto issue = [&](int stage, int k0) {
+#pragma unroll
+    for (int j = 0; j < JPW; ++j)
+      lds_dma16(src[j] + static_cast<int64_t>(k0) * 2,
+                smem + stage * STAGE + (wave + j * NW) * 8 * kRowBytes);
+  };
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // fragment read offsets (bytes inside a stage) for k16 step s = 0
+  int aoffs[MI], boffs[NI];
+  const int lrow = lane & 31;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) aoffs[i] = (wm * WTM + i * 32 + lrow) * kRowBytes;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) boffs[j] = (BM + wn * WTN + j * 32 + lrow) * kRowBytes;
+  const int rsw = lrow & 7;  // row % 8 is the same for every fragment row of this lane
+
+  const int KT = K / kDmaBK;
+  issue(0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's loads of stage kt landed
+    __syncthreads();                     // ...and every lane's; stage kt^1 is free again
+    if (kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * kDmaBK);
+    const char* st = smem + (kt & 1) * STAGE;
+#pragma unroll
+    for (int s = 0; s < kDmaBK / 16; ++s) {
+      const int cb = ((2 * s + (lane >> 5)) ^ rsw) * 16;
+      bf16x8_t fa[MI], fb[NI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(st + aoffs[i] + cb);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(st + boffs[j] + cb);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int n = n0 + wn * WTN + j * 32 + (lane & 31);
+    if (n >= N) continue;
+    const float bv = bias ? bf16_to_f32(bias[n].bits) : 0.f;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+        if (m >= rows) continue;
+        const float z = acc[i][j][q] + bv;
+        const int64_t o = static_cast<int64_t>(row0 + m) * a.ldo + n;
+        if (UP) {
+          const float h = (a.act == MOE_ACT_RELU) ? fmaxf(z, 0.f) : gelu_erf(z);
+          static_cast<bf16*>(a.out)[o] = bf16{f32_to_bf16(h)};
+        } else {
+          static_cast<float*>(a.out)[o] = gate_s[m] * z;
+        }
+      }
+    }
+  }
+}
+
 // Row tiles of BM rows per group, groups in order, from the dispatch offsets.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            int G, int BM,
                                                            RowTile* __restrict__ tiles,
                                                            int32_t* __restrict__ ntiles) {
-  __shared__ int32_t sc[2][kMaxExperts + 1];
+  __shared__ int32_t sc[2][kMaxExperts];
   const int g = threadIdx.x;
   int rows = 0, m = 0;
   if (g < G) {
@@ -237,7 +417,6 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   }
   int src = 0;
   sc[0][g] = m;
-  if (g == 0) sc[0][kMaxExperts] = 0;
   __syncthreads();
   for (int o = 1; o < kMaxExperts; o <<= 1) {
     const int v = sc[src][g] + (g >= o ? sc[src][g - o] : 0);
@@ -253,19 +432,17 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
       t.group = g;
       t.row0 = r0 + j * BM;
       t.rows = min(BM, rows - j * BM);
-      t.pad = 0;
+      t.first = start;
+      t.count = m;
+      t.pad0 = t.pad1 = t.pad2 = 0;
       tiles[start + j] = t;
     }
   }
   if (g == kMaxExperts - 1) ntiles[0] = sc[src][g];
 }
 
-template <typename T, int BM, int BNU, int BND, int BK, int WM, int WN>
-static void run_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
-  const int G = f.E + (f.Fs > 0 ? 1 : 0);
-  build_tiles_kernel<<<1, kMaxExperts, 0, st>>>(f.offsets, G, BM, f.tiles, f.ntiles);
+static GemmArgs up_args(const FfnArgs& f, int BN) {
   const int64_t ldh = f.F > f.Fs ? f.F : f.Fs;
-
   GemmArgs u{};
   u.tiles = f.tiles;
   u.ntiles = f.ntiles;
@@ -284,15 +461,16 @@ static void run_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   u.K = f.d;
   u.Ns = f.Fs;
   u.Ks = f.d;
-  u.n_tiles_n = static_cast<int>(ceil_div(ldh, BNU));
+  u.n_tiles_n = static_cast<int>(ceil_div(ldh, BN));
   u.out = f.H;
   u.ldo = ldh;
   u.act = f.act;
-  const int64_t gu = gp.tiles_max * u.n_tiles_n;
-  if (gu > 0)
-    grouped_gemm_kernel<T, BM, BNU, BK, WM, WN, true><<<static_cast<unsigned>(gu), WM * WN * 64, 0, st>>>(u);
+  return u;
+}
 
-  GemmArgs dn = u;
+static GemmArgs down_args(const FfnArgs& f, int BN) {
+  const int64_t ldh = f.F > f.Fs ? f.F : f.Fs;
+  GemmArgs dn = up_args(f, BN);
   dn.A = f.H;
   dn.lda = ldh;
   dn.W = f.W2;
@@ -303,20 +481,63 @@ static void run_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   dn.K = f.F;
   dn.Ns = f.d;
   dn.Ks = f.Fs;
-  dn.n_tiles_n = static_cast<int>(ceil_div(f.d, BND));
+  dn.n_tiles_n = static_cast<int>(ceil_div(f.d, BN));
   dn.out = f.y_rows;
   dn.ldo = f.d;
+  return dn;
+}
+
+template <typename T, int BM, int BNU, int BND, int BK, int WM, int WN>
+static void run_generic(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
+  const GemmArgs u = up_args(f, BNU);
+  const int64_t gu = gp.tiles_max * u.n_tiles_n;
+  if (gu > 0)
+    grouped_gemm_kernel<T, BM, BNU, BK, WM, WN, true>
+        <<<static_cast<unsigned>(gu), WM * WN * 64, 0, st>>>(u);
+  const GemmArgs dn = down_args(f, BND);
   const int64_t gd = gp.tiles_max * dn.n_tiles_n;
   if (gd > 0)
-    grouped_gemm_kernel<T, BM, BND, BK, WM, WN, false><<<static_cast<unsigned>(gd), WM * WN * 64, 0, st>>>(dn);
+    grouped_gemm_kernel<T, BM, BND, BK, WM, WN, false>
+        <<<static_cast<unsigned>(gd), WM * WN * 64, 0, st>>>(dn);
+}
+
+template <int BM, int BNU, int BND, int WM, int WN>
+static void run_dma(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
+  const GemmArgs u = up_args(f, BNU);
+  const int64_t gu = gp.tiles_max * u.n_tiles_n;
+  const size_t lu = 2 * (BM + BNU) * kRowBytes;
+  if (gu > 0) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<BM, BNU, WM, WN, true>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lu));
+    (void)attr;
+    grouped_gemm_dma_kernel<BM, BNU, WM, WN, true>
+        <<<static_cast<unsigned>(gu), WM * WN * 64, lu, st>>>(u);
+  }
+  const GemmArgs dn = down_args(f, BND);
+  const int64_t gd = gp.tiles_max * dn.n_tiles_n;
+  const size_t ld = 2 * (BM + BND) * kRowBytes;
+  if (gd > 0) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<BM, BND, WM, WN, false>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ld));
+    (void)attr;
+    grouped_gemm_dma_kernel<BM, BND, WM, WN, false>
+        <<<static_cast<unsigned>(gd), WM * WN * 64, ld, st>>>(dn);
+  }
 }
 
 hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
+  const int G = f.E + (f.Fs > 0 ? 1 : 0);
+  build_tiles_kernel<<<1, kMaxExperts, 0, st>>>(f.offsets, G, gp.BM, f.tiles, f.ntiles);
   switch (gp.shape) {
-    case kGemmF32: run_ffn<float, 64, 64, 64, 32, 2, 2>(gp, f, st); break;
-    case kGemmBf16Large: run_ffn<bf16, 128, 128, 128, 64, 2, 2>(gp, f, st); break;
-    case kGemmBf16Mid: run_ffn<bf16, 64, 128, 128, 64, 1, 4>(gp, f, st); break;
-    default: run_ffn<bf16, 32, 128, 128, 64, 1, 4>(gp, f, st); break;
+    case kGemmF32: run_generic<float, 64, 64, 64, 32, 2, 2>(gp, f, st); break;
+    case kGemmBf16Large: run_generic<bf16, 128, 128, 128, 64, 2, 2>(gp, f, st); break;
+    case kGemmBf16Mid: run_generic<bf16, 64, 128, 128, 64, 1, 4>(gp, f, st); break;
+    case kGemmBf16Small: run_generic<bf16, 32, 128, 128, 64, 1, 4>(gp, f, st); break;
+    case kGemmDma256: run_dma<256, 256, 256, 2, 2>(gp, f, st); break;
+    case kGemmDma128: run_dma<128, 128, 128, 2, 2>(gp, f, st); break;
+    default: run_dma<32, 128, 128, 1, 4>(gp, f, st); break;
   }
   return hipGetLastError();
 }

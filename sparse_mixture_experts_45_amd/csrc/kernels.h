@@ -16,7 +16,15 @@ struct RoutePlan {
 };
 
 // Row-tile shapes of the grouped GEMM.  Chosen on the host from the shape only.
-enum GemmShape { kGemmF32 = 0, kGemmBf16Large = 1, kGemmBf16Mid = 2, kGemmBf16Small = 3 };
+enum GemmShape {
+  kGemmF32 = 0,        // fp32 MFMA, register-staged tiles
+  kGemmBf16Large = 1,  // bf16, register-staged (any K multiple of 8)
+  kGemmBf16Mid = 2,
+  kGemmBf16Small = 3,
+  kGemmDma256 = 4,     // bf16, K multiple of 64, LDS-DMA tiles 256 x 256
+  kGemmDma128 = 5,     //   128 x 128
+  kGemmDmaSkinny = 6   //   32 x 128 (few rows per expert: weight streaming)
+};
 
 struct GemmPlan {
   int shape;        // GemmShape

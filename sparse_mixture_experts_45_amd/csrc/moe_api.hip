@@ -40,9 +40,19 @@ GemmPlan gemm_plan(const moe_config* c) {
   const int64_t rmax = c->capacity >= 0 ? std::min<int64_t>(pairs, int64_t(c->n_experts) * c->capacity)
                                         : pairs;
   const int64_t avg = rmax / c->n_experts;
+  const bool k64 = c->d_model % 64 == 0 && c->d_ff % 64 == 0 && c->shared_d_ff % 64 == 0;
   if (c->dtype == MOE_F32) {
     g.shape = kGemmF32;
     g.BM = 64;
+  } else if (k64 && avg >= 768) {
+    g.shape = kGemmDma256;
+    g.BM = 256;
+  } else if (k64 && avg >= 96) {
+    g.shape = kGemmDma128;
+    g.BM = 128;
+  } else if (k64) {
+    g.shape = kGemmDmaSkinny;
+    g.BM = 32;
   } else if (avg >= 128) {
     g.shape = kGemmBf16Large;
     g.BM = 128;
@@ -68,7 +78,7 @@ RoutePlan route_plan(const moe_config* c) {
   p.renorm = c->renormalize;
   p.nb = static_cast<int>(ceil_div(c->T, kGateTokens));
   // split d so the score kernel has >= ~512 blocks, chunks >= 128 columns
-  const int64_t base_blocks = ceil_div(c->T, 64) * ceil_div(c->n_experts, 64);
+  const int64_t base_blocks = ceil_div(c->T, 64) * ceil_div(c->n_experts, c->n_experts <= 16 ? 16 : 64);
   int S = static_cast<int>(std::max<int64_t>(1, ceil_div(512, std::max<int64_t>(1, base_blocks))));
   S = std::min(S, std::max(1, c->d_model / 128));
   S = std::min(S, 16);
@@ -131,7 +141,7 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 moe_status check_weights(const moe_config* c, const moe_weights* w) {
   if (!w || !w->Wg || !w->W1 || !w->W2) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(w->W1) || !aligned16(w->W2)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w->Wg) || !aligned16(w->W1) || !aligned16(w->W2)) return MOE_ERR_INVALID_ARG;
   if (c->shared_d_ff > 0) {
     if (!w->Ws1 || !w->Ws2 || !aligned16(w->Ws1) || !aligned16(w->Ws2)) return MOE_ERR_INVALID_ARG;
   }
@@ -185,6 +195,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const float* Wg, cons
   moe_status s = check_config(cfg);
   if (s != MOE_OK) return s;
   if (cfg->T > 0 && (!x || !Wg || !topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!aligned16(x) || !aligned16(Wg))) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(cfg);
   if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);

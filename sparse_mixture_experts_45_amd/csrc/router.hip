@@ -13,55 +13,130 @@ namespace moe {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// Scores.  Block = 4 waves; tile = 64 tokens x 64 experts over one K chunk.
-// Each wave owns 16 tokens and all 64 experts of the tile: 4 fp32 MFMA
-// 16x16x4 accumulators.  Partial sums of chunk s go to part[s][T][E]; the gate
-// kernel adds the chunks in order s = 0, 1, ... so the result is deterministic.
+// Scores.  Block = 4 waves; tile = 64 tokens x TE experts (TE = 16 or 64) over
+// one K chunk.  Each wave owns 16 tokens and all TE experts of the tile
+// (TE / 16 fp32 MFMA 16x16x4 accumulators).  The next K step is loaded into
+// registers while the current one is multiplied.  Partial sums of chunk s go
+// to part[s][T][E]; the gate kernel adds the chunks in order s = 0, 1, ...
+// so the result is deterministic.
 // ---------------------------------------------------------------------------
-constexpr int kRtM = 64, kRtE = 64, kRtK = 32;
+constexpr int kRtM = 64, kRtK = 32;
 
 template <typename XT>
+struct XLoad;
+template <>
+struct XLoad<bf16> {  // 8 bf16 per 16-byte chunk, 4 chunks per 32-wide row
+  static constexpr int kPer = 8;
+};
+template <>
+struct XLoad<float> {  // 4 floats per chunk, 8 chunks per row
+  static constexpr int kPer = 4;
+};
+
+template <typename XT, int TE>
 __global__ __launch_bounds__(256) void router_scores_kernel(const XT* __restrict__ x,
                                                             const float* __restrict__ Wg,
                                                             int64_t T, int d, int E, int kchunk,
                                                             float* __restrict__ part) {
+  constexpr int XP = XLoad<XT>::kPer;
+  constexpr int XCH = kRtM * kRtK / XP;  // x chunks per stage
+  constexpr int WCH = TE * kRtK / 4;     // W chunks (float4) per stage
+  constexpr int XPT = (XCH + 255) / 256, WPT = (WCH + 255) / 256;
+  constexpr int NB = TE / 16;
   __shared__ float xs[kRtM][kRtK + 1];
-  __shared__ float ws[kRtE][kRtK + 1];
+  __shared__ float ws[TE][kRtK + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRtM;
-  const int e0 = blockIdx.y * kRtE;
+  const int e0 = blockIdx.y * TE;
   const int s = blockIdx.z;
   const int kb = s * kchunk;
   const int ke = min(d, kb + kchunk);
-  f32x4 acc[4];
-#pragma unroll
-  for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = kb; k0 < ke; k0 += kRtK) {
+  float xr[XPT][XP];
+  float wr[WPT][4];
+  auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = tid; i < kRtM * kRtK; i += 256) {
-      const int r = i / kRtK, c = i % kRtK;
-      const int k = k0 + c;
+    for (int i = 0; i < XPT; ++i) {
+      const int c = tid + i * 256;
+      const int r = c / (kRtK / XP), kc = (c % (kRtK / XP)) * XP;
       const int64_t t = t0 + r;
-      xs[r][c] = (t < T && k < ke) ? to_f32(x[t * d + k]) : 0.f;
-      const int e = e0 + r;
-      ws[r][c] = (e < E && k < ke) ? Wg[static_cast<int64_t>(e) * d + k] : 0.f;
+      const int k = k0 + kc;
+      const bool ok = c < XCH && t < T && k < ke;  // ke and k are multiples of 8
+      if constexpr (XP == 8) {
+        uint4 u = ok ? *reinterpret_cast<const uint4*>(x + t * d + k) : make_uint4(0, 0, 0, 0);
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xr[i][2 * q] = __uint_as_float(w4[q] << 16);
+          xr[i][2 * q + 1] = __uint_as_float(w4[q] & 0xffff0000u);
+        }
+      } else {
+        float4 f = ok ? *reinterpret_cast<const float4*>(x + t * d + k) : make_float4(0, 0, 0, 0);
+        xr[i][0] = f.x;
+        xr[i][1] = f.y;
+        xr[i][2] = f.z;
+        xr[i][3] = f.w;
+      }
     }
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int c = tid + i * 256;
+      const int r = c / (kRtK / 4), kc = (c % (kRtK / 4)) * 4;
+      const int e = e0 + r;
+      const int k = k0 + kc;
+      const bool ok = c < WCH && e < E && k < ke;
+      float4 f = ok ? *reinterpret_cast<const float4*>(Wg + static_cast<int64_t>(e) * d + k)
+                    : make_float4(0, 0, 0, 0);
+      wr[i][0] = f.x;
+      wr[i][1] = f.y;
+      wr[i][2] = f.z;
+      wr[i][3] = f.w;
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int c = tid + i * 256;
+      if (c < XCH) {
+        const int r = c / (kRtK / XP), kc = (c % (kRtK / XP)) * XP;
+#pragma unroll
+        for (int q = 0; q < XP; ++q) xs[r][kc + q] = xr[i][q];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int c = tid + i * 256;
+      if (c < WCH) {
+        const int r = c / (kRtK / 4), kc = (c % (kRtK / 4)) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ws[r][kc + q] = wr[i][q];
+      }
+    }
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  gload(kb);
+  for (int k0 = kb; k0 < ke; k0 += kRtK) {
     __syncthreads();
+    sstore();
+    __syncthreads();
+    if (k0 + kRtK < ke) gload(k0 + kRtK);
 #pragma unroll
     for (int kk = 0; kk < kRtK; kk += 4) {
       const float a = xs[wave * 16 + (lane & 15)][kk + (lane >> 4)];
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
+      for (int n = 0; n < NB; ++n) {
         const float b = ws[n * 16 + (lane & 15)][kk + (lane >> 4)];
         acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[n], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
   // acc[n][j] holds token row (lane>>4)*4 + j of the wave, expert column lane&15.
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
+  for (int n = 0; n < NB; ++n) {
     const int e = e0 + n * 16 + (lane & 15);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -72,48 +147,60 @@ __global__ __launch_bounds__(256) void router_scores_kernel(const XT* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Gate.  One block handles kGateTokens tokens with 4 waves of 16 tokens each.
+// Gate.  One block handles kGateTokens tokens with 8 waves of 8 tokens each.
 // A token's E scores are spread over LPT lanes (LPT = min(64, next pow2 of E)),
 // VPL values per lane, expert e = s + v * LPT for lane sub-index s.  Max, sum,
 // and each of the k argmax rounds are xor-shuffle trees inside the LPT group,
 // so every lane of the group ends with identical values.  Ties pick the lower
-// expert index.  Per-block sums of the probabilities (fp64) and the count of
-// (token, slot) pairs per expert are reduced in a fixed order: no atomics.
+// expert index.  Per-block sums of the probabilities (fp64) are reduced in a
+// fixed order; the per-block count of (token, slot) pairs per expert uses LDS
+// integer atomics, whose result does not depend on their order.
 // ---------------------------------------------------------------------------
+constexpr int kGateWaves = 8;
+constexpr int kGateTPW = kGateTokens / kGateWaves;  // tokens per wave
+
 template <int VPL>
-__global__ __launch_bounds__(256) void router_gate_kernel(
+__global__ __launch_bounds__(kGateWaves * 64) void router_gate_kernel(
     const float* __restrict__ part, int S, const float* __restrict__ bg, int64_t T, int E, int k,
     int renorm, int lpt, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ probs, double* __restrict__ stat_part, int32_t* __restrict__ hist) {
   __shared__ double red_d[4][kMaxExperts];
-  __shared__ int32_t red_i[4][kMaxExperts];
+  __shared__ int32_t hcnt[kMaxExperts];
+  __shared__ float selp_s[kGateWaves][64];
+  __shared__ int32_t sele_s[kGateWaves][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s = lane & (lpt - 1);
   const int grp = lane / lpt;
   const int tpw = kWave / lpt;  // tokens per wave step
   const int64_t blk = blockIdx.x;
+  for (int e = tid; e < E; e += kGateWaves * 64) hcnt[e] = 0;
+  __syncthreads();
 
   double sacc[VPL];
-  int cnt[VPL];
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    sacc[v] = 0.0;
-    cnt[v] = 0;
-  }
+  for (int v = 0; v < VPL; ++v) sacc[v] = 0.0;
 
-  const int iters = (16 + tpw - 1) / tpw;  // each wave owns 16 tokens
+  const int iters = (kGateTPW + tpw - 1) / tpw;
   for (int it = 0; it < iters; ++it) {
     const int local = it * tpw + grp;
-    const int64_t t = blk * kGateTokens + wave * 16 + local;
-    const bool vt = local < 16 && t < T;
+    const int64_t t = blk * kGateTokens + wave * kGateTPW + local;
+    const bool vt = local < kGateTPW && t < T;
     float l[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int e = s + v * lpt;
       float z = -INFINITY;
       if (vt && e < E) {
-        z = part[t * E + e];
-        for (int sp = 1; sp < S; ++sp) z += part[(static_cast<int64_t>(sp) * T + t) * E + e];
+        const float* pp = part + t * E + e;
+        const int64_t stride = T * E;
+        z = 0.f;
+        int sp = 0;
+        for (; sp + 4 <= S; sp += 4) {  // four loads in flight, added in chunk order
+          const float a0 = pp[sp * stride], a1 = pp[(sp + 1) * stride];
+          const float a2 = pp[(sp + 2) * stride], a3 = pp[(sp + 3) * stride];
+          z = (((z + a0) + a1) + a2) + a3;
+        }
+        for (; sp < S; ++sp) z += pp[sp * stride];
         if (bg) z += bg[e];
       }
       l[v] = z;
@@ -143,76 +230,66 @@ __global__ __launch_bounds__(256) void router_gate_kernel(
     // top-k: k rounds of a group argmax over the not-yet-taken experts
     uint32_t taken = 0;
     float selsum = 0.f;
-    float selp[kMaxTopK];
-    int sele[kMaxTopK];
+    for (int i = 0; i < k; ++i) {
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < kMaxTopK; ++i) {
-      if (i < k) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
+      for (int v = 0; v < VPL; ++v) {
+        const int e = s + v * lpt;
+        if (e < E && !((taken >> v) & 1u) && (l[v] > bv || (l[v] == bv && e < be))) {
+          bv = l[v];
+          be = e;
+        }
+      }
+      for (int o = lpt >> 1; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oe = __shfl_xor(be, o);
+        if (ov > bv || (ov == bv && oe < be)) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if ((be & (lpt - 1)) == s) {
+        const int v = be / lpt;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          const int e = s + v * lpt;
-          if (e < E && !((taken >> v) & 1u) && (l[v] > bv || (l[v] == bv && e < be))) {
-            bv = l[v];
-            be = e;
-          }
-        }
-        for (int o = lpt >> 1; o >= 1; o >>= 1) {
-          const float ov = __shfl_xor(bv, o);
-          const int oe = __shfl_xor(be, o);
-          if (ov > bv || (ov == bv && oe < be)) {
-            bv = ov;
-            be = oe;
-          }
-        }
-        if ((be & (lpt - 1)) == s) {
-          const int v = be / lpt;
-#pragma unroll
-          for (int vv = 0; vv < VPL; ++vv)
-            if (vv == v) {
-              taken |= 1u << vv;
-              if (vt) cnt[vv] += 1;
-            }
-        }
-        const float p = expf(bv - m) / sum;  // same value the owner lane computed
-        selp[i] = p;
-        sele[i] = be;
-        selsum += p;
+        for (int vv = 0; vv < VPL; ++vv)
+          if (vv == v) taken |= 1u << vv;
+        if (vt) atomicAdd(&hcnt[be], 1);
+      }
+      const float p = expf(bv - m) / sum;  // same value the owner lane computed
+      selsum += p;
+      if (s == 0) {
+        selp_s[wave][grp * k + i] = p;
+        sele_s[wave][grp * k + i] = be;
       }
     }
-    if (vt && s == 0) {
-#pragma unroll
-      for (int i = 0; i < kMaxTopK; ++i)
-        if (i < k) {
-          topk_idx[t * k + i] = sele[i];
-          topk_w[t * k + i] = renorm ? selp[i] / selsum : selp[i];
-        }
+    __syncthreads();
+    if (vt && s < k) {
+      const float p = selp_s[wave][grp * k + s];
+      topk_idx[t * k + s] = sele_s[wave][grp * k + s];
+      topk_w[t * k + s] = renorm ? p / selsum : p;
     }
+    __syncthreads();
   }
 
-  // reduce across the token groups of the wave (lanes with the same s)
+  // reduce across the token groups of the wave (lanes with the same s), then
+  // across waves in a fixed order: (w0 + w4) + (w1 + w5) + (w2 + w6) + (w3 + w7)
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    for (int o = lpt; o < kWave; o <<= 1) {
-      sacc[v] += __shfl_xor(sacc[v], o);
-      cnt[v] += __shfl_xor(cnt[v], o);
-    }
-  }
-  if (grp == 0) {
+  for (int v = 0; v < VPL; ++v)
+    for (int o = lpt; o < kWave; o <<= 1) sacc[v] += __shfl_xor(sacc[v], o);
+  for (int half = 0; half < 2; ++half) {
+    if (grp == 0 && (wave >> 2) == half) {
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int e = s + v * lpt;
-      if (e < E) {
-        red_d[wave][e] = sacc[v];
-        red_i[wave][e] = cnt[v];
+      for (int v = 0; v < VPL; ++v) {
+        const int e = s + v * lpt;
+        if (e < E) red_d[wave & 3][e] = half ? red_d[wave & 3][e] + sacc[v] : sacc[v];
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int e = tid; e < E; e += 256) {
+  for (int e = tid; e < E; e += kGateWaves * 64) {
     stat_part[blk * E + e] = ((red_d[0][e] + red_d[1][e]) + red_d[2][e]) + red_d[3][e];
-    hist[blk * E + e] = red_i[0][e] + red_i[1][e] + red_i[2][e] + red_i[3][e];
+    hist[blk * E + e] = hcnt[e];
   }
 }
 
@@ -247,17 +324,21 @@ hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const flo
                          float* probs, double* stat_part, int32_t* hist, float* mean_prob,
                          float* balance, hipStream_t st) {
   if (p.T > 0) {
-    dim3 g1(static_cast<unsigned>(ceil_div(p.T, kRtM)), static_cast<unsigned>(ceil_div(p.E, kRtE)),
+    const int TE = p.E <= 16 ? 16 : 64;
+    dim3 g1(static_cast<unsigned>(ceil_div(p.T, kRtM)), static_cast<unsigned>(ceil_div(p.E, TE)),
             static_cast<unsigned>(p.S));
-    if (dtype == MOE_BF16)
-      router_scores_kernel<bf16><<<g1, 256, 0, st>>>(static_cast<const bf16*>(x), Wg, p.T, p.d, p.E,
-                                                     p.kchunk, part);
-    else
-      router_scores_kernel<float><<<g1, 256, 0, st>>>(static_cast<const float*>(x), Wg, p.T, p.d,
-                                                      p.E, p.kchunk, part);
+#define MOE_SCORES(XT, TEV)                                                                  \
+  router_scores_kernel<XT, TEV><<<g1, 256, 0, st>>>(static_cast<const XT*>(x), Wg, p.T, p.d, \
+                                                    p.E, p.kchunk, part)
+    if (dtype == MOE_BF16) {
+      if (TE == 16) MOE_SCORES(bf16, 16); else MOE_SCORES(bf16, 64);
+    } else {
+      if (TE == 16) MOE_SCORES(float, 16); else MOE_SCORES(float, 64);
+    }
+#undef MOE_SCORES
     const unsigned nb = static_cast<unsigned>(p.nb);
 #define MOE_GATE(V)                                                                            \
-  router_gate_kernel<V><<<nb, 256, 0, st>>>(part, p.S, bg, p.T, p.E, p.k, p.renorm, p.lpt,     \
+  router_gate_kernel<V><<<nb, kGateWaves * 64, 0, st>>>(part, p.S, bg, p.T, p.E, p.k, p.renorm, p.lpt,     \
                                             topk_idx, topk_w, probs, stat_part, hist)
     switch (p.vpl) {
       case 1: MOE_GATE(1); break;
