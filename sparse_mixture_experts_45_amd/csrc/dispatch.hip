@@ -38,35 +38,57 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
   for (int e = threadIdx.x; e < E; e += 256) hist[b * E + e] = h[e];
 }
 
+// One block.  Thread (e, c) owns expert e and the c-th contiguous range of the
+// per-block counts; ranges are summed, scanned across c, then re-walked to
+// write each block's base.  Integer sums: exact in any order.
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     const int32_t* __restrict__ hist, int nb, int E, int64_t T, int capacity, int shared,
     int32_t* __restrict__ base, int32_t* __restrict__ counts, int32_t* __restrict__ kept,
     int32_t* __restrict__ offsets) {
+  __shared__ int32_t part[kMaxExperts];
   __shared__ int32_t sc[2][kMaxExperts];
-  const int e = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int chunks = kMaxExperts / E;  // >= 1
+  const int e = tid % E, c = tid / E;
+  const int len = (nb + chunks - 1) / chunks;
+  const int b0 = c * len, b1 = min(nb, b0 + len);
+  int sum = 0;
+  if (c < chunks)
+    for (int b = b0; b < b1; ++b) sum += hist[static_cast<int64_t>(b) * E + e];
+  if (c < chunks) part[tid] = sum;
+  __syncthreads();
   int kp = 0;
-  if (e < E) {
-    int c = 0;
-    for (int b = 0; b < nb; ++b) {
-      base[static_cast<int64_t>(b) * E + e] = c;
-      c += hist[static_cast<int64_t>(b) * E + e];
+  if (tid < E) {
+    int run = 0;
+    for (int cc = 0; cc < chunks; ++cc) {
+      const int v = part[cc * E + tid];
+      part[cc * E + tid] = run;  // exclusive prefix over ranges
+      run += v;
     }
-    kp = capacity < 0 ? c : min(c, capacity);
-    counts[e] = c;
-    kept[e] = kp;
+    kp = capacity < 0 ? run : min(run, capacity);
+    counts[tid] = run;
+    kept[tid] = kp;
+  }
+  __syncthreads();
+  if (c < chunks) {
+    int run = part[tid];
+    for (int b = b0; b < b1; ++b) {
+      base[static_cast<int64_t>(b) * E + e] = run;
+      run += hist[static_cast<int64_t>(b) * E + e];
+    }
   }
   // inclusive Hillis-Steele scan of kept over the experts
   int src = 0;
-  sc[0][e] = kp;
+  sc[0][tid] = kp;
   __syncthreads();
   for (int o = 1; o < kMaxExperts; o <<= 1) {
-    const int v = sc[src][e] + (e >= o ? sc[src][e - o] : 0);
-    sc[src ^ 1][e] = v;
+    const int v = sc[src][tid] + (tid >= o ? sc[src][tid - o] : 0);
+    sc[src ^ 1][tid] = v;
     src ^= 1;
     __syncthreads();
   }
-  if (e < E) offsets[e] = sc[src][e] - kp;
-  if (e == 0) {
+  if (tid < E) offsets[tid] = sc[src][tid] - kp;
+  if (tid == 0) {
     const int total = sc[src][E - 1];
     offsets[E] = total;
     offsets[E + 1] = total + (shared ? static_cast<int32_t>(T) : 0);

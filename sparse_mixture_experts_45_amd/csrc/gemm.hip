@@ -253,18 +253,17 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel for K a multiple of 64.  Tiles go from global memory straight
-// into LDS with global_load_lds_dwordx4 (no register staging), two stages,
-// one barrier per 64-wide K step.  LDS rows are 128 bytes (eight 16-byte
-// chunks) with the chunk index XORed with (row % 8), so the eight rows an MFMA
-// fragment read touches per chunk land in eight different bank groups.  Each
-// wave instruction fills 8 consecutive tile rows (1 KB of LDS); lane L writes
-// chunk slot L % 8 of row L / 8 and fetches the global chunk that belongs
-// there.  Rows past the tile (or past N) are fetched from a clamped valid row
-// and their results are never stored.
+// bf16 kernel for K a multiple of BK (32 or 64).  Tiles go from global memory
+// straight into LDS with global_load_lds_dwordx4 (no register staging) through
+// a ring of NS stages, so NS - 1 K steps are in flight while one is
+// multiplied; one barrier per K step.  An LDS tile row holds BK bf16 (64 or
+// 128 bytes, 4 or 8 sixteen-byte chunks) with the chunk index XORed with a
+// function of the row (swz below), so the rows an MFMA fragment read touches
+// per chunk land in different banks.  Each wave instruction fills 1 KB of consecutive
+// tile rows; lane L writes chunk slot L % CPR of row L / CPR and fetches the
+// global chunk that belongs there.  Rows past the tile (or past N) are fetched
+// from a clamped valid row and their results are never stored.
 // ---------------------------------------------------------------------------
-constexpr int kDmaBK = 64;
-constexpr int kRowBytes = kDmaBK * 2;  // 128
 
 // 16 bytes from global memory to LDS; the wave's 64 lanes fill 1 KB starting at
 // the wave-uniform address `lds` (lane L at lds + 16 L).
@@ -272,15 +271,39 @@ __device__ __forceinline__ void lds_dma16(const void* g, char* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, bool UP>
+// Chunk swizzle of tile row r.  gfx950 LDS has 64 four-byte banks (256 bytes
+// per bank cycle) and services a 16-byte-per-lane read 16 lanes at a time; the
+// 16 lanes of a fragment read hit 16 consecutive tile rows at the same logical
+// chunk.  With 128-byte rows two rows share a bank line, so rows r and r + 2k
+// must land on different chunks: chunk ^ ((r / 2) % 8).  With 64-byte rows four
+// rows share a bank line: chunk ^ ((r / 4) % 4).
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  return CPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+
+// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BN, int BK, int NS, int WM, int WN, bool UP>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs a) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MI = WTM / 32, NI = WTN / 32;
+  constexpr int RB = BK * 2;               // bytes per LDS tile row
+  constexpr int CPR = BK / 8;              // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;            // rows per wave instruction
   constexpr int ROWS = BM + BN;            // A rows then B rows
-  constexpr int JPW = ROWS / 8 / NW;       // load instructions per wave per stage
-  constexpr int STAGE = ROWS * kRowBytes;  // bytes
-  static_assert(ROWS % (8 * NW) == 0 && MI >= 1 && NI >= 1, "tile shape");
+  constexpr int JPW = ROWS / RPI / NW;     // load instructions per wave per stage
+  constexpr int STAGE = ROWS * RB;         // bytes
+  constexpr int KS = BK / 16;              // k16 MFMA steps per stage
+  static_assert(ROWS % (RPI * NW) == 0 && MI >= 1 && NI >= 1, "tile shape");
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(NS >= 2 && JPW * (NS - 2) < 64, "stages");
 
   extern __shared__ __align__(16) char smem[];
   __shared__ float gate_s[BM];
@@ -316,11 +339,11 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
 
   // global source of this lane's chunk for each of its load instructions
   const char* src[JPW];
-  const int swz = lane >> 3;  // tile row % 8 of this lane's row
+  const int lr = lane / CPR;  // row inside the instruction's rows
 #pragma unroll
   for (int j = 0; j < JPW; ++j) {
-    const int r = (wave + j * NW) * 8 + swz;  // combined tile row
-    const int chunk = (lane & 7) ^ swz;
+    const int r = (wave + j * NW) * RPI + lr;  // combined tile row
+    const int chunk = (lane % CPR) ^ swz<CPR>(r);
     const char* base;
     if (r < BM) {
       const int rr = min(r, rows - 1);
@@ -336,7 +359,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
 #pragma unroll
     for (int j = 0; j < JPW; ++j)
       lds_dma16(src[j] + static_cast<int64_t>(k0) * 2,
-                smem + stage * STAGE + (wave + j * NW) * 8 * kRowBytes);
+                smem + stage * STAGE + (wave + j * NW) * RPI * RB);
   };
 
   f32x16 acc[MI][NI];
@@ -347,35 +370,76 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // fragment read offsets (bytes inside a stage) for k16 step s = 0
   int aoffs[MI], boffs[NI];
   const int lrow = lane & 31;
 #pragma unroll
-  for (int i = 0; i < MI; ++i) aoffs[i] = (wm * WTM + i * 32 + lrow) * kRowBytes;
+  for (int i = 0; i < MI; ++i) aoffs[i] = (wm * WTM + i * 32 + lrow) * RB;
 #pragma unroll
-  for (int j = 0; j < NI; ++j) boffs[j] = (BM + wn * WTN + j * 32 + lrow) * kRowBytes;
-  const int rsw = lrow & 7;  // row % 8 is the same for every fragment row of this lane
+  for (int j = 0; j < NI; ++j) boffs[j] = (BM + wn * WTN + j * 32 + lrow) * RB;
+  const int rsw = swz<CPR>(lrow);  // the same for every fragment row of this lane
 
-  const int KT = K / kDmaBK;
-  issue(0, 0);
+  const int KT = K / BK;
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < KT) issue(p, p * BK);
   for (int kt = 0; kt < KT; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's loads of stage kt landed
-    __syncthreads();                     // ...and every lane's; stage kt^1 is free again
-    if (kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * kDmaBK);
-    const char* st = smem + (kt & 1) * STAGE;
-#pragma unroll
-    for (int s = 0; s < kDmaBK / 16; ++s) {
+    // this lane's loads of stage kt have landed once at most the loads of the
+    // later stages already issued (min(NS - 2, KT - 1 - kt) of them) are pending
+    if (kt + NS - 2 < KT) {
+      wait_vmcnt<JPW * (NS - 2)>();
+    } else if constexpr (NS > 2) {
+      if (kt + 1 == KT) wait_vmcnt<0>();
+      else if constexpr (NS > 3) {
+        if (kt + 2 == KT) wait_vmcnt<JPW>();
+        else wait_vmcnt<0>();
+      }
+    }
+    // Every lane's loads of stage kt landed; every wave finished reading stage
+    // kt - 1 (its fragments were consumed by MFMAs already issued).  A plain
+    // s_barrier: a workgroup fence here would also wait for the later stages.
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (kt + NS - 1 < KT) issue((kt + NS - 1) % NS, (kt + NS - 1) * BK);
+    const char* st = smem + (kt % NS) * STAGE;
+    // fragments of k16 step s + 1 are read while the MFMAs of step s run
+    bf16x8_t fa[2][MI], fb[2][NI];
+    auto frags = [&](int s, int buf) {
       const int cb = ((2 * s + (lane >> 5)) ^ rsw) * 16;
-      bf16x8_t fa[MI], fb[NI];
 #pragma unroll
-      for (int i = 0; i < MI; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(st + aoffs[i] + cb);
+      for (int i = 0; i < MI; ++i)
+        fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + aoffs[i] + cb);
 #pragma unroll
-      for (int j = 0; j < NI; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(st + boffs[j] + cb);
+      for (int j = 0; j < NI; ++j)
+        fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boffs[j] + cb);
+    };
+    frags(0, 0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) frags(s + 1, (s + 1) & 1);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
+                                                              acc[i][j], 0, 0, 0);
+    }
+    // Instruction order for the scheduler: the first step's fragment reads, then
+    // for each step its MFMAs with the next step's reads spread between them,
+    // so LDS latency hides under MFMA issue instead of stalling each step.
+    constexpr int NR = MI + NI, NM = MI * NI;
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if (NM % NR) __builtin_amdgcn_sched_group_barrier(0x008, NM % NR, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+      }
     }
   }
 
@@ -501,28 +565,28 @@ static void run_generic(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
         <<<static_cast<unsigned>(gd), WM * WN * 64, 0, st>>>(dn);
 }
 
-template <int BM, int BNU, int BND, int WM, int WN>
+template <int BM, int BNU, int BND, int BK, int NS, int WM, int WN>
 static void run_dma(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const GemmArgs u = up_args(f, BNU);
   const int64_t gu = gp.tiles_max * u.n_tiles_n;
-  const size_t lu = 2 * (BM + BNU) * kRowBytes;
+  const size_t lu = static_cast<size_t>(NS) * (BM + BNU) * BK * 2;
   if (gu > 0) {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<BM, BNU, WM, WN, true>),
+        reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<BM, BNU, BK, NS, WM, WN, true>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lu));
     (void)attr;
-    grouped_gemm_dma_kernel<BM, BNU, WM, WN, true>
+    grouped_gemm_dma_kernel<BM, BNU, BK, NS, WM, WN, true>
         <<<static_cast<unsigned>(gu), WM * WN * 64, lu, st>>>(u);
   }
   const GemmArgs dn = down_args(f, BND);
   const int64_t gd = gp.tiles_max * dn.n_tiles_n;
-  const size_t ld = 2 * (BM + BND) * kRowBytes;
+  const size_t ld = static_cast<size_t>(NS) * (BM + BND) * BK * 2;
   if (gd > 0) {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<BM, BND, WM, WN, false>),
+        reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<BM, BND, BK, NS, WM, WN, false>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ld));
     (void)attr;
-    grouped_gemm_dma_kernel<BM, BND, WM, WN, false>
+    grouped_gemm_dma_kernel<BM, BND, BK, NS, WM, WN, false>
         <<<static_cast<unsigned>(gd), WM * WN * 64, ld, st>>>(dn);
   }
 }
@@ -535,9 +599,12 @@ hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
     case kGemmBf16Large: run_generic<bf16, 128, 128, 128, 64, 2, 2>(gp, f, st); break;
     case kGemmBf16Mid: run_generic<bf16, 64, 128, 128, 64, 1, 4>(gp, f, st); break;
     case kGemmBf16Small: run_generic<bf16, 32, 128, 128, 64, 1, 4>(gp, f, st); break;
-    case kGemmDma256: run_dma<256, 256, 256, 2, 2>(gp, f, st); break;
-    case kGemmDma128: run_dma<128, 128, 128, 2, 2>(gp, f, st); break;
-    default: run_dma<32, 128, 128, 1, 4>(gp, f, st); break;
+#define MOE_RUN_DMA(C) run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN>(gp, f, st)
+    case kGemmDmaLarge: MOE_RUN_DMA(kDmaLarge); break;
+    case kGemmDmaMid: MOE_RUN_DMA(kDmaMid); break;
+    case kGemmDmaSmall: MOE_RUN_DMA(kDmaSmall); break;
+    default: MOE_RUN_DMA(kDmaSkinny); break;
+#undef MOE_RUN_DMA
   }
   return hipGetLastError();
 }

@@ -21,10 +21,21 @@ enum GemmShape {
   kGemmBf16Large = 1,  // bf16, register-staged (any K multiple of 8)
   kGemmBf16Mid = 2,
   kGemmBf16Small = 3,
-  kGemmDma256 = 4,     // bf16, K multiple of 64, LDS-DMA tiles 256 x 256
-  kGemmDma128 = 5,     //   128 x 128
-  kGemmDmaSkinny = 6   //   32 x 128 (few rows per expert: weight streaming)
+  kGemmDmaLarge = 4,   // bf16, K multiple of 64, LDS-DMA tiles (kDma* below)
+  kGemmDmaMid = 5,
+  kGemmDmaSmall = 6,
+  kGemmDmaSkinny = 7
 };
+
+// Tile configurations of the LDS-DMA grouped GEMM.  The host plan (row-tile
+// height for the tile list) and the launcher read the same table.
+struct DmaCfg {
+  int BM, BNU, BND, BK, NS, WM, WN;  // rows, up/down columns, K step, stages, wave grid
+};
+constexpr DmaCfg kDmaLarge{256, 256, 256, 64, 2, 2, 4};   // >= 768 rows per expert
+constexpr DmaCfg kDmaMid{128, 256, 256, 64, 2, 2, 4};     // >= 256
+constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 4, 1, 4};    // >= 48
+constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 4, 1, 4};   // fewer: weight streaming
 
 struct GemmPlan {
   int shape;        // GemmShape

@@ -45,14 +45,17 @@ GemmPlan gemm_plan(const moe_config* c) {
     g.shape = kGemmF32;
     g.BM = 64;
   } else if (k64 && avg >= 768) {
-    g.shape = kGemmDma256;
-    g.BM = 256;
-  } else if (k64 && avg >= 96) {
-    g.shape = kGemmDma128;
-    g.BM = 128;
+    g.shape = kGemmDmaLarge;
+    g.BM = kDmaLarge.BM;
+  } else if (k64 && avg >= 256) {
+    g.shape = kGemmDmaMid;
+    g.BM = kDmaMid.BM;
+  } else if (k64 && avg >= 48) {
+    g.shape = kGemmDmaSmall;
+    g.BM = kDmaSmall.BM;
   } else if (k64) {
     g.shape = kGemmDmaSkinny;
-    g.BM = 32;
+    g.BM = kDmaSkinny.BM;
   } else if (avg >= 128) {
     g.shape = kGemmBf16Large;
     g.BM = 128;

@@ -156,14 +156,22 @@ __global__ __launch_bounds__(256) void router_scores_kernel(const XT* __restrict
 // fixed order; the per-block count of (token, slot) pairs per expert uses LDS
 // integer atomics, whose result does not depend on their order.
 // ---------------------------------------------------------------------------
-constexpr int kGateWaves = 8;
-constexpr int kGateTPW = kGateTokens / kGateWaves;  // tokens per wave
+// Sum of the score chunks in chunk order, written over chunk 0.
+__global__ __launch_bounds__(256) void router_reduce_kernel(float* __restrict__ part, int S,
+                                                            int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  float z = part[i];
+  for (int sp = 1; sp < S; ++sp) z += part[static_cast<int64_t>(sp) * n + i];
+  part[i] = z;
+}
 
-template <int VPL>
+template <int VPL, int kGateWaves>
 __global__ __launch_bounds__(kGateWaves * 64) void router_gate_kernel(
-    const float* __restrict__ part, int S, const float* __restrict__ bg, int64_t T, int E, int k,
+    const float* __restrict__ logit, const float* __restrict__ bg, int64_t T, int E, int k,
     int renorm, int lpt, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ probs, double* __restrict__ stat_part, int32_t* __restrict__ hist) {
+  constexpr int kGateTPW = kGateTokens / kGateWaves;  // tokens per wave
   __shared__ double red_d[4][kMaxExperts];
   __shared__ int32_t hcnt[kMaxExperts];
   __shared__ float selp_s[kGateWaves][64];
@@ -191,16 +199,7 @@ __global__ __launch_bounds__(kGateWaves * 64) void router_gate_kernel(
       const int e = s + v * lpt;
       float z = -INFINITY;
       if (vt && e < E) {
-        const float* pp = part + t * E + e;
-        const int64_t stride = T * E;
-        z = 0.f;
-        int sp = 0;
-        for (; sp + 4 <= S; sp += 4) {  // four loads in flight, added in chunk order
-          const float a0 = pp[sp * stride], a1 = pp[(sp + 1) * stride];
-          const float a2 = pp[(sp + 2) * stride], a3 = pp[(sp + 3) * stride];
-          z = (((z + a0) + a1) + a2) + a3;
-        }
-        for (; sp < S; ++sp) z += pp[sp * stride];
+        z = logit[t * E + e];
         if (bg) z += bg[e];
       }
       l[v] = z;
@@ -273,11 +272,12 @@ __global__ __launch_bounds__(kGateWaves * 64) void router_gate_kernel(
   }
 
   // reduce across the token groups of the wave (lanes with the same s), then
-  // across waves in a fixed order: (w0 + w4) + (w1 + w5) + (w2 + w6) + (w3 + w7)
+  // across waves in a fixed order: slot w % 4 accumulates waves w % 4, w % 4 + 4,
+  // ... in wave order, then the four slots are added in order
 #pragma unroll
   for (int v = 0; v < VPL; ++v)
     for (int o = lpt; o < kWave; o <<= 1) sacc[v] += __shfl_xor(sacc[v], o);
-  for (int half = 0; half < 2; ++half) {
+  for (int half = 0; half < kGateWaves / 4; ++half) {
     if (grp == 0 && (wave >> 2) == half) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
@@ -337,15 +337,19 @@ hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const flo
     }
 #undef MOE_SCORES
     const unsigned nb = static_cast<unsigned>(p.nb);
-#define MOE_GATE(V)                                                                            \
-  router_gate_kernel<V><<<nb, kGateWaves * 64, 0, st>>>(part, p.S, bg, p.T, p.E, p.k, p.renorm, p.lpt,     \
-                                            topk_idx, topk_w, probs, stat_part, hist)
+    if (p.S > 1) {
+      const int64_t n = p.T * p.E;
+      router_reduce_kernel<<<static_cast<unsigned>(ceil_div(n, 256)), 256, 0, st>>>(part, p.S, n);
+    }
+#define MOE_GATE(V, W)                                                                      \
+  router_gate_kernel<V, W><<<nb, W * 64, 0, st>>>(part, bg, p.T, p.E, p.k, p.renorm, p.lpt, \
+                                                  topk_idx, topk_w, probs, stat_part, hist)
     switch (p.vpl) {
-      case 1: MOE_GATE(1); break;
-      case 2: MOE_GATE(2); break;
-      case 4: MOE_GATE(4); break;
-      case 8: MOE_GATE(8); break;
-      default: MOE_GATE(16); break;
+      case 1: MOE_GATE(1, 16); break;
+      case 2: MOE_GATE(2, 16); break;
+      case 4: MOE_GATE(4, 16); break;
+      case 8: MOE_GATE(8, 8); break;
+      default: MOE_GATE(16, 8); break;
     }
 #undef MOE_GATE
   }

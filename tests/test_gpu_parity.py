@@ -49,11 +49,12 @@ SMALL = [
     S("bf16_many_experts", T=130, d=64, F=32, E=1000, k=20, router_bias="none"),
     S("bf16_no_expert_bias", T=150, d=128, F=128, E=8, k=2, expert_bias=False,
       router_bias="none"),
-    # K multiples of 64: the LDS-DMA kernels (256x256, 128x128 and 32x128 tiles)
-    S("dma256_ntail", T=800, d=192, F=320, E=2, k=2),
-    S("dma256_shared", T=900, d=256, F=256, E=2, k=2, Fs=192, act="relu"),
-    S("dma128_ragged", T=300, d=128, F=192, E=4, k=2),
-    S("dma128_capacity", T=700, d=128, F=256, E=8, k=2, capacity=150, router_bias="zipf1.1"),
+    # K multiples of 64: the LDS-DMA kernels; tile tier follows rows per expert
+    S("dma_large_ntail", T=800, d=192, F=320, E=2, k=2),
+    S("dma_large_shared", T=900, d=256, F=256, E=2, k=2, Fs=192, act="relu"),
+    S("dma_mid_ntail", T=600, d=192, F=320, E=4, k=2),
+    S("dma_small_ragged", T=300, d=128, F=192, E=4, k=2),
+    S("dma_small_capacity", T=700, d=128, F=256, E=8, k=2, capacity=150, router_bias="zipf1.1"),
     S("dma_skinny_shared", T=64, d=128, F=192, E=16, k=2, Fs=128),
     S("dma_skinny_many", T=96, d=256, F=128, E=64, k=6, router_bias="none"),
 ]
