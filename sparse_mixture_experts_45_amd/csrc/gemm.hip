@@ -60,8 +60,22 @@ struct Mfma<float> {
   }
 };
 
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26:
+// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+// t = 1 / (1 + p x) for x >= 0, odd in x; absolute error <= 1.5e-7.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = 1.0f / (1.0f + 0.3275911f * ax);
+  const float poly =
+      t * (0.254829592f +
+           t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float e = 1.0f - poly * __expf(-ax * ax);
+  return copysignf(e, x);
+}
+
+// GELU, exact (erf) form: 0.5 z (1 + erf(z / sqrt 2))
 __device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+  return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752440f));
 }
 
 struct GemmArgs {
@@ -73,6 +87,7 @@ struct GemmArgs {
   const int32_t* row_token;
   const int32_t* row_slot;
   const float* topk_w;
+  const float* row_gate;  // gate of each row (1 for shared rows), built with the tile list
   int k;
   const void* W;         // routed weights [E, N, K]
   const void* Wsh;       // shared weights [Ns, Ks]
@@ -85,12 +100,11 @@ struct GemmArgs {
   int act;
 };
 
-// Block id -> (row tile, n tile), or false if the block has no work.
-__device__ __forceinline__ bool decode_tile(const GemmArgs& a, int* rt, int* nt) {
+// Tile id -> (row tile, n tile).  XCD i % 8 runs the blocks with id i, and
+// the ids are remapped so each XCD walks a contiguous range of the tile list.
+__device__ __forceinline__ void decode_tile(const GemmArgs& a, int pid, int total, int* rt,
+                                            int* nt) {
   const int NT = a.n_tiles_n;
-  const int total = *a.ntiles * NT;
-  const int pid = blockIdx.x;
-  if (pid >= total) return false;
   const int q = total / kXcd, r = total % kXcd;
   const int x = pid % kXcd, local = pid / kXcd;
   const int v = x * q + min(x, r) + local;  // bijection onto [0, total)
@@ -101,7 +115,6 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, int* rt, int* nt)
   const int rem = ve - band * m * kBand;
   *nt = band * kBand + rem / m;
   *rt = t.first + rem % m;
-  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -126,8 +139,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
   __shared__ __align__(16) T Bs[BN * LDK];
   __shared__ float gate_s[BM];
 
+  const int total = *a.ntiles * a.n_tiles_n;
+  if (static_cast<int>(blockIdx.x) >= total) return;
   int rt, nt;
-  if (!decode_tile(a, &rt, &nt)) return;
+  decode_tile(a, blockIdx.x, total, &rt, &nt);
   const RowTile tile = a.tiles[rt];
   const int g = tile.group;
   const bool sh = (g == a.E);
@@ -289,9 +304,30 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM, int BN, int BK, int NS, int WM, int WN, bool UP>
-__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs a) {
+// Scheduling hints for N k16 steps: each step's NM MFMAs (0x008) with the NR
+// fragment reads (0x100: DS reads) of the following step spread between them.
+template <int S, int N, int NR, int NM>
+__device__ __forceinline__ void sched_steps() {
+  if constexpr (S < N) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NM / NR > 0 ? NM / NR : 1, 0);
+    }
+    if constexpr (NM > NR && NM % NR != 0) __builtin_amdgcn_sched_group_barrier(0x008, NM % NR, 0);
+    sched_steps<S + 1, N, NR, NM>();
+  }
+}
+
+// Persistent kernel: one block per CU slot walks tiles t = blockIdx.x,
+// blockIdx.x + gridDim.x, ...  While tile t is multiplied, the metadata of the
+// next tile (its token rows, its gates) is already loaded; after the K loop
+// the next tile's first stages are issued before tile t's epilogue runs, so
+// load latency hides under the epilogue instead of idling the CU.
+template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, bool UP>
+__global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(GemmArgs a) {
   constexpr int NW = WM * WN;
+  constexpr int NT = NW * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MI = WTM / 32, NI = WTN / 32;
   constexpr int RB = BK * 2;               // bytes per LDS tile row
@@ -301,75 +337,21 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
   constexpr int JPW = ROWS / RPI / NW;     // load instructions per wave per stage
   constexpr int STAGE = ROWS * RB;         // bytes
   constexpr int KS = BK / 16;              // k16 MFMA steps per stage
+  constexpr int GPT = (BM + NT - 1) / NT;  // gates per thread
   static_assert(ROWS % (RPI * NW) == 0 && MI >= 1 && NI >= 1, "tile shape");
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(NS >= 2 && JPW * (NS - 2) < 64, "stages");
 
   extern __shared__ __align__(16) char smem[];
-  __shared__ float gate_s[BM];
+  __shared__ float gate_s[2][BM];
 
-  int rt, nt;
-  if (!decode_tile(a, &rt, &nt)) return;
-  const RowTile tile = a.tiles[rt];
-  const int g = tile.group;
-  const bool sh = (g == a.E);
-  const int N = sh ? a.Ns : a.N;
-  const int K = sh ? a.Ks : a.K;
-  const int n0 = nt * BN;
-  if (n0 >= N) return;
-  const bf16* Bw =
-      static_cast<const bf16*>(sh ? a.Wsh : a.W) + (sh ? 0 : static_cast<int64_t>(g) * N * K);
-  const bf16* bias = static_cast<const bf16*>(sh ? a.bias_sh : a.bias);
-  if (bias && !sh) bias += static_cast<int64_t>(g) * N;
-  const int row0 = tile.row0, rows = tile.rows;
+  const int total = *a.ntiles * a.n_tiles_n;
+  int t = blockIdx.x;
+  if (t >= total) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-
-  if (!UP) {
-    for (int m = tid; m < BM; m += NW * 64) {
-      float gv = 0.f;
-      if (m < rows) {
-        const int r = row0 + m;
-        gv = sh ? 1.0f : a.topk_w[static_cast<int64_t>(a.row_token[r]) * a.k + a.row_slot[r]];
-      }
-      gate_s[m] = gv;
-    }
-  }
-
-  // global source of this lane's chunk for each of its load instructions
-  const char* src[JPW];
-  const int lr = lane / CPR;  // row inside the instruction's rows
-#pragma unroll
-  for (int j = 0; j < JPW; ++j) {
-    const int r = (wave + j * NW) * RPI + lr;  // combined tile row
-    const int chunk = (lane % CPR) ^ swz<CPR>(r);
-    const char* base;
-    if (r < BM) {
-      const int rr = min(r, rows - 1);
-      const int64_t arow = UP ? static_cast<int64_t>(a.row_token[row0 + rr]) : (row0 + rr);
-      base = reinterpret_cast<const char*>(static_cast<const bf16*>(a.A) + arow * a.lda);
-    } else {
-      const int nn = min(n0 + r - BM, N - 1);
-      base = reinterpret_cast<const char*>(Bw + static_cast<int64_t>(nn) * K);
-    }
-    src[j] = base + chunk * 16;
-  }
-  auto issue = [&](int stage, int k0) {
-#pragma unroll
-    for (int j = 0; j < JPW; ++j)
-      lds_dma16(src[j] + static_cast<int64_t>(k0) * 2,
-                smem + stage * STAGE + (wave + j * NW) * RPI * RB);
-  };
-
-  f32x16 acc[MI][NI];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
+  const int lr = lane / CPR;  // row inside a load instruction's rows
   int aoffs[MI], boffs[NI];
   const int lrow = lane & 31;
 #pragma unroll
@@ -378,100 +360,228 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
   for (int j = 0; j < NI; ++j) boffs[j] = (BM + wn * WTN + j * 32 + lrow) * RB;
   const int rsw = swz<CPR>(lrow);  // the same for every fragment row of this lane
 
-  const int KT = K / BK;
+  struct Tile {
+    int row0, rows, n0, N, K;
+    const bf16* bw;    // weight rows of this group
+    const bf16* bias;  // bias of this group, or null
+  };
+  // Tile fields are the same for the whole block: readfirstlane keeps them in
+  // scalar registers (the vector register budget is tight).
+  auto decode = [&](int tt) {
+    int rt, nt;
+    decode_tile(a, tt, total, &rt, &nt);
+    rt = __builtin_amdgcn_readfirstlane(rt);
+    nt = __builtin_amdgcn_readfirstlane(nt);
+    const RowTile& rtile = a.tiles[rt];
+    const int group = __builtin_amdgcn_readfirstlane(rtile.group);
+    const bool sh = (group == a.E);
+    Tile c;
+    c.row0 = __builtin_amdgcn_readfirstlane(rtile.row0);
+    c.rows = __builtin_amdgcn_readfirstlane(rtile.rows);
+    c.n0 = nt * BN;
+    c.N = sh ? a.Ns : a.N;
+    c.K = sh ? a.Ks : a.K;
+    c.bw = static_cast<const bf16*>(sh ? a.Wsh : a.W) +
+           (sh ? 0 : static_cast<int64_t>(group) * c.N * c.K);
+    c.bias = static_cast<const bf16*>(sh ? a.bias_sh : a.bias);
+    if (c.bias && !sh) c.bias += static_cast<int64_t>(group) * c.N;
+    return c;
+  };
+  // token row (up-projection) or H row (down-projection) behind A row r
+  auto arow_of = [&](const Tile& c, int r) -> int {
+    const int rr = min(r, c.rows - 1);
+    return UP ? a.row_token[c.row0 + rr] : c.row0 + rr;
+  };
+  // Load instruction j of this wave fills tile rows (wave + j NW) RPI ...; the
+  // first JA instructions hold A rows, the rest B rows.  Sources are kept as
+  // 32-bit byte offsets from the tensor (A) or the group's weights (B).
+  constexpr int JA = BM / (RPI * NW);
+  static_assert(BM % (RPI * NW) == 0, "A rows per load instruction");
+  auto a_off = [&](int j, int arow) -> uint32_t {
+    const int r = (wave + j * NW) * RPI + lr;
+    const int chunk = (lane % CPR) ^ swz<CPR>(r);
+    return static_cast<uint32_t>(arow) * static_cast<uint32_t>(a.lda * 2) + chunk * 16;
+  };
+  auto b_off = [&](const Tile& c, int j) -> uint32_t {
+    const int r = (wave + j * NW) * RPI + lr;
+    const int chunk = (lane % CPR) ^ swz<CPR>(r);
+    const int nn = min(c.n0 + r - BM, c.N - 1);
+    return static_cast<uint32_t>(nn) * static_cast<uint32_t>(c.K * 2) + chunk * 16;
+  };
+  auto gate_of = [&](const Tile& c, int m) -> float {
+    return m < c.rows ? a.row_gate[c.row0 + m] : 0.f;
+  };
+
+  Tile cur = decode(t);
+  uint32_t src[JPW];
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < KT) issue(p, p * BK);
-  for (int kt = 0; kt < KT; ++kt) {
-    // this lane's loads of stage kt have landed once at most the loads of the
-    // later stages already issued (min(NS - 2, KT - 1 - kt) of them) are pending
-    if (kt + NS - 2 < KT) {
-      wait_vmcnt<JPW * (NS - 2)>();
-    } else if constexpr (NS > 2) {
-      if (kt + 1 == KT) wait_vmcnt<0>();
-      else if constexpr (NS > 3) {
-        if (kt + 2 == KT) wait_vmcnt<JPW>();
-        else wait_vmcnt<0>();
-      }
-    }
-    // Every lane's loads of stage kt landed; every wave finished reading stage
-    // kt - 1 (its fragments were consumed by MFMAs already issued).  A plain
-    // s_barrier: a workgroup fence here would also wait for the later stages.
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (kt + NS - 1 < KT) issue((kt + NS - 1) % NS, (kt + NS - 1) * BK);
-    const char* st = smem + (kt % NS) * STAGE;
-    // fragments of k16 step s + 1 are read while the MFMAs of step s run
-    bf16x8_t fa[2][MI], fb[2][NI];
-    auto frags = [&](int s, int buf) {
-      const int cb = ((2 * s + (lane >> 5)) ^ rsw) * 16;
+  for (int j = 0; j < JPW; ++j)
+    src[j] = j < JA ? a_off(j, arow_of(cur, (wave + j * NW) * RPI + lr)) : b_off(cur, j);
+  if (!UP) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-        fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + aoffs[i] + cb);
+    for (int g = 0; g < GPT; ++g)
+      if (tid + g * NT < BM) gate_s[0][tid + g * NT] = gate_of(cur, tid + g * NT);
+  }
+  const char* abase = static_cast<const char*>(a.A);
+  const char* bbase = reinterpret_cast<const char*>(cur.bw);
+  auto issue = [&](int stage, int k0) {
 #pragma unroll
-      for (int j = 0; j < NI; ++j)
-        fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boffs[j] + cb);
-    };
-    frags(0, 0);
+    for (int j = 0; j < JPW; ++j)
+      lds_dma16((j < JA ? abase : bbase) + src[j] + static_cast<uint32_t>(k0) * 2,
+                smem + stage * STAGE + (wave + j * NW) * RPI * RB);
+  };
+  {
+    const int KT = cur.K / BK;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (s + 1 < KS) frags(s + 1, (s + 1) & 1);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
-                                                              acc[i][j], 0, 0, 0);
-    }
-    // Instruction order for the scheduler: the first step's fragment reads, then
-    // for each step its MFMAs with the next step's reads spread between them,
-    // so LDS latency hides under MFMA issue instead of stalling each step.
-    constexpr int NR = MI + NI, NM = MI * NI;
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (s + 1 < KS) {
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        if (NM % NR) __builtin_amdgcn_sched_group_barrier(0x008, NM % NR, 0);
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-      }
-    }
+    for (int p = 0; p < NS - 1; ++p)
+      if (p < KT) issue(p, p * BK);
   }
 
+  int gb = 0;
+  for (;;) {
+    const int tn = t + gridDim.x;
+    const bool has_next = PERSIST && tn < total;
+    Tile nxt = cur;
+    if (has_next) nxt = decode(tn);
+    int ntok[JA];
+    float ngate[GPT];
 #pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int n = n0 + wn * WTN + j * 32 + (lane & 31);
-    if (n >= N) continue;
-    const float bv = bias ? bf16_to_f32(bias[n].bits) : 0.f;
+    for (int j = 0; j < JA; ++j) ntok[j] = 0;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+    for (int g = 0; g < GPT; ++g) ngate[g] = 0.f;
+
+    f32x16 acc[MI][NI];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-        if (m >= rows) continue;
-        const float z = acc[i][j][q] + bv;
-        const int64_t o = static_cast<int64_t>(row0 + m) * a.ldo + n;
-        if (UP) {
-          const float h = (a.act == MOE_ACT_RELU) ? fmaxf(z, 0.f) : gelu_erf(z);
-          static_cast<bf16*>(a.out)[o] = bf16{f32_to_bf16(h)};
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    const int KT = cur.K / BK;
+    for (int kt = 0; kt < KT; ++kt) {
+      // this lane's loads of stage kt have landed once at most the loads of the
+      // later stages already issued (min(NS - 2, KT - 1 - kt) of them) are
+      // pending; the first step of a tile waits for everything (the previous
+      // tile's epilogue stores were issued after this tile's first stages)
+      if (kt == 0) {
+        wait_vmcnt<0>();
+      } else if (kt + NS - 2 < KT) {
+        wait_vmcnt<JPW * (NS - 2)>();
+      } else if constexpr (NS > 2) {
+        if (kt + 1 == KT) wait_vmcnt<0>();
+        else if constexpr (NS > 3) {
+          if (kt + 2 == KT) wait_vmcnt<JPW>();
+          else wait_vmcnt<0>();
         } else {
-          static_cast<float*>(a.out)[o] = gate_s[m] * z;
+          wait_vmcnt<0>();
         }
       }
+      // Every lane's loads of stage kt landed; every wave finished reading stage
+      // kt - 1.  A plain s_barrier: a workgroup fence would also wait for the
+      // later stages.
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (kt == 0 && has_next) {
+        // next tile's token rows and gates: loaded now, used after the K loop
+#pragma unroll
+        for (int j = 0; j < JA; ++j) ntok[j] = arow_of(nxt, (wave + j * NW) * RPI + lr);
+        if (!UP) {
+#pragma unroll
+          for (int g = 0; g < GPT; ++g)
+            if (tid + g * NT < BM) ngate[g] = gate_of(nxt, tid + g * NT);
+        }
+      }
+      if (kt + NS - 1 < KT) issue((kt + NS - 1) % NS, (kt + NS - 1) * BK);
+      const char* st = smem + (kt % NS) * STAGE;
+      // fragments of k16 step s + 1 are read while the MFMAs of step s run
+      bf16x8_t fa[2][MI], fb[2][NI];
+      auto frags = [&](int s, int buf) {
+        const int cb = ((2 * s + (lane >> 5)) ^ rsw) * 16;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + aoffs[i] + cb);
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boffs[j] + cb);
+      };
+      frags(0, 0);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) frags(s + 1, (s + 1) & 1);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
+                                                                acc[i][j], 0, 0, 0);
+      }
+      // Instruction order for the scheduler: the first step's fragment reads,
+      // then each step's MFMAs with the next step's reads spread between them.
+      __builtin_amdgcn_sched_group_barrier(0x100, MI + NI, 0);
+      sched_steps<0, KS - 1, MI + NI, MI * NI>();
+      __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
     }
+    // Every wave is done reading this tile's stages (and every load of it has
+    // landed: the last iteration waited for all of them).
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (has_next) {
+#pragma unroll
+      for (int j = 0; j < JPW; ++j) src[j] = j < JA ? a_off(j, ntok[j]) : b_off(nxt, j);
+      bbase = reinterpret_cast<const char*>(nxt.bw);
+      const int KTn = nxt.K / BK;
+#pragma unroll
+      for (int p = 0; p < NS - 1; ++p)
+        if (p < KTn) issue(p, p * BK);
+      if (!UP) {
+#pragma unroll
+        for (int g = 0; g < GPT; ++g)
+          if (tid + g * NT < BM) gate_s[gb ^ 1][tid + g * NT] = ngate[g];
+      }
+    }
+
+    // epilogue of tile t (gates of this tile are in gate_s[gb])
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int n = cur.n0 + wn * WTN + j * 32 + (lane & 31);
+      if (n >= cur.N) continue;
+      const float bv = cur.bias ? bf16_to_f32(cur.bias[n].bits) : 0.f;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m = wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+          if (m >= cur.rows) continue;
+          const float z = acc[i][j][q] + bv;
+          const int64_t o = static_cast<int64_t>(cur.row0 + m) * a.ldo + n;
+          if (UP) {
+            const float h = (a.act == MOE_ACT_RELU) ? fmaxf(z, 0.f) : gelu_erf(z);
+            static_cast<bf16*>(a.out)[o] = bf16{f32_to_bf16(h)};
+          } else {
+            static_cast<float*>(a.out)[o] = gate_s[gb][m] * z;
+          }
+        }
+        // one 32x32 block at a time: keeps the epilogue's temporaries few
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (!has_next) break;
+    cur = nxt;
+    t = tn;
+    gb ^= 1;
   }
 }
 
 // Row tiles of BM rows per group, groups in order, from the dispatch offsets.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
-                                                           int G, int BM,
+                                                           int G, int BM, int E, int k,
+                                                           const int32_t* __restrict__ row_token,
+                                                           const int32_t* __restrict__ row_slot,
+                                                           const float* __restrict__ topk_w,
                                                            RowTile* __restrict__ tiles,
-                                                           int32_t* __restrict__ ntiles) {
+                                                           int32_t* __restrict__ ntiles,
+                                                           float* __restrict__ row_gate) {
   __shared__ int32_t sc[2][kMaxExperts];
   const int g = threadIdx.x;
   int rows = 0, m = 0;
@@ -503,6 +613,10 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     }
   }
   if (g == kMaxExperts - 1) ntiles[0] = sc[src][g];
+  // gate of every row: topk_w of its (token, slot); 1 for the shared expert's rows
+  const int routed = offsets[E], nrows = offsets[G];
+  for (int r = g; r < nrows; r += kMaxExperts)
+    row_gate[r] = r < routed ? topk_w[static_cast<int64_t>(row_token[r]) * k + row_slot[r]] : 1.0f;
 }
 
 static GemmArgs up_args(const FfnArgs& f, int BN) {
@@ -516,6 +630,7 @@ static GemmArgs up_args(const FfnArgs& f, int BN) {
   u.row_token = f.row_token;
   u.row_slot = f.row_slot;
   u.topk_w = f.topk_w;
+  u.row_gate = f.row_gate;
   u.k = f.k;
   u.W = f.W1;
   u.Wsh = f.Ws1;
@@ -565,41 +680,56 @@ static void run_generic(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
         <<<static_cast<unsigned>(gd), WM * WN * 64, 0, st>>>(dn);
 }
 
-template <int BM, int BNU, int BND, int BK, int NS, int WM, int WN>
+// Compute units of the current device (host query, no synchronisation).
+static int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  return n;
+}
+
+// Persistent launch: as many blocks as can be resident, capped by the tile
+// count; otherwise one block per tile.
+template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, bool UP>
+static void launch_dma(const GemmArgs& g, int64_t tiles, hipStream_t st) {
+  if (tiles <= 0) return;
+  auto kern = grouped_gemm_dma_kernel<BM, BN, BK, NS, WM, WN, OCC, PERSIST, UP>;
+  const size_t lds = static_cast<size_t>(NS) * (BM + BN) * BK * 2;
+  static int per_cu = [&] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, WM * WN * 64, lds) != hipSuccess ||
+        b < 1)
+      b = 1;
+    return b;
+  }();
+  const int64_t grid =
+      PERSIST ? std::min<int64_t>(tiles, static_cast<int64_t>(cu_count()) * per_cu) : tiles;
+  kern<<<static_cast<unsigned>(grid), WM * WN * 64, lds, st>>>(g);
+}
+
+template <int BM, int BNU, int BND, int BK, int NS, int WM, int WN, int OCC, int PERSIST>
 static void run_dma(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const GemmArgs u = up_args(f, BNU);
-  const int64_t gu = gp.tiles_max * u.n_tiles_n;
-  const size_t lu = static_cast<size_t>(NS) * (BM + BNU) * BK * 2;
-  if (gu > 0) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<BM, BNU, BK, NS, WM, WN, true>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lu));
-    (void)attr;
-    grouped_gemm_dma_kernel<BM, BNU, BK, NS, WM, WN, true>
-        <<<static_cast<unsigned>(gu), WM * WN * 64, lu, st>>>(u);
-  }
+  launch_dma<BM, BNU, BK, NS, WM, WN, OCC, PERSIST, true>(u, gp.tiles_max * u.n_tiles_n, st);
   const GemmArgs dn = down_args(f, BND);
-  const int64_t gd = gp.tiles_max * dn.n_tiles_n;
-  const size_t ld = static_cast<size_t>(NS) * (BM + BND) * BK * 2;
-  if (gd > 0) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&grouped_gemm_dma_kernel<BM, BND, BK, NS, WM, WN, false>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ld));
-    (void)attr;
-    grouped_gemm_dma_kernel<BM, BND, BK, NS, WM, WN, false>
-        <<<static_cast<unsigned>(gd), WM * WN * 64, ld, st>>>(dn);
-  }
+  launch_dma<BM, BND, BK, NS, WM, WN, OCC, PERSIST, false>(dn, gp.tiles_max * dn.n_tiles_n, st);
 }
 
 hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const int G = f.E + (f.Fs > 0 ? 1 : 0);
-  build_tiles_kernel<<<1, kMaxExperts, 0, st>>>(f.offsets, G, gp.BM, f.tiles, f.ntiles);
+  build_tiles_kernel<<<1, kMaxExperts, 0, st>>>(f.offsets, G, gp.BM, f.E, f.k, f.row_token,
+                                                f.row_slot, f.topk_w, f.tiles, f.ntiles,
+                                                f.row_gate);
   switch (gp.shape) {
     case kGemmF32: run_generic<float, 64, 64, 64, 32, 2, 2>(gp, f, st); break;
     case kGemmBf16Large: run_generic<bf16, 128, 128, 128, 64, 2, 2>(gp, f, st); break;
     case kGemmBf16Mid: run_generic<bf16, 64, 128, 128, 64, 1, 4>(gp, f, st); break;
     case kGemmBf16Small: run_generic<bf16, 32, 128, 128, 64, 1, 4>(gp, f, st); break;
-#define MOE_RUN_DMA(C) run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN>(gp, f, st)
+#define MOE_RUN_DMA(C) \
+  run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN, C.OCC, C.PERSIST>(gp, f, st)
     case kGemmDmaLarge: MOE_RUN_DMA(kDmaLarge); break;
     case kGemmDmaMid: MOE_RUN_DMA(kDmaMid); break;
     case kGemmDmaSmall: MOE_RUN_DMA(kDmaSmall); break;

@@ -30,12 +30,15 @@ enum GemmShape {
 // Tile configurations of the LDS-DMA grouped GEMM.  The host plan (row-tile
 // height for the tile list) and the launcher read the same table.
 struct DmaCfg {
-  int BM, BNU, BND, BK, NS, WM, WN;  // rows, up/down columns, K step, stages, wave grid
+  // rows, up/down columns, K step, stages, wave grid, the waves per SIMD the
+  // register budget is sized for, and whether blocks stay resident and walk
+  // several tiles (1) or each block takes one tile (0)
+  int BM, BNU, BND, BK, NS, WM, WN, OCC, PERSIST;
 };
-constexpr DmaCfg kDmaLarge{256, 256, 256, 64, 2, 2, 4};   // >= 768 rows per expert
-constexpr DmaCfg kDmaMid{128, 256, 256, 64, 2, 2, 4};     // >= 256
-constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 4, 1, 4};    // >= 48
-constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 4, 1, 4};   // fewer: weight streaming
+constexpr DmaCfg kDmaLarge{256, 256, 256, 64, 2, 2, 4, 2, 0};   // >= 768 rows per expert
+constexpr DmaCfg kDmaMid{128, 256, 256, 64, 2, 2, 4, 2, 1};     // >= 256
+constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 4, 1, 4, 2, 1};    // >= 48
+constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 4, 1, 4, 2, 0};   // fewer: weight streaming
 
 struct GemmPlan {
   int shape;        // GemmShape
@@ -54,6 +57,7 @@ struct FfnArgs {
   float* y_rows;     // [rows_max, d]
   RowTile* tiles;    // [tiles_max]
   int32_t* ntiles;   // [1]
+  float* row_gate;   // [rows_max]
 };
 
 hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const float* Wg,

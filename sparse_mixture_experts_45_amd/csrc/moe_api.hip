@@ -13,7 +13,7 @@ struct Layout {
   GemmPlan gp;
   int64_t rows_max;  // T*k + (Fs ? T : 0)
   size_t part, stat, hist, base, topk_idx, topk_w, counts, kept, offsets, row_token, row_slot,
-      inv, tiles, ntiles, H, y_rows, total;
+      inv, tiles, ntiles, row_gate, H, y_rows, total;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -126,6 +126,7 @@ Layout layout(const moe_config* c) {
   L.inv = take(sizeof(int32_t) * T * k);
   L.tiles = take(sizeof(RowTile) * L.gp.tiles_max);
   L.ntiles = take(sizeof(int32_t));
+  L.row_gate = take(sizeof(float) * L.rows_max);
   L.H = take(elt * L.rows_max * ldh);
   L.y_rows = take(sizeof(float) * L.rows_max * c->d_model);
   L.total = o;
@@ -180,6 +181,7 @@ moe_status run_ffn(const moe_config* c, const Layout& L, const void* x, const mo
   f.y_rows = y_rows;
   f.tiles = reinterpret_cast<RowTile*>(at(ws, L.tiles));
   f.ntiles = reinterpret_cast<int32_t*>(at(ws, L.ntiles));
+  f.row_gate = reinterpret_cast<float*>(at(ws, L.row_gate));
   return hip_status(launch_ffn(L.gp, f, st));
 }
 
