@@ -11,7 +11,8 @@ struct RoutePlan {
   int64_t T;
   int d, E, k, renorm;
   int S, kchunk;  // router score split over d: S chunks of kchunk columns
-  int lpt, vpl;   // gate: lanes per token, values per lane
+  int lpt, vpl;   // gate: lanes per token (16 or 64), values per lane
+  int fused;      // scores and gate in one kernel (bf16, E <= 64, S = 1)
   int nb;         // gate blocks = ceil(T / kGateTokens)
 };
 

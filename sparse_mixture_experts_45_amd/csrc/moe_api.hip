@@ -80,17 +80,24 @@ RoutePlan route_plan(const moe_config* c) {
   p.k = c->top_k;
   p.renorm = c->renormalize;
   p.nb = static_cast<int>(ceil_div(c->T, kGateTokens));
-  // split d so the score kernel has >= ~512 blocks, chunks >= 128 columns
-  const int64_t base_blocks = ceil_div(c->T, 64) * ceil_div(c->n_experts, c->n_experts <= 16 ? 16 : 64);
-  int S = static_cast<int>(std::max<int64_t>(1, ceil_div(512, std::max<int64_t>(1, base_blocks))));
-  S = std::min(S, std::max(1, c->d_model / 128));
-  S = std::min(S, 16);
+  // bf16 layers whose experts fit one score tile (E <= 64): one K chunk, and
+  // the gate runs inside the score kernel.  Otherwise split d so the score
+  // kernel has >= ~256 blocks, each K slice of a block keeping >= 2 K steps.
+  const int TE = c->n_experts <= 16 ? 16 : 64;
+  const int QK = 16 / (TE / 16);
+  p.fused = c->dtype == MOE_BF16 && c->n_experts <= 64;
+  int S = 1;
+  if (!p.fused) {
+    const int64_t base_blocks = ceil_div(c->T, 64) * ceil_div(c->n_experts, TE);
+    S = static_cast<int>(std::max<int64_t>(1, ceil_div(256, std::max<int64_t>(1, base_blocks))));
+    S = std::min(S, std::max(1, c->d_model / (QK * 64)));
+    S = std::min(S, 16);
+  }
   p.kchunk = static_cast<int>(align_up(ceil_div(c->d_model, S), 32));
   p.S = static_cast<int>(ceil_div(c->d_model, p.kchunk));
-  int lpt = 1;
-  while (lpt < c->n_experts && lpt < 64) lpt <<= 1;
-  p.lpt = lpt;
-  const int need = static_cast<int>(ceil_div(c->n_experts, lpt));
+  // gate: 16 lanes per token up to 256 experts (DPP-only reductions), else 64
+  p.lpt = c->n_experts <= 256 ? 16 : 64;
+  const int need = static_cast<int>(ceil_div(c->n_experts, p.lpt));
   int vpl = 1;
   while (vpl < need) vpl <<= 1;
   p.vpl = vpl;

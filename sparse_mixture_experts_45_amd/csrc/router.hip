@@ -11,36 +11,218 @@
 namespace moe {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-// ---------------------------------------------------------------------------
-// Scores.  Block = 4 waves; tile = 64 tokens x TE experts (TE = 16 or 64) over
-// one K chunk.  Each wave owns 16 tokens and all TE experts of the tile
-// (TE / 16 fp32 MFMA 16x16x4 accumulators).  The next K step is loaded into
-// registers while the current one is multiplied.  Partial sums of chunk s go
-// to part[s][T][E]; the gate kernel adds the chunks in order s = 0, 1, ...
-// so the result is deterministic.
-// ---------------------------------------------------------------------------
 constexpr int kRtM = 64, kRtK = 32;
+constexpr int kRw = 16;  // waves per block of the bf16 score kernel and of the gate
 
-template <typename XT>
-struct XLoad;
-template <>
-struct XLoad<bf16> {  // 8 bf16 per 16-byte chunk, 4 chunks per 32-wide row
-  static constexpr int kPer = 8;
-};
-template <>
-struct XLoad<float> {  // 4 floats per chunk, 8 chunks per row
-  static constexpr int kPer = 4;
+// ---------------------------------------------------------------------------
+// Butterfly exchange inside a group of lanes.  Levels 1 and 2 swap lanes of a
+// quad, levels 4 and 8 mirror a half row / a row (DPP, no LDS traffic); 16 and
+// 32 cross rows.  For an all-reduce with a commutative combine, a mirror
+// partner is as good as the xor partner: after the previous levels every lane
+// of the smaller group already holds that group's result.
+// ---------------------------------------------------------------------------
+template <int O>
+__device__ __forceinline__ int xchg(int v) {
+  if constexpr (O == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (O == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (O == 4) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  else if constexpr (O == 8) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  else return __shfl_xor(v, O);
+}
+template <int O>
+__device__ __forceinline__ float xchg(float v) {
+  return __int_as_float(xchg<O>(__float_as_int(v)));
+}
+
+template <int LPT, int O = 1>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (O < LPT) return group_max<LPT, O * 2>(fmaxf(v, xchg<O>(v)));
+  else return v;
+}
+template <int LPT, int O = 1>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (O < LPT) return group_sum<LPT, O * 2>(v + xchg<O>(v));
+  else return v;
+}
+// larger value wins; equal values go to the lower expert index
+template <int LPT, int O = 1>
+__device__ __forceinline__ void group_argmax(float& bv, int& be) {
+  if constexpr (O < LPT) {
+    const float ov = xchg<O>(bv);
+    const int oe = xchg<O>(be);
+    if (ov > bv || (ov == bv && oe < be)) {
+      bv = ov;
+      be = oe;
+    }
+    group_argmax<LPT, O * 2>(bv, be);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gate of one block of kGateTokens tokens, kRw waves of kGateTokens / kRw
+// tokens.  A token's E scores are spread over LPT lanes (16, or 64 for E > 256),
+// VPL values per lane: expert e = s + v * LPT for lane sub-index s.  Max, sum
+// and each of the k argmax rounds are all-reduces inside the LPT group, so
+// every lane of the group ends with identical values and lane s keeps the
+// selections of rounds s, s + LPT, ...  Ties pick the lower expert index.
+// Per-block sums of the probabilities (fp64) are reduced in a fixed order; the
+// per-block count of (token, slot) pairs per expert uses LDS integer atomics,
+// whose result does not depend on their order.  `logit(tl, e)` gives the raw
+// score (bias excluded) of local token tl and expert e.
+// ---------------------------------------------------------------------------
+template <int EM>
+struct GateSmem {  // EM: largest expert count the block handles
+  double red_d[4][EM];
+  int32_t hcnt[EM];
 };
 
-template <typename XT, int TE>
-__global__ __launch_bounds__(256) void router_scores_kernel(const XT* __restrict__ x,
-                                                            const float* __restrict__ Wg,
-                                                            int64_t T, int d, int E, int kchunk,
-                                                            float* __restrict__ part) {
-  constexpr int XP = XLoad<XT>::kPer;
-  constexpr int XCH = kRtM * kRtK / XP;  // x chunks per stage
-  constexpr int WCH = TE * kRtK / 4;     // W chunks (float4) per stage
+template <int LPT, int VPL, int EM, class Logit>
+__device__ __forceinline__ void gate_block(Logit logit, GateSmem<EM>& sm, int64_t blk,
+                                           const float* __restrict__ bg, int64_t T, int E,
+                                           int k, int renorm, int32_t* __restrict__ topk_idx,
+                                           float* __restrict__ topk_w, float* __restrict__ probs,
+                                           double* __restrict__ stat_part,
+                                           int32_t* __restrict__ hist) {
+  constexpr int TPW = kGateTokens / kRw;  // tokens per wave
+  constexpr int TPS = kWave / LPT;        // tokens per wave step
+  constexpr int ITERS = (TPW + TPS - 1) / TPS;
+  constexpr int NSL = (kMaxTopK + LPT - 1) / LPT;  // output slots per lane
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = lane & (LPT - 1);
+  const int grp = lane / LPT;
+  for (int e = tid; e < E; e += kRw * 64) sm.hcnt[e] = 0;
+  __syncthreads();
+
+  double sacc[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) sacc[v] = 0.0;
+
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int local = it * TPS + grp;
+    const int tl = wave * TPW + local;
+    const int64_t t = blk * kGateTokens + tl;
+    const bool vt = local < TPW && t < T;
+    float l[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = s + v * LPT;
+      float z = -INFINITY;
+      if (vt && e < E) {
+        z = logit(tl, e);
+        if (bg) z += bg[e];
+      }
+      l[v] = z;
+    }
+    float m = l[0];
+#pragma unroll
+    for (int v = 1; v < VPL; ++v) m = fmaxf(m, l[v]);
+    m = group_max<LPT>(m);
+    float pz[VPL];
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      pz[v] = (l[v] == -INFINITY) ? 0.f : expf(l[v] - m);
+      sum += pz[v];
+    }
+    sum = group_sum<LPT>(sum);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = s + v * LPT;
+      const float p = pz[v] / sum;
+      if (vt && e < E) {
+        if (probs) probs[t * E + e] = p;
+        sacc[v] += static_cast<double>(p);
+      }
+    }
+
+    // top-k: k rounds of a group argmax over the not-yet-taken experts
+    uint32_t taken = 0;
+    float selsum = 0.f;
+    float myp[NSL];
+    int mye[NSL];
+#pragma unroll
+    for (int j = 0; j < NSL; ++j) {
+      myp[j] = 0.f;
+      mye[j] = 0;
+    }
+    for (int i = 0; i < k; ++i) {
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int e = s + v * LPT;
+        if (e < E && !((taken >> v) & 1u) && (l[v] > bv || (l[v] == bv && e < be))) {
+          bv = l[v];
+          be = e;
+        }
+      }
+      group_argmax<LPT>(bv, be);
+      if ((be & (LPT - 1)) == s) {
+        const int v = be / LPT;
+#pragma unroll
+        for (int vv = 0; vv < VPL; ++vv)
+          if (vv == v) taken |= 1u << vv;
+        if (vt) atomicAdd(&sm.hcnt[be], 1);
+      }
+      const float p = expf(bv - m) / sum;  // same value the owner lane computed
+      selsum += p;
+#pragma unroll
+      for (int j = 0; j < NSL; ++j)
+        if (i == s + j * LPT) {
+          myp[j] = p;
+          mye[j] = be;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NSL; ++j) {
+      const int slot = s + j * LPT;
+      if (vt && slot < k) {
+        topk_idx[t * k + slot] = mye[j];
+        topk_w[t * k + slot] = renorm ? myp[j] / selsum : myp[j];
+      }
+    }
+  }
+
+  // reduce across the token groups of the wave (lanes with the same s), then
+  // across waves in a fixed order: slot w % 4 accumulates waves w % 4, w % 4 + 4,
+  // ... in wave order, then the slots are added in order
+#pragma unroll
+  for (int v = 0; v < VPL; ++v)
+    for (int o = LPT; o < kWave; o <<= 1) sacc[v] += __shfl_xor(sacc[v], o);
+  for (int round = 0; round < kRw / 4; ++round) {
+    if (grp == 0 && (wave >> 2) == round) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int e = s + v * LPT;
+        if (e < E) sm.red_d[wave & 3][e] = round ? sm.red_d[wave & 3][e] + sacc[v] : sacc[v];
+      }
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < E; e += kRw * 64) {
+    const double tot = ((sm.red_d[0][e] + sm.red_d[1][e]) + sm.red_d[2][e]) + sm.red_d[3][e];
+    stat_part[blk * E + e] = tot;
+    hist[blk * E + e] = sm.hcnt[e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scores, fp32 x.  Block = 4 waves; tile = 64 tokens x TE experts (TE = 16 or
+// 64) over one K chunk; each wave owns 16 tokens (fp32 MFMA 16x16x4).  The
+// next K step is loaded into registers while the current one is multiplied.
+// Partial sums of chunk s go to part[s][T][E].
+// ---------------------------------------------------------------------------
+template <int TE>
+__global__ __launch_bounds__(256) void router_scores_f32_kernel(const float* __restrict__ x,
+                                                                const float* __restrict__ Wg,
+                                                                int64_t T, int d, int E,
+                                                                int kchunk,
+                                                                float* __restrict__ part) {
+  constexpr int XCH = kRtM * kRtK / 4;  // x float4 chunks per stage
+  constexpr int WCH = TE * kRtK / 4;    // W float4 chunks per stage
   constexpr int XPT = (XCH + 255) / 256, WPT = (WCH + 255) / 256;
   constexpr int NB = TE / 16;
   __shared__ float xs[kRtM][kRtK + 1];
@@ -52,45 +234,26 @@ __global__ __launch_bounds__(256) void router_scores_kernel(const XT* __restrict
   const int kb = s * kchunk;
   const int ke = min(d, kb + kchunk);
 
-  float xr[XPT][XP];
-  float wr[WPT][4];
+  float4 xr[XPT], wr[WPT];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int c = tid + i * 256;
-      const int r = c / (kRtK / XP), kc = (c % (kRtK / XP)) * XP;
+      const int r = c / (kRtK / 4), kc = (c % (kRtK / 4)) * 4;
       const int64_t t = t0 + r;
-      const int k = k0 + kc;
-      const bool ok = c < XCH && t < T && k < ke;  // ke and k are multiples of 8
-      if constexpr (XP == 8) {
-        uint4 u = ok ? *reinterpret_cast<const uint4*>(x + t * d + k) : make_uint4(0, 0, 0, 0);
-        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          xr[i][2 * q] = __uint_as_float(w4[q] << 16);
-          xr[i][2 * q + 1] = __uint_as_float(w4[q] & 0xffff0000u);
-        }
-      } else {
-        float4 f = ok ? *reinterpret_cast<const float4*>(x + t * d + k) : make_float4(0, 0, 0, 0);
-        xr[i][0] = f.x;
-        xr[i][1] = f.y;
-        xr[i][2] = f.z;
-        xr[i][3] = f.w;
-      }
+      const int kk = k0 + kc;
+      xr[i] = (c < XCH && t < T && kk < ke) ? *reinterpret_cast<const float4*>(x + t * d + kk)
+                                           : make_float4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
       const int c = tid + i * 256;
       const int r = c / (kRtK / 4), kc = (c % (kRtK / 4)) * 4;
       const int e = e0 + r;
-      const int k = k0 + kc;
-      const bool ok = c < WCH && e < E && k < ke;
-      float4 f = ok ? *reinterpret_cast<const float4*>(Wg + static_cast<int64_t>(e) * d + k)
-                    : make_float4(0, 0, 0, 0);
-      wr[i][0] = f.x;
-      wr[i][1] = f.y;
-      wr[i][2] = f.z;
-      wr[i][3] = f.w;
+      const int kk = k0 + kc;
+      wr[i] = (c < WCH && e < E && kk < ke)
+                  ? *reinterpret_cast<const float4*>(Wg + static_cast<int64_t>(e) * d + kk)
+                  : make_float4(0, 0, 0, 0);
     }
   };
   auto sstore = [&]() {
@@ -98,9 +261,11 @@ __global__ __launch_bounds__(256) void router_scores_kernel(const XT* __restrict
     for (int i = 0; i < XPT; ++i) {
       const int c = tid + i * 256;
       if (c < XCH) {
-        const int r = c / (kRtK / XP), kc = (c % (kRtK / XP)) * XP;
-#pragma unroll
-        for (int q = 0; q < XP; ++q) xs[r][kc + q] = xr[i][q];
+        const int r = c / (kRtK / 4), kc = (c % (kRtK / 4)) * 4;
+        xs[r][kc] = xr[i].x;
+        xs[r][kc + 1] = xr[i].y;
+        xs[r][kc + 2] = xr[i].z;
+        xs[r][kc + 3] = xr[i].w;
       }
     }
 #pragma unroll
@@ -108,8 +273,10 @@ __global__ __launch_bounds__(256) void router_scores_kernel(const XT* __restrict
       const int c = tid + i * 256;
       if (c < WCH) {
         const int r = c / (kRtK / 4), kc = (c % (kRtK / 4)) * 4;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ws[r][kc + q] = wr[i][q];
+        ws[r][kc] = wr[i].x;
+        ws[r][kc + 1] = wr[i].y;
+        ws[r][kc + 2] = wr[i].z;
+        ws[r][kc + 3] = wr[i].w;
       }
     }
   };
@@ -117,7 +284,6 @@ __global__ __launch_bounds__(256) void router_scores_kernel(const XT* __restrict
   f32x4 acc[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   gload(kb);
   for (int k0 = kb; k0 < ke; k0 += kRtK) {
     __syncthreads();
@@ -147,150 +313,170 @@ __global__ __launch_bounds__(256) void router_scores_kernel(const XT* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Gate.  One block handles kGateTokens tokens with 8 waves of 8 tokens each.
-// A token's E scores are spread over LPT lanes (LPT = min(64, next pow2 of E)),
-// VPL values per lane, expert e = s + v * LPT for lane sub-index s.  Max, sum,
-// and each of the k argmax rounds are xor-shuffle trees inside the LPT group,
-// so every lane of the group ends with identical values.  Ties pick the lower
-// expert index.  Per-block sums of the probabilities (fp64) are reduced in a
-// fixed order; the per-block count of (token, slot) pairs per expert uses LDS
-// integer atomics, whose result does not depend on their order.
+// Scores, bf16 x, on bf16 MFMA with fp32 accumulation.  Each fp32 router weight
+// is cut into three bf16 parts whose sum is exactly w: hi = w with the low 16
+// bits cleared, mid = the same cut of r = w - hi, lo = r - mid (at most 8
+// significant bits left, so it is a bf16 value; weights in the normal range).
+// x is exactly bf16, so every product x * part is exact in fp32 and the score
+// sum_k x w = S(hi) + S(mid + lo) is accumulated in fp32: the precision of an
+// fp32 dot product.
+//
+// Block = 16 waves over 64 tokens x TE experts (TE = 16 or 64) and one K chunk.
+// Wave w takes expert block w % (TE / 16) and K slice w / (TE / 16): the chunk's
+// 32-wide K steps are dealt round-robin to the slices.  A wave multiplies all
+// four 16-token row blocks with its 16 experts (v_mfma_f32_16x16x32_bf16: lane l
+// supplies row l % 16, k = (l / 16) * 8 + 0..7), loading its x and W fragments
+// straight from global memory, two K steps in flight.  The slices' partial
+// tiles are added in slice order through LDS.  With FUSE (one chunk, E <= TE)
+// the gate runs in the same block on those scores; otherwise chunk s goes to
+// part[s][T][E].
 // ---------------------------------------------------------------------------
-// Sum of the score chunks in chunk order, written over chunk 0.
-__global__ __launch_bounds__(256) void router_reduce_kernel(float* __restrict__ part, int S,
-                                                            int64_t n) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= n) return;
-  float z = part[i];
-  for (int sp = 1; sp < S; ++sp) z += part[static_cast<int64_t>(sp) * n + i];
-  part[i] = z;
+__device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);  // a.hi16 | b.hi16 << 16
 }
 
-template <int VPL, int kGateWaves>
-__global__ __launch_bounds__(kGateWaves * 64) void router_gate_kernel(
-    const float* __restrict__ logit, const float* __restrict__ bg, int64_t T, int E, int k,
-    int renorm, int lpt, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ probs, double* __restrict__ stat_part, int32_t* __restrict__ hist) {
-  constexpr int kGateTPW = kGateTokens / kGateWaves;  // tokens per wave
-  __shared__ double red_d[4][kMaxExperts];
-  __shared__ int32_t hcnt[kMaxExperts];
-  __shared__ float selp_s[kGateWaves][64];
-  __shared__ int32_t sele_s[kGateWaves][64];
+template <int TE, bool FUSE, int LPT, int VPL>
+__global__ __launch_bounds__(kRw * 64) void router_scores_bf16_kernel(
+    const bf16* __restrict__ x, const float* __restrict__ Wg, const float* __restrict__ bg,
+    int64_t T, int d, int E, int kchunk, float* __restrict__ part, int k, int renorm,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ probs,
+    double* __restrict__ stat_part, int32_t* __restrict__ hist) {
+  constexpr int NE = TE / 16;   // expert blocks
+  constexpr int QK = kRw / NE;  // K slices
+  constexpr int G = 2;          // K steps in flight per wave
+  __shared__ float red[kRw][kRtM * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = lane & (lpt - 1);
-  const int grp = lane / lpt;
-  const int tpw = kWave / lpt;  // tokens per wave step
-  const int64_t blk = blockIdx.x;
-  for (int e = tid; e < E; e += kGateWaves * 64) hcnt[e] = 0;
+  const int eb = wave % NE, q = wave / NE;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRtM;
+  const int e = blockIdx.y * TE + eb * 16 + (lane & 15);
+  const int kb = blockIdx.z * kchunk;
+  const int ke = min(d, kb + kchunk);
+  const int nks = (ke - kb + 31) / 32;
+  const int kl = (lane >> 4) * 8;
+
+  const bf16* xr[4];
+  bool rv[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int64_t t = t0 + rb * 16 + (lane & 15);
+    rv[rb] = t < T;
+    xr[rb] = x + (rv[rb] ? t : 0) * d + kl;
+  }
+  const bool ev = e < E;
+  const float* wrow = Wg + static_cast<int64_t>(ev ? e : 0) * d + kl;
+
+  f32x4 ah[4], al[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    ah[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    al[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int j0 = q; j0 < nks; j0 += G * QK) {
+    uint4 a[G][4];
+    float4 w[G][2];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int k0 = kb + (j0 + g * QK) * 32 + kl;
+      const bool kv = (j0 + g * QK) < nks && k0 < ke;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        a[g][rb] = (kv && rv[rb]) ? *reinterpret_cast<const uint4*>(xr[rb] + (k0 - kl))
+                                  : make_uint4(0, 0, 0, 0);
+      w[g][0] = (kv && ev) ? *reinterpret_cast<const float4*>(wrow + (k0 - kl))
+                           : make_float4(0, 0, 0, 0);
+      w[g][1] = (kv && ev) ? *reinterpret_cast<const float4*>(wrow + (k0 - kl) + 4)
+                           : make_float4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float wv[8] = {w[g][0].x, w[g][0].y, w[g][0].z, w[g][0].w,
+                           w[g][1].x, w[g][1].y, w[g][1].z, w[g][1].w};
+      uint32_t hb[8], mb[8], lb[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hb[i] = __float_as_uint(wv[i]);
+        const float r1 = wv[i] - __uint_as_float(hb[i] & 0xffff0000u);
+        mb[i] = __float_as_uint(r1);
+        lb[i] = __float_as_uint(r1 - __uint_as_float(mb[i] & 0xffff0000u));
+      }
+      uint4 bh, bm, bl;
+      bh = make_uint4(hi16x2(hb[0], hb[1]), hi16x2(hb[2], hb[3]), hi16x2(hb[4], hb[5]),
+                      hi16x2(hb[6], hb[7]));
+      bm = make_uint4(hi16x2(mb[0], mb[1]), hi16x2(mb[2], mb[3]), hi16x2(mb[4], mb[5]),
+                      hi16x2(mb[6], mb[7]));
+      bl = make_uint4(hi16x2(lb[0], lb[1]), hi16x2(lb[2], lb[3]), hi16x2(lb[4], lb[5]),
+                      hi16x2(lb[6], lb[7]));
+      const bf16x8_t fh = __builtin_bit_cast(bf16x8_t, bh);
+      const bf16x8_t fm = __builtin_bit_cast(bf16x8_t, bm);
+      const bf16x8_t fl = __builtin_bit_cast(bf16x8_t, bl);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, a[g][rb]);
+        ah[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fh, ah[rb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, a[g][rb]);
+        al[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fm, al[rb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, a[g][rb]);
+        al[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fl, al[rb], 0, 0, 0);
+      }
+    }
+  }
+  // C layout: ah[rb][j] is token row rb*16 + (lane>>4)*4 + j, expert column lane&15
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      red[wave][(rb * 16 + (lane >> 4) * 4 + j) * 16 + (lane & 15)] = ah[rb][j] + al[rb][j];
   __syncthreads();
-
-  double sacc[VPL];
+  // add the K slices in slice order; the sum lands in slice 0's tile
+  for (int i = tid; i < NE * kRtM * 16; i += kRw * 64) {
+    const int b = i / (kRtM * 16), off = i % (kRtM * 16);
+    float z = red[b][off];
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) sacc[v] = 0.0;
-
-  const int iters = (kGateTPW + tpw - 1) / tpw;
-  for (int it = 0; it < iters; ++it) {
-    const int local = it * tpw + grp;
-    const int64_t t = blk * kGateTokens + wave * kGateTPW + local;
-    const bool vt = local < kGateTPW && t < T;
-    float l[VPL];
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int e = s + v * lpt;
-      float z = -INFINITY;
-      if (vt && e < E) {
-        z = logit[t * E + e];
-        if (bg) z += bg[e];
-      }
-      l[v] = z;
-    }
-    float m = l[0];
-#pragma unroll
-    for (int v = 1; v < VPL; ++v) m = fmaxf(m, l[v]);
-    for (int o = lpt >> 1; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    float pz[VPL];
-    float sum = 0.f;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      pz[v] = (l[v] == -INFINITY) ? 0.f : expf(l[v] - m);
-      sum += pz[v];
-    }
-    for (int o = lpt >> 1; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int e = s + v * lpt;
-      const float p = pz[v] / sum;
-      if (vt && e < E) {
-        if (probs) probs[t * E + e] = p;
-        sacc[v] += static_cast<double>(p);
-      }
-    }
-
-    // top-k: k rounds of a group argmax over the not-yet-taken experts
-    uint32_t taken = 0;
-    float selsum = 0.f;
-    for (int i = 0; i < k; ++i) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const int e = s + v * lpt;
-        if (e < E && !((taken >> v) & 1u) && (l[v] > bv || (l[v] == bv && e < be))) {
-          bv = l[v];
-          be = e;
-        }
-      }
-      for (int o = lpt >> 1; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oe = __shfl_xor(be, o);
-        if (ov > bv || (ov == bv && oe < be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if ((be & (lpt - 1)) == s) {
-        const int v = be / lpt;
-#pragma unroll
-        for (int vv = 0; vv < VPL; ++vv)
-          if (vv == v) taken |= 1u << vv;
-        if (vt) atomicAdd(&hcnt[be], 1);
-      }
-      const float p = expf(bv - m) / sum;  // same value the owner lane computed
-      selsum += p;
-      if (s == 0) {
-        selp_s[wave][grp * k + i] = p;
-        sele_s[wave][grp * k + i] = be;
-      }
-    }
-    __syncthreads();
-    if (vt && s < k) {
-      const float p = selp_s[wave][grp * k + s];
-      topk_idx[t * k + s] = sele_s[wave][grp * k + s];
-      topk_w[t * k + s] = renorm ? p / selsum : p;
-    }
-    __syncthreads();
+    for (int qq = 1; qq < QK; ++qq) z += red[b + qq * NE][off];
+    red[b][off] = z;
   }
-
-  // reduce across the token groups of the wave (lanes with the same s), then
-  // across waves in a fixed order: slot w % 4 accumulates waves w % 4, w % 4 + 4,
-  // ... in wave order, then the four slots are added in order
-#pragma unroll
-  for (int v = 0; v < VPL; ++v)
-    for (int o = lpt; o < kWave; o <<= 1) sacc[v] += __shfl_xor(sacc[v], o);
-  for (int half = 0; half < kGateWaves / 4; ++half) {
-    if (grp == 0 && (wave >> 2) == half) {
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const int e = s + v * lpt;
-        if (e < E) red_d[wave & 3][e] = half ? red_d[wave & 3][e] + sacc[v] : sacc[v];
-      }
+  __syncthreads();
+  if constexpr (FUSE) {
+    __shared__ GateSmem<TE> gsm;
+    gate_block<LPT, VPL>([&](int tl, int ee) { return red[ee >> 4][tl * 16 + (ee & 15)]; }, gsm,
+                         blockIdx.x, bg, T, E, k, renorm, topk_idx, topk_w, probs, stat_part,
+                         hist);
+  } else {
+    for (int i = tid; i < kRtM * TE; i += kRw * 64) {
+      const int tl = i / TE, el = i % TE;
+      const int64_t t = t0 + tl;
+      const int ee = blockIdx.y * TE + el;
+      if (t < T && ee < E)
+        part[(static_cast<int64_t>(blockIdx.z) * T + t) * E + ee] =
+            red[el >> 4][tl * 16 + (el & 15)];
     }
-    __syncthreads();
   }
-  for (int e = tid; e < E; e += kGateWaves * 64) {
-    stat_part[blk * E + e] = ((red_d[0][e] + red_d[1][e]) + red_d[2][e]) + red_d[3][e];
-    hist[blk * E + e] = hcnt[e];
-  }
+}
+
+// Gate over scores held as S chunk partials part[s][T][E]; the chunks are
+// added in chunk order.
+template <int LPT, int VPL>
+__global__ __launch_bounds__(kRw * 64) void router_gate_kernel(
+    const float* __restrict__ part, int S, const float* __restrict__ bg, int64_t T, int E, int k,
+    int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ probs, double* __restrict__ stat_part, int32_t* __restrict__ hist) {
+  __shared__ GateSmem<kMaxExperts> gsm;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kGateTokens;
+  const int64_t n = T * E;
+  gate_block<LPT, VPL>(
+      [&](int tl, int e) {
+        const int64_t i = (t0 + tl) * E + e;
+        float z = part[i];
+        for (int sp = 1; sp < S; ++sp) z += part[sp * n + i];
+        return z;
+      },
+      gsm, blockIdx.x, bg, T, E, k, renorm, topk_idx, topk_w, probs, stat_part, hist);
 }
 
 // mean_prob[e] = (sum over blocks, in block order) / T; balance = unbiased
@@ -319,6 +505,12 @@ __global__ __launch_bounds__(1024) void router_stats_kernel(const double* __rest
 }
 
 // ------------------------------------------------------------------ launches
+// Fused score + gate kernels: TE = 16 (E <= 16) or 64 (E <= 64, VPL 2 or 4).
+#define MOE_FUSED(TE_, VPL_)                                                                    \
+  router_scores_bf16_kernel<TE_, true, 16, VPL_><<<g1, kRw * 64, 0, st>>>(                     \
+      static_cast<const bf16*>(x), Wg, bg, p.T, p.d, p.E, p.kchunk, part, p.k, p.renorm,       \
+      topk_idx, topk_w, probs, stat_part, hist)
+
 hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const float* Wg,
                          const float* bg, float* part, int32_t* topk_idx, float* topk_w,
                          float* probs, double* stat_part, int32_t* hist, float* mean_prob,
@@ -327,35 +519,52 @@ hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const flo
     const int TE = p.E <= 16 ? 16 : 64;
     dim3 g1(static_cast<unsigned>(ceil_div(p.T, kRtM)), static_cast<unsigned>(ceil_div(p.E, TE)),
             static_cast<unsigned>(p.S));
-#define MOE_SCORES(XT, TEV)                                                                  \
-  router_scores_kernel<XT, TEV><<<g1, 256, 0, st>>>(static_cast<const XT*>(x), Wg, p.T, p.d, \
-                                                    p.E, p.kchunk, part)
-    if (dtype == MOE_BF16) {
-      if (TE == 16) MOE_SCORES(bf16, 16); else MOE_SCORES(bf16, 64);
+    if (p.fused) {
+      // one block holds every score of its 64 tokens: the gate runs in place
+      if (TE == 16) MOE_FUSED(16, 1);
+      else if (p.vpl <= 2) MOE_FUSED(64, 2);
+      else MOE_FUSED(64, 4);
     } else {
-      if (TE == 16) MOE_SCORES(float, 16); else MOE_SCORES(float, 64);
-    }
-#undef MOE_SCORES
-    const unsigned nb = static_cast<unsigned>(p.nb);
-    if (p.S > 1) {
-      const int64_t n = p.T * p.E;
-      router_reduce_kernel<<<static_cast<unsigned>(ceil_div(n, 256)), 256, 0, st>>>(part, p.S, n);
-    }
-#define MOE_GATE(V, W)                                                                      \
-  router_gate_kernel<V, W><<<nb, W * 64, 0, st>>>(part, bg, p.T, p.E, p.k, p.renorm, p.lpt, \
-                                                  topk_idx, topk_w, probs, stat_part, hist)
-    switch (p.vpl) {
-      case 1: MOE_GATE(1, 16); break;
-      case 2: MOE_GATE(2, 16); break;
-      case 4: MOE_GATE(4, 16); break;
-      case 8: MOE_GATE(8, 8); break;
-      default: MOE_GATE(16, 8); break;
-    }
+      if (dtype == MOE_BF16) {
+        if (TE == 16)
+          router_scores_bf16_kernel<16, false, 16, 1><<<g1, kRw * 64, 0, st>>>(
+              static_cast<const bf16*>(x), Wg, bg, p.T, p.d, p.E, p.kchunk, part, p.k,
+              p.renorm, topk_idx, topk_w, probs, stat_part, hist);
+        else
+          router_scores_bf16_kernel<64, false, 16, 1><<<g1, kRw * 64, 0, st>>>(
+              static_cast<const bf16*>(x), Wg, bg, p.T, p.d, p.E, p.kchunk, part, p.k,
+              p.renorm, topk_idx, topk_w, probs, stat_part, hist);
+      } else {
+        if (TE == 16)
+          router_scores_f32_kernel<16><<<g1, 256, 0, st>>>(static_cast<const float*>(x), Wg,
+                                                            p.T, p.d, p.E, p.kchunk, part);
+        else
+          router_scores_f32_kernel<64><<<g1, 256, 0, st>>>(static_cast<const float*>(x), Wg,
+                                                            p.T, p.d, p.E, p.kchunk, part);
+      }
+      const unsigned nb = static_cast<unsigned>(p.nb);
+#define MOE_GATE(L, V)                                                                         \
+  router_gate_kernel<L, V><<<nb, kRw * 64, 0, st>>>(part, p.S, bg, p.T, p.E, p.k, p.renorm,    \
+                                                    topk_idx, topk_w, probs, stat_part, hist)
+      if (p.lpt == 16) {
+        switch (p.vpl) {
+          case 1: MOE_GATE(16, 1); break;
+          case 2: MOE_GATE(16, 2); break;
+          case 4: MOE_GATE(16, 4); break;
+          case 8: MOE_GATE(16, 8); break;
+          default: MOE_GATE(16, 16); break;
+        }
+      } else {
+        if (p.vpl <= 8) MOE_GATE(64, 8);
+        else MOE_GATE(64, 16);
+      }
 #undef MOE_GATE
+    }
   }
   if (mean_prob || balance)
     router_stats_kernel<<<1, 1024, 0, st>>>(stat_part, p.nb, p.E, p.T, mean_prob, balance);
   return hipGetLastError();
 }
+#undef MOE_FUSED
 
 }  // namespace moe
