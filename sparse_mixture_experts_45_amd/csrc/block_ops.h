@@ -1,0 +1,103 @@
+// Block-wide helpers for blocks of kMaxExperts threads: integer scans of the
+// dispatch, the row-tile list of the grouped GEMM, and the load statistics.
+#pragma once
+#include "kernels.h"
+
+namespace moe {
+
+// Exclusive prefix sum of v over the block's threads in thread order (wave
+// shuffle scans, then the 16 wave totals); `total` gets the block sum.  wsum:
+// 16 ints of LDS.  Integer sums, exact.
+__device__ inline int block_excl_scan(int v, int32_t* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kMaxExperts / 64; ++w) {
+    const int s = wsum[w];
+    pre += w < wave ? s : 0;
+    tot += s;
+  }
+  total = tot;
+  __syncthreads();
+  return pre + x - v;
+}
+
+// Group g (expert g, or the shared expert as group E) owns rows
+// off[g] .. off[g+1] and is cut into ceil(rows / BM) tiles of at most BM rows;
+// tiles are listed group by group, row-ascending.  `off` may sit in global
+// memory or LDS.
+__device__ inline void build_tile_list(const int32_t* off, int G, int BM,
+                                       RowTile* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                       int32_t* wsum) {
+  const int g = threadIdx.x;
+  int rows = 0, m = 0;
+  if (g < G) {
+    rows = off[g + 1] - off[g];
+    m = (rows + BM - 1) / BM;
+  }
+  int total;
+  const int start = block_excl_scan(m, wsum, total);
+  if (g < G) {
+    const int r0 = off[g];
+    for (int j = 0; j < m; ++j) {
+      RowTile t;
+      t.group = g;
+      t.row0 = r0 + j * BM;
+      t.rows = min(BM, rows - j * BM);
+      t.first = start;
+      t.count = m;
+      t.pad0 = t.pad1 = t.pad2 = 0;
+      tiles[start + j] = t;
+    }
+  }
+  if (g == 0) ntiles[0] = total;
+}
+
+// Sum of v over the block: xor-shuffle tree in each wave (every lane ends with
+// the same value), then the 16 wave sums in wave order.  Fixed order, so the
+// result does not change from run to run.  wsd: 16 doubles of LDS.
+__device__ inline double block_sum_d(double v, double* wsd) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  if (lane == 0) wsd[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < kMaxExperts / 64; ++w) t += wsd[w];
+  __syncthreads();
+  return t;
+}
+
+// Load statistics from the gate's per-block probability sums (fp64):
+// mean_prob[e] = (sum over the nb blocks, in block order) / T, and balance =
+// unbiased variance of mean_prob over the E experts.  Either output may be null;
+// T = 0 gives NaN means, E = 1 a NaN variance.
+__device__ inline void load_stats(const double* __restrict__ stat_part, int nb, int E, int64_t T,
+                                  float* __restrict__ mean_prob, float* __restrict__ balance,
+                                  double* wsd) {
+  const int e = threadIdx.x;
+  double mp = 0.0;
+  if (e < E) {
+    double acc = 0.0;
+    for (int b = 0; b < nb; ++b) acc += stat_part[static_cast<int64_t>(b) * E + e];
+    mp = acc / static_cast<double>(T);
+    if (mean_prob) mean_prob[e] = static_cast<float>(mp);
+  }
+  if (balance) {
+    const double mean = block_sum_d(e < E ? mp : 0.0, wsd) / static_cast<double>(E);
+    const double dv = e < E ? mp - mean : 0.0;
+    const double var = block_sum_d(dv * dv, wsd);
+    if (e == 0) balance[0] = static_cast<float>(var / static_cast<double>(E - 1));
+  }
+}
+
+}  // namespace moe

@@ -18,6 +18,7 @@
 //      the block with the same expert (ballot match on the expert id bits),
 //      adds the block base, and scatters kept pairs to their rows.
 #include "kernels.h"
+#include "block_ops.h"
 
 namespace moe {
 
@@ -38,61 +39,207 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
   for (int e = threadIdx.x; e < E; e += 256) hist[b * E + e] = h[e];
 }
 
-// One block.  Thread (e, c) owns expert e and the c-th contiguous range of the
-// per-block counts; ranges are summed, scanned across c, then re-walked to
-// write each block's base.  Integer sums: exact in any order.
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
-    const int32_t* __restrict__ hist, int nb, int E, int64_t T, int capacity, int shared,
-    int32_t* __restrict__ base, int32_t* __restrict__ counts, int32_t* __restrict__ kept,
-    int32_t* __restrict__ offsets) {
-  __shared__ int32_t part[kMaxExperts];
-  __shared__ int32_t sc[2][kMaxExperts];
+// Scan of the per-block histogram by one block of kMaxExperts threads.
+// Thread e * chunks + c owns expert e and the c-th contiguous range of blocks;
+// one block-wide scan of the range sums in thread order gives, for every
+// range, the expert's pairs in earlier ranges (subtracting the value at the
+// expert's first range), and the expert's total.  kept = min(count, C);
+// offsets = exclusive scan of kept, offsets[E] = routed rows, offsets[E + 1] =
+// routed + shared rows.  base[b][e] (LDS or global) = pairs of expert e in
+// blocks before b.  Integer sums: exact in any order.  Ends with a barrier.
+__device__ void scan_hist(const int32_t* __restrict__ hist, int nb, int E, int64_t T,
+                          int capacity, int shared, int32_t* base, int32_t* __restrict__ counts,
+                          int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
+                          int32_t* skept, int32_t* soff, int32_t* sh, int32_t* wsum) {
   const int tid = threadIdx.x;
-  const int chunks = kMaxExperts / E;  // >= 1
-  const int e = tid % E, c = tid / E;
+  const int chunks = max(1, min(kMaxExperts / E, nb));
+  const int e = tid / chunks, c = tid % chunks;
+  const bool own = e < E;
   const int len = (nb + chunks - 1) / chunks;
   const int b0 = c * len, b1 = min(nb, b0 + len);
   int sum = 0;
-  if (c < chunks)
+  if (own)
     for (int b = b0; b < b1; ++b) sum += hist[static_cast<int64_t>(b) * E + e];
-  if (c < chunks) part[tid] = sum;
+  int total;
+  const int ex = block_excl_scan(sum, wsum, total);
+  sh[tid] = ex;
   __syncthreads();
-  int kp = 0;
-  if (tid < E) {
-    int run = 0;
-    for (int cc = 0; cc < chunks; ++cc) {
-      const int v = part[cc * E + tid];
-      part[cc * E + tid] = run;  // exclusive prefix over ranges
-      run += v;
-    }
-    kp = capacity < 0 ? run : min(run, capacity);
-    counts[tid] = run;
-    kept[tid] = kp;
-  }
-  __syncthreads();
-  if (c < chunks) {
-    int run = part[tid];
+  if (own) {
+    int run = ex - sh[e * chunks];
     for (int b = b0; b < b1; ++b) {
       base[static_cast<int64_t>(b) * E + e] = run;
       run += hist[static_cast<int64_t>(b) * E + e];
     }
   }
-  // inclusive Hillis-Steele scan of kept over the experts
-  int src = 0;
-  sc[0][tid] = kp;
-  __syncthreads();
-  for (int o = 1; o < kMaxExperts; o <<= 1) {
-    const int v = sc[src][tid] + (tid >= o ? sc[src][tid - o] : 0);
-    sc[src ^ 1][tid] = v;
-    src ^= 1;
-    __syncthreads();
+  int kp = 0;
+  if (tid < E) {
+    const int s1 = (tid + 1) * chunks < kMaxExperts ? sh[(tid + 1) * chunks] : total;
+    const int cnt = s1 - sh[tid * chunks];
+    kp = capacity < 0 ? cnt : min(cnt, capacity);
+    counts[tid] = cnt;
+    kept[tid] = kp;
+    if (skept) skept[tid] = kp;
   }
-  if (tid < E) offsets[tid] = sc[src][tid] - kp;
+  int ktot;
+  const int kx = block_excl_scan(kp, wsum, ktot);
+  if (tid < E) {
+    offsets[tid] = kx;
+    if (soff) soff[tid] = kx;
+  }
   if (tid == 0) {
-    const int total = sc[src][E - 1];
-    offsets[E] = total;
-    offsets[E + 1] = total + (shared ? static_cast<int32_t>(T) : 0);
+    const int end = ktot + (shared ? static_cast<int32_t>(T) : 0);
+    offsets[E] = ktot;
+    offsets[E + 1] = end;
+    if (soff) {
+      soff[E] = ktot;
+      soff[E + 1] = end;
+    }
   }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
+    const int32_t* __restrict__ hist, int nb, int E, int64_t T, int capacity, int shared,
+    int32_t* __restrict__ base, int32_t* __restrict__ counts, int32_t* __restrict__ kept,
+    int32_t* __restrict__ offsets) {
+  __shared__ int32_t sh[kMaxExperts];
+  __shared__ int32_t wsum[kMaxExperts / 64];
+  scan_hist(hist, nb, E, T, capacity, shared, base, counts, kept, offsets, nullptr, nullptr, sh,
+            wsum);
+}
+
+// Expert ids (and, with topk_w set, gates) of the pairs of 64-token block b,
+// lane = token; -1 / 0 past T or past k.
+template <int KM>
+__device__ __forceinline__ void load_block(int64_t b, const int32_t* __restrict__ topk_idx,
+                                           const float* __restrict__ topk_w, int64_t T, int k,
+                                           int (&mine)[KM], float (&wsel)[KM]) {
+  const int64_t t = b * kGateTokens + (threadIdx.x & 63);
+  const bool valid = t < T;
+#pragma unroll
+  for (int i = 0; i < KM; ++i) {
+    mine[i] = (valid && i < k) ? topk_idx[t * k + i] : -1;
+    wsel[i] = (topk_w && valid && i < k) ? topk_w[t * k + i] : 0.f;
+  }
+}
+
+// Lanes below this one (in `live`) whose expert id v equals e: the id bits are
+// compared through nbits ballots, one per bit.
+__device__ __forceinline__ int lower_matches(int v, int e, int nbits, uint64_t live) {
+  uint64_t m = live;
+#pragma unroll
+  for (int q = 0; q < 10; ++q) {
+    if (q < nbits) {
+      const uint64_t bq = __ballot((v >> q) & 1);
+      m &= ((e >> q) & 1) ? bq : ~bq;
+    }
+  }
+  return __popcll(m);
+}
+
+// Row of pair (t, i) of expert e with `rank` earlier pairs of e in its 64-token
+// block, or -1 when e is out of range or the pair falls beyond the capacity;
+// writes the row's token, slot and (with row_gate) gate, and inv.
+__device__ __forceinline__ void place_pair(int64_t t, int i, int k, int e, int rank, int E,
+                                           const int32_t* base, const int32_t* kept,
+                                           const int32_t* offsets, float gate,
+                                           int32_t* __restrict__ row_token,
+                                           int32_t* __restrict__ row_slot,
+                                           int32_t* __restrict__ inv,
+                                           float* __restrict__ row_gate) {
+  const bool ok = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+  const int gr = ok ? base[e] + rank : 0;
+  if (ok && gr < kept[e]) {
+    const int row = offsets[e] + gr;
+    row_token[row] = static_cast<int32_t>(t);
+    row_slot[row] = i;
+    inv[t * k + i] = row;
+    if (row_gate) row_gate[row] = gate;
+  } else {
+    inv[t * k + i] = -1;
+  }
+}
+
+__device__ __forceinline__ void place_shared(int64_t t, int E, const int32_t* offsets,
+                                             int32_t* __restrict__ row_token,
+                                             int32_t* __restrict__ row_slot,
+                                             float* __restrict__ row_gate) {
+  const int row = offsets[E] + static_cast<int>(t);
+  row_token[row] = static_cast<int32_t>(t);
+  row_slot[row] = -1;
+  if (row_gate) row_gate[row] = 1.0f;
+}
+
+// Ranks and scatters the pairs of 64-token block b; one wave, lane = token.
+// A pair's rank is the number of lower lanes that picked the same expert in any
+// slot (a token never picks an expert twice), so pairs of an expert land
+// token-ascending.  `base` points at the block's per-expert count of earlier
+// pairs.  With row_gate set, also writes each kept row's gate (its pair's
+// topk_w; 1 for the shared expert's row).
+//
+// Up to 4 slots: ids and gates preloaded by load_block, all slots unrolled.
+template <int KM>
+__device__ __forceinline__ void scatter_block_few(int64_t b, const int (&mine)[KM],
+                                                  const float (&wsel)[KM], int64_t T, int k,
+                                                  int E, int nbits, const int32_t* base,
+                                                  const int32_t* kept, const int32_t* offsets,
+                                                  int shared, int32_t* __restrict__ row_token,
+                                                  int32_t* __restrict__ row_slot,
+                                                  int32_t* __restrict__ inv,
+                                                  float* __restrict__ row_gate) {
+  static_assert(KM <= 4, "few slots only");
+  const int lane = threadIdx.x & 63;
+  const int64_t t = b * kGateTokens + lane;
+  const bool valid = t < T;
+  const uint64_t live = __ballot(valid) & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)));
+  int rank[KM];
+#pragma unroll
+  for (int i = 0; i < KM; ++i) rank[i] = 0;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    if (j < k) {
+      const int v = valid ? mine[j] : 0;
+#pragma unroll
+      for (int i = 0; i < KM; ++i)
+        if (i < k) rank[i] += lower_matches(v, mine[i], nbits, live);
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < KM; ++i)
+      if (i < k)
+        place_pair(t, i, k, mine[i], rank[i], E, base, kept, offsets, wsel[i], row_token,
+                   row_slot, inv, row_gate);
+    if (shared) place_shared(t, E, offsets, row_token, row_slot, row_gate);
+  }
+}
+
+// Any k: slots rolled, each pair placed as soon as its rank is known; ids and
+// gates read from cache (keeps the registers few for large k).
+__device__ __forceinline__ void scatter_block_any(int64_t b, const int32_t* __restrict__ topk_idx,
+                                                  const float* __restrict__ topk_w, int64_t T,
+                                                  int k, int E, int nbits, const int32_t* base,
+                                                  const int32_t* kept, const int32_t* offsets,
+                                                  int shared, int32_t* __restrict__ row_token,
+                                                  int32_t* __restrict__ row_slot,
+                                                  int32_t* __restrict__ inv,
+                                                  float* __restrict__ row_gate) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = b * kGateTokens + lane;
+  const bool valid = t < T;
+  const uint64_t live = __ballot(valid) & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)));
+  for (int i = 0; i < k; ++i) {
+    const int ei = valid ? topk_idx[t * k + i] : 0;
+    int rank = 0;
+    for (int j = 0; j < k; ++j) {
+      const int v = valid ? topk_idx[t * k + j] : 0;
+      rank += lower_matches(v, ei, nbits, live);
+    }
+    if (valid)
+      place_pair(t, i, k, ei, rank, E, base, kept, offsets, row_gate ? topk_w[t * k + i] : 0.f,
+                 row_token, row_slot, inv, row_gate);
+  }
+  if (valid && shared) place_shared(t, E, offsets, row_token, row_slot, row_gate);
 }
 
 template <int KM>
@@ -101,60 +248,83 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(
     const int32_t* __restrict__ base, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ offsets, int shared, int32_t* __restrict__ row_token,
     int32_t* __restrict__ row_slot, int32_t* __restrict__ inv) {
-  const int lane = threadIdx.x;
   const int64_t b = blockIdx.x;
-  const int64_t t = b * kGateTokens + lane;
-  const bool valid = t < T;
-  const uint64_t vmask = __ballot(valid);
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if constexpr (KM <= 4) {
+    int mine[KM];
+    float wsel[KM];
+    load_block<KM>(b, topk_idx, nullptr, T, k, mine, wsel);
+    scatter_block_few<KM>(b, mine, wsel, T, k, E, nbits, base + b * E, kept, offsets, shared,
+                          row_token, row_slot, inv, nullptr);
+  } else {
+    scatter_block_any(b, topk_idx, nullptr, T, k, E, nbits, base + b * E, kept, offsets, shared,
+                      row_token, row_slot, inv, nullptr);
+  }
+}
 
-  int mine[KM];
-  int rank[KM];
+// The whole dispatch of a batch whose per-block bases fit in LDS, in one block
+// of kMaxExperts threads: load statistics (mean router probability per expert
+// and its unbiased variance, fp64), the scan of the gate's
+// per-block histogram, the GEMM row-tile list, and the scatter (16 waves walk
+// the 64-token blocks), which also writes every row's gate.  Same arithmetic
+// and the same outputs as the multi-kernel path.
+template <int KM>
+__global__ __launch_bounds__(1024) void dispatch_one_block_kernel(DispatchArgs a) {
+  __shared__ int32_t sbase[kDispatchLdsBases];
+  __shared__ int32_t sh[kMaxExperts];
+  __shared__ int32_t wsum[kMaxExperts / 64];
+  __shared__ double wsd[kMaxExperts / 64];
+  __shared__ int32_t skept[kMaxExperts];
+  __shared__ int32_t soff[kMaxExperts + 2];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int E = a.E, nb = a.nb;
+  constexpr int kWaves = kMaxExperts / 64;
+  // few slots: the ids and gates of the wave's first two 64-token blocks do
+  // not depend on the scan, so their loads go out first and overlap it
+  constexpr int PF = KM <= 4 ? 2 : 0;
+  constexpr int KP = KM <= 4 ? KM : 1;
+  int mine[PF > 0 ? PF : 1][KP];
+  float wsel[PF > 0 ? PF : 1][KP];
 #pragma unroll
-  for (int i = 0; i < KM; ++i) {
-    mine[i] = (valid && i < k) ? topk_idx[t * k + i] : -1;
-    rank[i] = 0;
-  }
-  // rank[i] = number of lower lanes that picked expert mine[i] in any slot
-  for (int j = 0; j < k; ++j) {
-    const int v = valid ? topk_idx[t * k + j] : 0;
-    uint64_t bits[10];
+  for (int p = 0; p < PF; ++p)
+    load_block<KP>(wave + p * kWaves, a.topk_idx, a.topk_w, a.T, a.k, mine[p], wsel[p]);
+
+  if (a.mean_prob || a.balance)
+    load_stats(a.stat_part, nb, E, a.T, a.mean_prob, a.balance, wsd);
+
+  scan_hist(a.hist, nb, E, a.T, a.capacity, a.shared, sbase, a.counts, a.kept, a.offsets, skept,
+            soff, sh, wsum);
+  build_tile_list(soff, E + (a.shared ? 1 : 0), a.BM, a.tiles, a.ntiles, wsum);
+
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  if constexpr (KM <= 4) {
 #pragma unroll
-    for (int q = 0; q < 10; ++q) bits[q] = (q < nbits) ? __ballot((v >> q) & 1) : 0ull;
-#pragma unroll
-    for (int i = 0; i < KM; ++i) {
-      if (i < k) {
-        uint64_t m = vmask & below;
-#pragma unroll
-        for (int q = 0; q < 10; ++q)
-          if (q < nbits) m &= ((mine[i] >> q) & 1) ? bits[q] : ~bits[q];
-        rank[i] += __popcll(m);
-      }
+    for (int p = 0; p < PF; ++p) {
+      const int b = wave + p * kWaves;
+      if (b < nb)
+        scatter_block_few<KP>(b, mine[p], wsel[p], a.T, a.k, E, nbits, sbase + b * E, skept,
+                              soff, a.shared, a.row_token, a.row_slot, a.inv, a.row_gate);
     }
-  }
-  if (valid) {
-#pragma unroll
-    for (int i = 0; i < KM; ++i) {
-      if (i < k) {
-        const int e = mine[i];
-        const bool ok = static_cast<unsigned>(e) < static_cast<unsigned>(E);
-        const int gr = ok ? base[b * E + e] + rank[i] : 0;
-        if (ok && gr < kept[e]) {
-          const int row = offsets[e] + gr;
-          row_token[row] = static_cast<int32_t>(t);
-          row_slot[row] = i;
-          inv[t * k + i] = row;
-        } else {
-          inv[t * k + i] = -1;
-        }
-      }
+    for (int b = wave + PF * kWaves; b < nb; b += kWaves) {
+      load_block<KP>(b, a.topk_idx, a.topk_w, a.T, a.k, mine[0], wsel[0]);
+      scatter_block_few<KP>(b, mine[0], wsel[0], a.T, a.k, E, nbits, sbase + b * E, skept, soff,
+                            a.shared, a.row_token, a.row_slot, a.inv, a.row_gate);
     }
-    if (shared) {
-      const int row = offsets[E] + static_cast<int>(t);
-      row_token[row] = static_cast<int32_t>(t);
-      row_slot[row] = -1;
-    }
+  } else {
+    for (int b = wave; b < nb; b += kWaves)
+      scatter_block_any(b, a.topk_idx, a.topk_w, a.T, a.k, E, nbits, sbase + b * E, skept, soff,
+                        a.shared, a.row_token, a.row_slot, a.inv, a.row_gate);
   }
+}
+
+hipError_t launch_dispatch_one_block(const DispatchArgs& a, hipStream_t st) {
+#define MOE_ONE(KM) dispatch_one_block_kernel<KM><<<1, kMaxExperts, 0, st>>>(a)
+  if (a.k <= 1) MOE_ONE(1);
+  else if (a.k <= 2) MOE_ONE(2);
+  else if (a.k <= 4) MOE_ONE(4);
+  else MOE_ONE(kMaxTopK);  // slots rolled
+#undef MOE_ONE
+  return hipGetLastError();
 }
 
 hipError_t launch_dispatch(int64_t T, int E, int k, int capacity, int shared, int nb,
@@ -173,9 +343,7 @@ hipError_t launch_dispatch(int64_t T, int E, int k, int capacity, int shared, in
     if (k <= 1) MOE_SCAT(1);
     else if (k <= 2) MOE_SCAT(2);
     else if (k <= 4) MOE_SCAT(4);
-    else if (k <= 8) MOE_SCAT(8);
-    else if (k <= 16) MOE_SCAT(16);
-    else MOE_SCAT(32);
+    else MOE_SCAT(kMaxTopK);  // slots rolled
 #undef MOE_SCAT
   }
   return hipGetLastError();

@@ -22,6 +22,7 @@
 // with the group's row tiles fastest: the blocks that run together on one XCD
 // share the same weight columns and the same token rows.
 #include "kernels.h"
+#include "block_ops.h"
 
 namespace moe {
 
@@ -582,37 +583,9 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
                                                            RowTile* __restrict__ tiles,
                                                            int32_t* __restrict__ ntiles,
                                                            float* __restrict__ row_gate) {
-  __shared__ int32_t sc[2][kMaxExperts];
+  __shared__ int32_t wsum[kMaxExperts / 64];
+  build_tile_list(offsets, G, BM, tiles, ntiles, wsum);
   const int g = threadIdx.x;
-  int rows = 0, m = 0;
-  if (g < G) {
-    rows = offsets[g + 1] - offsets[g];
-    m = (rows + BM - 1) / BM;
-  }
-  int src = 0;
-  sc[0][g] = m;
-  __syncthreads();
-  for (int o = 1; o < kMaxExperts; o <<= 1) {
-    const int v = sc[src][g] + (g >= o ? sc[src][g - o] : 0);
-    sc[src ^ 1][g] = v;
-    src ^= 1;
-    __syncthreads();
-  }
-  const int start = sc[src][g] - m;
-  if (g < G) {
-    const int r0 = offsets[g];
-    for (int j = 0; j < m; ++j) {
-      RowTile t;
-      t.group = g;
-      t.row0 = r0 + j * BM;
-      t.rows = min(BM, rows - j * BM);
-      t.first = start;
-      t.count = m;
-      t.pad0 = t.pad1 = t.pad2 = 0;
-      tiles[start + j] = t;
-    }
-  }
-  if (g == kMaxExperts - 1) ntiles[0] = sc[src][g];
   // gate of every row: topk_w of its (token, slot); 1 for the shared expert's rows
   const int routed = offsets[E], nrows = offsets[G];
   for (int r = g; r < nrows; r += kMaxExperts)
@@ -720,9 +693,10 @@ static void run_dma(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
 
 hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const int G = f.E + (f.Fs > 0 ? 1 : 0);
-  build_tiles_kernel<<<1, kMaxExperts, 0, st>>>(f.offsets, G, gp.BM, f.E, f.k, f.row_token,
-                                                f.row_slot, f.topk_w, f.tiles, f.ntiles,
-                                                f.row_gate);
+  if (!f.tiles_ready)
+    build_tiles_kernel<<<1, kMaxExperts, 0, st>>>(f.offsets, G, gp.BM, f.E, f.k, f.row_token,
+                                                  f.row_slot, f.topk_w, f.tiles, f.ntiles,
+                                                  f.row_gate);
   switch (gp.shape) {
     case kGemmF32: run_generic<float, 64, 64, 64, 32, 2, 2>(gp, f, st); break;
     case kGemmBf16Large: run_generic<bf16, 128, 128, 128, 64, 2, 2>(gp, f, st); break;

@@ -59,7 +59,27 @@ struct FfnArgs {
   RowTile* tiles;    // [tiles_max]
   int32_t* ntiles;   // [1]
   float* row_gate;   // [rows_max]
+  int tiles_ready;   // tiles, ntiles and row_gate already written by the dispatch
 };
+
+// Everything the single-block dispatch reads and writes.
+struct DispatchArgs {
+  const int32_t* topk_idx;  // [T, k]
+  const float* topk_w;      // [T, k]
+  const int32_t* hist;      // [nb, E] pairs per 64-token block and expert
+  const double* stat_part;  // [nb, E] per-block sums of router probabilities
+  int64_t T;
+  int nb, E, k, capacity, shared, BM;
+  int32_t *counts, *kept, *offsets, *row_token, *row_slot, *inv;
+  float* row_gate;
+  RowTile* tiles;
+  int32_t* ntiles;
+  float *mean_prob, *balance;  // optional
+};
+
+// per-block bases of the single-block dispatch live in LDS: nb * E must fit
+constexpr int kDispatchLdsBases = 8192;
+inline bool dispatch_one_block(int64_t nb, int E) { return nb * E <= kDispatchLdsBases; }
 
 hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const float* Wg,
                          const float* bg, float* part, int32_t* topk_idx, float* topk_w,
@@ -70,6 +90,8 @@ hipError_t launch_dispatch(int64_t T, int E, int k, int capacity, int shared, in
                            const int32_t* topk_idx, bool need_hist, int32_t* hist, int32_t* base,
                            int32_t* counts, int32_t* kept, int32_t* offsets, int32_t* row_token,
                            int32_t* row_slot, int32_t* inv, hipStream_t st);
+
+hipError_t launch_dispatch_one_block(const DispatchArgs& a, hipStream_t st);
 
 hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& a, hipStream_t st);
 

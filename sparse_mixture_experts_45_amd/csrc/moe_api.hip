@@ -161,7 +161,8 @@ moe_status check_weights(const moe_config* c, const moe_weights* w) {
 
 moe_status run_ffn(const moe_config* c, const Layout& L, const void* x, const moe_weights* w,
                    const int32_t* offsets, const int32_t* row_token, const int32_t* row_slot,
-                   const float* topk_w, float* y_rows, void* ws, hipStream_t st) {
+                   const float* topk_w, float* y_rows, void* ws, hipStream_t st,
+                   bool tiles_ready = false) {
   FfnArgs f{};
   f.T = c->T;
   f.d = c->d_model;
@@ -189,6 +190,7 @@ moe_status run_ffn(const moe_config* c, const Layout& L, const void* x, const mo
   f.tiles = reinterpret_cast<RowTile*>(at(ws, L.tiles));
   f.ntiles = reinterpret_cast<int32_t*>(at(ws, L.ntiles));
   f.row_gate = reinterpret_cast<float*>(at(ws, L.row_gate));
+  f.tiles_ready = tiles_ready ? 1 : 0;
   return hip_status(launch_ffn(L.gp, f, st));
 }
 
@@ -284,19 +286,50 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
   int32_t* hist = reinterpret_cast<int32_t*>(at(ws, L.hist));
   float* y_rows = reinterpret_cast<float*>(at(ws, L.y_rows));
 
+  double* stat_part = reinterpret_cast<double*>(at(ws, L.stat));
+  // small batches: the whole dispatch (and the load statistics) in one block
+  const bool one = dispatch_one_block(L.rp.nb, cfg->n_experts);
   if ((s = hip_status(launch_router(L.rp, x, cfg->dtype, w->Wg, w->bg,
                                     reinterpret_cast<float*>(at(ws, L.part)), topk_idx, topk_w,
-                                    nullptr, reinterpret_cast<double*>(at(ws, L.stat)), hist,
-                                    o.mean_prob, o.balance, st))) != MOE_OK)
+                                    nullptr, stat_part, hist, one ? nullptr : o.mean_prob,
+                                    one ? nullptr : o.balance, st))) != MOE_OK)
     return s;
   // the gate kernel already wrote the per-block expert histogram
-  if ((s = hip_status(launch_dispatch(cfg->T, cfg->n_experts, cfg->top_k, cfg->capacity,
-                                      cfg->shared_d_ff > 0, L.rp.nb, topk_idx, false, hist,
-                                      reinterpret_cast<int32_t*>(at(ws, L.base)), counts, kept,
-                                      offsets, row_token, row_slot, inv, st))) != MOE_OK)
+  if (one) {
+    DispatchArgs d{};
+    d.topk_idx = topk_idx;
+    d.topk_w = topk_w;
+    d.hist = hist;
+    d.stat_part = stat_part;
+    d.T = cfg->T;
+    d.nb = L.rp.nb;
+    d.E = cfg->n_experts;
+    d.k = cfg->top_k;
+    d.capacity = cfg->capacity;
+    d.shared = cfg->shared_d_ff > 0;
+    d.BM = L.gp.BM;
+    d.counts = counts;
+    d.kept = kept;
+    d.offsets = offsets;
+    d.row_token = row_token;
+    d.row_slot = row_slot;
+    d.inv = inv;
+    d.row_gate = reinterpret_cast<float*>(at(ws, L.row_gate));
+    d.tiles = reinterpret_cast<RowTile*>(at(ws, L.tiles));
+    d.ntiles = reinterpret_cast<int32_t*>(at(ws, L.ntiles));
+    d.mean_prob = o.mean_prob;
+    d.balance = o.balance;
+    if ((s = hip_status(launch_dispatch_one_block(d, st))) != MOE_OK) return s;
+  } else if ((s = hip_status(launch_dispatch(cfg->T, cfg->n_experts, cfg->top_k, cfg->capacity,
+                                             cfg->shared_d_ff > 0, L.rp.nb, topk_idx, false,
+                                             hist, reinterpret_cast<int32_t*>(at(ws, L.base)),
+                                             counts, kept, offsets, row_token, row_slot, inv,
+                                             st))) != MOE_OK) {
     return s;
+  }
   if (cfg->T == 0) return MOE_OK;
-  if ((s = run_ffn(cfg, L, x, w, offsets, row_token, row_slot, topk_w, y_rows, ws, st)) != MOE_OK)
+  if ((s = run_ffn(cfg, L, x, w, offsets, row_token, row_slot, topk_w, y_rows, ws, st, one)) !=
+      MOE_OK)
     return s;
   return hip_status(launch_combine(cfg->T, cfg->d_model, cfg->n_experts, cfg->top_k,
                                    cfg->shared_d_ff > 0, cfg->dtype, y_rows, inv, offsets, y, st));

@@ -7,6 +7,7 @@
 // of Experts", router formula Softmax(TopK(x W_g)) and "Tiny example";
 // botmartz "Load Balancing" (mean router probability per expert).
 #include "kernels.h"
+#include "block_ops.h"
 
 namespace moe {
 
@@ -479,29 +480,13 @@ __global__ __launch_bounds__(kRw * 64) void router_gate_kernel(
       gsm, blockIdx.x, bg, T, E, k, renorm, topk_idx, topk_w, probs, stat_part, hist);
 }
 
-// mean_prob[e] = (sum over blocks, in block order) / T; balance = unbiased
-// variance of mean_prob over experts.  fp64 inside, fp32 out.
+// Load statistics from the per-block probability sums, one block.
 __global__ __launch_bounds__(1024) void router_stats_kernel(const double* __restrict__ stat_part,
                                                             int nb, int E, int64_t T,
                                                             float* __restrict__ mean_prob,
                                                             float* __restrict__ balance) {
-  __shared__ double mp[kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    double acc = 0.0;
-    for (int b = 0; b < nb; ++b) acc += stat_part[static_cast<int64_t>(b) * E + e];
-    const double v = acc / static_cast<double>(T);  // T = 0 gives NaN
-    mp[e] = v;
-    if (mean_prob) mean_prob[e] = static_cast<float>(v);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0 && balance) {
-    double mean = 0.0;
-    for (int e = 0; e < E; ++e) mean += mp[e];
-    mean /= static_cast<double>(E);
-    double var = 0.0;
-    for (int e = 0; e < E; ++e) var += (mp[e] - mean) * (mp[e] - mean);
-    balance[0] = static_cast<float>(var / static_cast<double>(E - 1));  // E = 1 gives NaN
-  }
+  __shared__ double wsd[kMaxExperts / 64];
+  load_stats(stat_part, nb, E, T, mean_prob, balance, wsd);
 }
 
 // ------------------------------------------------------------------ launches

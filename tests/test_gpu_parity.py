@@ -57,6 +57,15 @@ SMALL = [
     S("dma_small_capacity", T=700, d=128, F=256, E=8, k=2, capacity=150, router_bias="zipf1.1"),
     S("dma_skinny_shared", T=64, d=128, F=192, E=16, k=2, Fs=128),
     S("dma_skinny_many", T=96, d=256, F=128, E=64, k=6, router_bias="none"),
+    # router variants: fused gate with two values per lane, split-K scores with
+    # the gate adding the chunks, 64 lanes per token, fp32 split-K
+    S("router_fused_e24", T=250, d=96, F=64, E=24, k=3),
+    S("router_splitk_e160", T=200, d=1024, F=64, E=160, k=6),
+    S("router_e300", T=70, d=128, F=64, E=300, k=4, router_bias="none"),
+    S("router_f32_splitk", T=64, d=2048, F=64, E=8, k=2, dtype="f32"),
+    # 129 blocks x 64 experts: the per-block bases no longer fit one block's
+    # LDS, so the multi-kernel dispatch runs
+    S("dispatch_multiblock", T=8256, d=64, F=64, E=64, k=2, capacity=300),
 ]
 
 
@@ -124,6 +133,8 @@ def test_route_stage(shape):
     assert float(np.max(np.abs(probs.cpu().numpy() - ref["probs"]))) <= PROBS_ABS
     rel = np.abs(mp.cpu().numpy() - ref["mean_prob"]) / ref["mean_prob"]
     assert float(rel.max()) <= 1e-5
+    b, br = float(bal.cpu()[0]), ref["balance"]
+    assert abs(b - br) <= max(1e-4 * abs(br), 1e-9)
 
 
 @pytest.mark.parametrize("shape", [S("disp_cap", T=1000, E=16, k=3, capacity=150,
