@@ -17,9 +17,12 @@ Measurement legs:
     the host cores (rank 0, one GPU only).
 """
 import argparse
+import glob
+import hashlib
 import json
 import math
 import os
+import sqlite3
 import sys
 import time
 
@@ -46,7 +49,157 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--graph", type=int, default=1,
                    help="1: replay moe_forward from a captured HIP graph")
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE: a plain device "
+                        "copy of known size, then moe_expert_ffn calls")
+    p.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                   help="turn the two probe databases into the stored traffic summary")
     return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic of the expert GEMM from rocprofv3 counters.  FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch) are taken in two runs of the probe, each
+# scaled by what the same counter reads for a device-to-device copy of
+# COPY_BYTES; the summary records a hash of the kernel sources and is used
+# only while the sources are unchanged.
+COPY_BYTES = 256 << 20
+
+
+def source_hash():
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "sparse_mixture_experts_45_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "moe.h"))
+    for f in files:
+        if f.endswith((".hip", ".h")):
+            h.update(os.path.relpath(f, ROOT).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", "traffic_expert_gemm_%s.md" % workload)
+
+
+def stored_traffic(workload):
+    """Bytes per moe_expert_ffn call (up + down GEMM), or None if absent or stale."""
+    path = traffic_path(workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec["traffic_bytes_per_call"]
+
+
+def traffic_probe(args):
+    import torch
+    import sparse_mixture_experts_45_amd as moe
+    from moe_synth import make_inputs, to_device, workload
+
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    shape = workload(args.workload)
+    dev = to_device(make_inputs(shape, args.seed), "cuda")
+    tdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    cfg = moe.config(shape.T, shape.d, shape.F, shape.E, shape.k, act=shape.act, dtype=tdt,
+                     capacity=shape.capacity, renormalize=bool(shape.renormalize),
+                     shared_d_ff=shape.Fs)
+    ws = moe.workspace(cfg)
+    T, k, E = shape.T, shape.k, shape.E
+    nrows = T * k + (T if shape.Fs else 0)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    topk_idx, inv = torch.empty((T, k), **i32), torch.empty((T, k), **i32)
+    topk_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts, kept, offsets = torch.empty(E, **i32), torch.empty(E, **i32), torch.empty(E + 2, **i32)
+    row_token, row_slot = torch.empty(nrows, **i32), torch.empty(nrows, **i32)
+    y_rows = torch.empty((nrows, shape.d), dtype=torch.float32, device="cuda")
+    moe.moe_route(cfg, dev["x"], dev["Wg"], dev["bg"], topk_idx, topk_w, None, None, None, ws)
+    moe.moe_dispatch(cfg, topk_idx, counts, kept, offsets, row_token, row_slot, inv, ws)
+    for _ in range(5):
+        moe.moe_expert_ffn(cfg, dev["x"], dev, offsets, row_token, row_slot, topk_w, y_rows, ws)
+    torch.cuda.synchronize()
+    print("traffic probe done:", shape.name, flush=True)
+
+
+def _counter_rows(db, counter):
+    con = sqlite3.connect(db)
+    rows = con.execute("select dispatch_id, kernel_name, value from counters_collection "
+                       "where counter_name = ? order by dispatch_id", (counter,)).fetchall()
+    con.close()
+    return rows
+
+
+def traffic_summarize(args):
+    fetch_db, write_db = args.traffic_summarize
+    rec = {"workload": args.workload, "source_hash": source_hash(), "copy_bytes": COPY_BYTES}
+    kib = {}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        rows = _counter_rows(db, counter)
+        copies = [v for _, n, v in rows if "copyBuffer" in n][:3]
+        if len(copies) < 3:
+            sys.exit("no calibration copies in %s" % db)
+        factor = (COPY_BYTES / 1024.0) / float(np.mean(copies))
+        rec[counter.lower() + "_copy_kib"] = float(np.mean(copies))
+        rec[counter.lower() + "_factor"] = round(factor, 4)
+        for tag, flag in (("up", "true>"), ("down", "false>")):
+            vals = [v for _, n, v in rows if "grouped_gemm" in n and flag in n]
+            if not vals:
+                sys.exit("no %s GEMM dispatches in %s" % (tag, db))
+            kib[(tag, counter)] = (float(np.mean(vals)), len(vals), factor)
+    total = 0.0
+    rec["kernels"] = {}
+    for tag in ("up", "down"):
+        f_kib, n, f_fac = kib[(tag, "FETCH_SIZE")]
+        w_kib, _, w_fac = kib[(tag, "WRITE_SIZE")]
+        fb, wb = f_kib * 1024 * f_fac, w_kib * 1024 * w_fac
+        rec["kernels"][tag] = {"fetch_kib": round(f_kib, 1), "write_kib": round(w_kib, 1),
+                               "fetch_bytes": round(fb), "write_bytes": round(wb),
+                               "dispatches": n}
+        total += fb + wb
+    rec["traffic_bytes_per_call"] = round(total)
+    wl = args.workload
+    cmds = [
+        "cd /tmp && export TMPDIR=/tmp   # then, from the repository root:",
+        "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/traffic_fetch -o run -- "
+        "python3 bench.py --traffic-probe --workload %s" % wl,
+        "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/traffic_write -o run -- "
+        "python3 bench.py --traffic-probe --workload %s" % wl,
+        "python3 bench.py --workload %s --traffic-summarize "
+        "gpurun_out/traffic_fetch/run_results.db gpurun_out/traffic_write/run_results.db" % wl,
+    ]
+    lines = [
+        "# HBM traffic of the expert grouped GEMM: %s" % wl, "",
+        "FETCH_SIZE and WRITE_SIZE per dispatch (rocprofv3 `--pmc`, one counter per run), each "
+        "scaled by what the same counter reads for a device-to-device copy of %d MiB "
+        "(the first three `__amd_rocclr_copyBuffer` dispatches of the probe)." % (COPY_BYTES >> 20),
+        "", "Commands (committed files only):", "", "```"] + cmds + ["```", "",
+        "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | fetch bytes (scaled) | "
+        "write bytes (scaled) |", "|---|---|---|---|---|---|"]
+    for tag in ("up", "down"):
+        r = rec["kernels"][tag]
+        lines.append("| %s-projection | %d | %.1f | %.1f | %.0f | %.0f |" % (
+            tag, r["dispatches"], r["fetch_kib"], r["write_kib"], r["fetch_bytes"],
+            r["write_bytes"]))
+    lines += ["", "Calibration: copy FETCH_SIZE %.1f KiB (factor %.4f), WRITE_SIZE %.1f KiB "
+              "(factor %.4f) for %d KiB moved." % (rec["fetch_size_copy_kib"],
+                                                   rec["fetch_size_factor"],
+                                                   rec["write_size_copy_kib"],
+                                                   rec["write_size_factor"], COPY_BYTES >> 10),
+              "", "Traffic per moe_expert_ffn call (up + down): %.1f MB." % (total / 1e6),
+              "", "```json", json.dumps(rec, indent=1), "```", ""]
+    with open(traffic_path(wl), "w") as fh:
+        fh.write("\n".join(lines))
+    print(json.dumps(rec))
 
 
 def algorithmic(shape, kept_rows, hit_experts):
@@ -89,11 +242,18 @@ def cpu_baseline(shape, inp, seconds):
 
 def main():
     args = parse()
+    if args.traffic_summarize:
+        traffic_summarize(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the MoE layer here is the data-parallel "
               "replica of one GPU; multi-GPU runs are not part of this build "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if args.traffic_probe:
+        traffic_probe(args)
+        return
 
     import torch
     import sparse_mixture_experts_45_amd as moe
@@ -169,12 +329,26 @@ def main():
         for _ in range(3):
             moe.moe_expert_ffn(cfg, x, dev, offsets, row_token, row_slot, topk_w, y_rows, ws,
                                stream=stream)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for a, b in evs:
-            a.record(stream)
+    torch.cuda.synchronize()
+    # one moe_expert_ffn call (tile list, up GEMM, down GEMM) replayed from a
+    # graph, so the events bracket the three kernels without host launch gaps
+    ffn_graph = None
+    if args.graph:
+        ffn_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ffn_graph, stream=stream):
             moe.moe_expert_ffn(cfg, x, dev, offsets, row_token, row_slot, topk_w, y_rows, ws,
                                stream=stream)
+        torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            a.record(stream)
+            if ffn_graph is not None:
+                ffn_graph.replay()
+            else:
+                moe.moe_expert_ffn(cfg, x, dev, offsets, row_token, row_slot, topk_w, y_rows,
+                                   ws, stream=stream)
             b.record(stream)
     torch.cuda.synchronize()
     ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
@@ -190,8 +364,10 @@ def main():
         achieved = nbytes / (ffn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
-    roof.update(kernel="expert grouped GEMM: up-projection + down-projection launches of one "
-                       "moe_expert_ffn call", kernel_ms=round(ffn_ms, 4),
+    traffic = stored_traffic(shape.name)
+    roof["traffic"] = None if traffic is None else float(traffic)
+    roof.update(kernel="expert FFN: one moe_expert_ffn call (row-tile list, up-projection "
+                       "GEMM, down-projection GEMM)", kernel_ms=round(ffn_ms, 4),
                 algorithmic_flop=flop, algorithmic_bytes=nbytes)
 
     value = T * args.steps / elapsed

@@ -21,6 +21,8 @@
 // tile list, and the list is ordered group by group, in bands of kBand N tiles
 // with the group's row tiles fastest: the blocks that run together on one XCD
 // share the same weight columns and the same token rows.
+#include <type_traits>
+
 #include "kernels.h"
 #include "block_ops.h"
 
@@ -66,7 +68,7 @@ struct Mfma<float> {
 // t = 1 / (1 + p x) for x >= 0, odd in x; absolute error <= 1.5e-7.
 __device__ __forceinline__ float erf_as(float x) {
   const float ax = fabsf(x);
-  const float t = 1.0f / (1.0f + 0.3275911f * ax);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);  // 1 ulp: far below the 1.5e-7 bound
   const float poly =
       t * (0.254829592f +
            t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
@@ -542,30 +544,56 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
       }
     }
 
-    // epilogue of tile t (gates of this tile are in gate_s[gb])
+    // epilogue of tile t (gates of this tile are in gate_s[gb]).  Stores address
+    // the tile from one uniform base with 32-bit offsets; a full tile takes the
+    // path without bounds checks; the activation is chosen once per tile.
+    float bv[NI];
+    int ncol[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int n = cur.n0 + wn * WTN + j * 32 + (lane & 31);
-      if (n >= cur.N) continue;
-      const float bv = cur.bias ? bf16_to_f32(cur.bias[n].bits) : 0.f;
+      ncol[j] = wn * WTN + j * 32 + (lane & 31);  // column inside the tile
+      const int n = cur.n0 + ncol[j];
+      bv[j] = (cur.bias && n < cur.N) ? bf16_to_f32(cur.bias[n].bits) : 0.f;
+    }
+    constexpr int OE = UP ? 2 : 4;  // output element bytes
+    char* obase = static_cast<char*>(a.out) +
+                  (static_cast<int64_t>(cur.row0) * a.ldo + cur.n0) * OE;
+    const uint32_t ldo = static_cast<uint32_t>(a.ldo);
+    auto epilogue = [&](auto checked, auto relu) {
+      constexpr bool CHK = decltype(checked)::value;
+      constexpr bool RELU = decltype(relu)::value;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int m = wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-          if (m >= cur.rows) continue;
-          const float z = acc[i][j][q] + bv;
-          const int64_t o = static_cast<int64_t>(cur.row0 + m) * a.ldo + n;
-          if (UP) {
-            const float h = (a.act == MOE_ACT_RELU) ? fmaxf(z, 0.f) : gelu_erf(z);
-            static_cast<bf16*>(a.out)[o] = bf16{f32_to_bf16(h)};
-          } else {
-            static_cast<float*>(a.out)[o] = gate_s[gb][m] * z;
+          if (CHK && m >= cur.rows) continue;
+          const uint32_t orow = static_cast<uint32_t>(m) * ldo;
+          const float g = UP ? 1.f : gate_s[gb][m];
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            if (CHK && cur.n0 + ncol[j] >= cur.N) continue;
+            const float z = acc[i][j][q] + bv[j];
+            const uint32_t off = (orow + static_cast<uint32_t>(ncol[j])) * OE;
+            if constexpr (UP) {
+              const float h = RELU ? fmaxf(z, 0.f) : gelu_erf(z);
+              *reinterpret_cast<uint16_t*>(obase + off) = f32_to_bf16(h);
+            } else {
+              *reinterpret_cast<float*>(obase + off) = g * z;
+            }
           }
         }
-        // one 32x32 block at a time: keeps the epilogue's temporaries few
+        // one 32-row block at a time: keeps the epilogue's temporaries few
         __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    const bool full = cur.rows == BM && cur.n0 + BN <= cur.N;
+    if (UP && a.act == MOE_ACT_RELU) {
+      if (full) epilogue(std::false_type{}, std::true_type{});
+      else epilogue(std::true_type{}, std::true_type{});
+    } else {
+      if (full) epilogue(std::false_type{}, std::false_type{});
+      else epilogue(std::true_type{}, std::false_type{});
     }
     if (!has_next) break;
     cur = nxt;

@@ -37,7 +37,7 @@ struct DmaCfg {
   int BM, BNU, BND, BK, NS, WM, WN, OCC, PERSIST;
 };
 constexpr DmaCfg kDmaLarge{256, 256, 256, 64, 2, 2, 4, 2, 0};   // >= 768 rows per expert
-constexpr DmaCfg kDmaMid{128, 256, 256, 64, 2, 2, 4, 2, 1};     // >= 256
+constexpr DmaCfg kDmaMid{128, 128, 128, 64, 2, 2, 4, 2, 0};     // >= 256
 constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 4, 1, 4, 2, 1};    // >= 48
 constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 4, 1, 4, 2, 0};   // fewer: weight streaming
 
