@@ -17,7 +17,6 @@ Measurement legs:
     the host cores (rank 0, one GPU only).
 """
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -61,20 +60,26 @@ def parse():
 # HBM traffic of the expert GEMM from rocprofv3 counters.  FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch) are taken in two runs of the probe, each
 # scaled by what the same counter reads for a device-to-device copy of
-# COPY_BYTES; the summary records a hash of the kernel sources and is used
-# only while the sources are unchanged.
+# COPY_BYTES; the summary records a hash of the GEMM kernel's sources and is
+# used only while they are unchanged.
 COPY_BYTES = 256 << 20
+
+
+# sources of the grouped-GEMM kernels whose traffic is stored (the kernel file and
+# every header it includes)
+GEMM_SOURCES = ["sparse_mixture_experts_45_amd/csrc/gemm.hip",
+                "sparse_mixture_experts_45_amd/csrc/kernels.h",
+                "sparse_mixture_experts_45_amd/csrc/common.h",
+                "sparse_mixture_experts_45_amd/csrc/block_ops.h",
+                "include/moe.h"]
 
 
 def source_hash():
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "sparse_mixture_experts_45_amd", "csrc", "*")))
-    files.append(os.path.join(ROOT, "include", "moe.h"))
-    for f in files:
-        if f.endswith((".hip", ".h")):
-            h.update(os.path.relpath(f, ROOT).encode())
-            with open(f, "rb") as fh:
-                h.update(fh.read())
+    for rel in GEMM_SOURCES:
+        h.update(rel.encode())
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -88,6 +88,7 @@ __device__ inline void load_stats(const double* __restrict__ stat_part, int nb, 
   double mp = 0.0;
   if (e < E) {
     double acc = 0.0;
+#pragma unroll 8
     for (int b = 0; b < nb; ++b) acc += stat_part[static_cast<int64_t>(b) * E + e];
     mp = acc / static_cast<double>(T);
     if (mean_prob) mean_prob[e] = static_cast<float>(mp);

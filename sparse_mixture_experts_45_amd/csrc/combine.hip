@@ -23,39 +23,64 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = u;
 }
 
-template <typename OT>
+// One thread per 4 columns of one token; the grid is (T, ceil(d / 1024)) so a
+// wide row is spread over several blocks.  The token's row indices are uniform
+// over the block; all k (+1) row loads are issued before the additions, which
+// then run in slot order.  KM >= k slots are unrolled.
+template <typename OT, int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_rows,
                                                       const int32_t* __restrict__ inv,
                                                       const int32_t* __restrict__ offsets,
                                                       int64_t T, int d, int E, int k, int shared,
                                                       OT* __restrict__ y) {
-  __shared__ int32_t rows_s[kMaxTopK + 1];
   const int64_t t = blockIdx.x;
-  if (threadIdx.x < k) rows_s[threadIdx.x] = inv[t * k + threadIdx.x];
-  if (threadIdx.x == 0) rows_s[kMaxTopK] = shared ? offsets[E] + static_cast<int32_t>(t) : -1;
-  __syncthreads();
-  for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = 0; i < k; ++i) {
-      const int r = rows_s[i];
-      if (r >= 0) {
-        const float4 v = *reinterpret_cast<const float4*>(y_rows + static_cast<int64_t>(r) * d + c);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
-      }
-    }
-    const int rs = rows_s[kMaxTopK];
-    if (rs >= 0) {
-      const float4 v = *reinterpret_cast<const float4*>(y_rows + static_cast<int64_t>(rs) * d + c);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
-    }
-    store4<OT>(y + t * d + c, acc);
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c >= d) return;
+  int rows[KM];
+  float4 v[KM];
+#pragma unroll
+  for (int i = 0; i < KM; ++i) {
+    rows[i] = i < k ? inv[t * k + i] : -1;
+    v[i] = rows[i] >= 0
+               ? *reinterpret_cast<const float4*>(y_rows + static_cast<int64_t>(rows[i]) * d + c)
+               : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  const int rs = shared ? offsets[E] + static_cast<int32_t>(t) : -1;
+  const float4 vs = rs >= 0
+                        ? *reinterpret_cast<const float4*>(y_rows + static_cast<int64_t>(rs) * d + c)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < KM; ++i) {
+    if (rows[i] >= 0) {
+      acc.x += v[i].x;
+      acc.y += v[i].y;
+      acc.z += v[i].z;
+      acc.w += v[i].w;
+    }
+  }
+  if (rs >= 0) {
+    acc.x += vs.x;
+    acc.y += vs.y;
+    acc.z += vs.z;
+    acc.w += vs.w;
+  }
+  store4<OT>(y + t * d + c, acc);
+}
+
+template <typename OT>
+static void run_combine(int64_t T, int d, int E, int k, int shared, const float* y_rows,
+                        const int32_t* inv, const int32_t* offsets, OT* y, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(ceil_div(d, 1024)));
+#define MOE_COMB(KM) \
+  combine_kernel<OT, KM><<<grid, 256, 0, st>>>(y_rows, inv, offsets, T, d, E, k, shared, y)
+  if (k <= 1) MOE_COMB(1);
+  else if (k <= 2) MOE_COMB(2);
+  else if (k <= 4) MOE_COMB(4);
+  else if (k <= 8) MOE_COMB(8);
+  else if (k <= 16) MOE_COMB(16);
+  else MOE_COMB(32);
+#undef MOE_COMB
 }
 
 hipError_t launch_combine(int64_t T, int d, int E, int k, int shared, int dtype,
@@ -63,11 +88,9 @@ hipError_t launch_combine(int64_t T, int d, int E, int k, int shared, int dtype,
                           void* y, hipStream_t st) {
   if (T > 0) {
     if (dtype == MOE_BF16)
-      combine_kernel<bf16><<<static_cast<unsigned>(T), 256, 0, st>>>(y_rows, inv, offsets, T, d, E,
-                                                                     k, shared, static_cast<bf16*>(y));
+      run_combine<bf16>(T, d, E, k, shared, y_rows, inv, offsets, static_cast<bf16*>(y), st);
     else
-      combine_kernel<float><<<static_cast<unsigned>(T), 256, 0, st>>>(y_rows, inv, offsets, T, d, E,
-                                                                      k, shared, static_cast<float*>(y));
+      run_combine<float>(T, d, E, k, shared, y_rows, inv, offsets, static_cast<float*>(y), st);
   }
   return hipGetLastError();
 }

@@ -39,58 +39,94 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
   for (int e = threadIdx.x; e < E; e += 256) hist[b * E + e] = h[e];
 }
 
-// Scan of the per-block histogram by one block of kMaxExperts threads.
-// Thread e * chunks + c owns expert e and the c-th contiguous range of blocks;
-// one block-wide scan of the range sums in thread order gives, for every
-// range, the expert's pairs in earlier ranges (subtracting the value at the
-// expert's first range), and the expert's total.  kept = min(count, C);
+// Scan of the per-block histogram by one block of kMaxExperts threads.  The
+// blocks are cut into `chunks` contiguous ranges.  Pass 1: thread (c, e) =
+// (tid / E, tid % E) sums expert e over range c (consecutive threads read
+// consecutive experts: coalesced, and free of LDS bank conflicts).  The range
+// sums go to sh in expert-major order with an odd row stride; one block-wide
+// scan in that order gives, for every (expert, range), the pairs of the expert
+// in earlier ranges (minus the value at the expert's first range) and the
+// expert's total.  Pass 2: thread (c, e) walks its range again and writes
+// base[b][e] = pairs of expert e in blocks before b.  kept = min(count, C);
 // offsets = exclusive scan of kept, offsets[E] = routed rows, offsets[E + 1] =
-// routed + shared rows.  base[b][e] (LDS or global) = pairs of expert e in
-// blocks before b.  Integer sums: exact in any order.  Ends with a barrier.
-__device__ void scan_hist(const int32_t* __restrict__ hist, int nb, int E, int64_t T,
-                          int capacity, int shared, int32_t* base, int32_t* __restrict__ counts,
-                          int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
-                          int32_t* skept, int32_t* soff, int32_t* sh, int32_t* wsum) {
+// routed + shared rows.  With INLDS, base, skept and soff are LDS and base
+// (nb * E entries) is first filled with the histogram.  sh: 2 * kMaxExperts
+// ints of LDS.  Integer sums: exact in any order.  Ends with a barrier.
+template <bool INLDS>
+__device__ __forceinline__ void scan_hist(const int32_t* __restrict__ ghist, int nb, int E,
+                                          int64_t T, int capacity, int shared, int32_t* base,
+                                          int32_t* __restrict__ counts,
+                                          int32_t* __restrict__ kept,
+                                          int32_t* __restrict__ offsets, int32_t* skept,
+                                          int32_t* soff, int32_t* sh, int32_t* wsum) {
   const int tid = threadIdx.x;
+  if constexpr (INLDS) {
+    // coalesced copy; all of a thread's loads are issued before the stores
+    constexpr int CP = kDispatchLdsBases / kMaxExperts;
+    const int n = nb * E;
+    int v[CP];
+#pragma unroll
+    for (int c = 0; c < CP; ++c)
+      v[c] = tid + c * kMaxExperts < n ? ghist[tid + c * kMaxExperts] : 0;
+#pragma unroll
+    for (int c = 0; c < CP; ++c)
+      if (tid + c * kMaxExperts < n) base[tid + c * kMaxExperts] = v[c];
+    __syncthreads();
+  }
+  // read from LDS (INLDS) or global memory, chosen at compile time so each
+  // access is a plain LDS or global instruction
+  const int32_t* hist = INLDS ? base : ghist;
   const int chunks = max(1, min(kMaxExperts / E, nb));
-  const int e = tid / chunks, c = tid % chunks;
-  const bool own = e < E;
   const int len = (nb + chunks - 1) / chunks;
-  const int b0 = c * len, b1 = min(nb, b0 + len);
-  int sum = 0;
-  if (own)
-    for (int b = b0; b < b1; ++b) sum += hist[static_cast<int64_t>(b) * E + e];
-  int total;
-  const int ex = block_excl_scan(sum, wsum, total);
-  sh[tid] = ex;
+  const int P = chunks + 1;  // odd row stride of the expert-major range sums
+  // pass 1: range sums, thread (c, e)
+  const int c1 = tid / E, e1 = tid - c1 * E;
+  const bool own1 = c1 < chunks;
+  const int b0 = c1 * len, b1 = min(nb, b0 + len);
+  if (own1) {
+    int sum = 0;
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) sum += hist[static_cast<int64_t>(b) * E + e1];
+    sh[e1 * P + c1] = sum;
+  }
   __syncthreads();
-  if (own) {
-    int run = ex - sh[e * chunks];
+  // expert-major scan, thread (e, c)
+  const int e2 = tid / chunks, c2 = tid - e2 * chunks;
+  const bool own2 = e2 < E;
+  int total;
+  const int ex = block_excl_scan(own2 ? sh[e2 * P + c2] : 0, wsum, total);
+  if (own2) sh[e2 * P + c2] = ex;
+  __syncthreads();
+  // pass 2: bases, thread (c, e)
+  if (own1) {
+    int run = sh[e1 * P + c1] - sh[e1 * P];
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) {
-      base[static_cast<int64_t>(b) * E + e] = run;
-      run += hist[static_cast<int64_t>(b) * E + e];
+      const int h = hist[static_cast<int64_t>(b) * E + e1];  // read before base overwrites it
+      base[static_cast<int64_t>(b) * E + e1] = run;
+      run += h;
     }
   }
   int kp = 0;
   if (tid < E) {
-    const int s1 = (tid + 1) * chunks < kMaxExperts ? sh[(tid + 1) * chunks] : total;
-    const int cnt = s1 - sh[tid * chunks];
+    const int s1 = tid + 1 < E ? sh[(tid + 1) * P] : total;
+    const int cnt = s1 - sh[tid * P];
     kp = capacity < 0 ? cnt : min(cnt, capacity);
     counts[tid] = cnt;
     kept[tid] = kp;
-    if (skept) skept[tid] = kp;
+    if (INLDS) skept[tid] = kp;
   }
   int ktot;
   const int kx = block_excl_scan(kp, wsum, ktot);
   if (tid < E) {
     offsets[tid] = kx;
-    if (soff) soff[tid] = kx;
+    if (INLDS) soff[tid] = kx;
   }
   if (tid == 0) {
     const int end = ktot + (shared ? static_cast<int32_t>(T) : 0);
     offsets[E] = ktot;
     offsets[E + 1] = end;
-    if (soff) {
+    if (INLDS) {
       soff[E] = ktot;
       soff[E + 1] = end;
     }
@@ -102,10 +138,10 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     const int32_t* __restrict__ hist, int nb, int E, int64_t T, int capacity, int shared,
     int32_t* __restrict__ base, int32_t* __restrict__ counts, int32_t* __restrict__ kept,
     int32_t* __restrict__ offsets) {
-  __shared__ int32_t sh[kMaxExperts];
+  __shared__ int32_t sh[2 * kMaxExperts];
   __shared__ int32_t wsum[kMaxExperts / 64];
-  scan_hist(hist, nb, E, T, capacity, shared, base, counts, kept, offsets, nullptr, nullptr, sh,
-            wsum);
+  scan_hist<false>(hist, nb, E, T, capacity, shared, base, counts, kept, offsets, nullptr, nullptr,
+                   sh, wsum);
 }
 
 // Expert ids (and, with topk_w set, gates) of the pairs of 64-token block b,
@@ -214,10 +250,13 @@ __device__ __forceinline__ void scatter_block_few(int64_t b, const int (&mine)[K
   }
 }
 
-// Any k: slots rolled, each pair placed as soon as its rank is known; ids and
-// gates read from cache (keeps the registers few for large k).
-__device__ __forceinline__ void scatter_block_any(int64_t b, const int32_t* __restrict__ topk_idx,
-                                                  const float* __restrict__ topk_w, int64_t T,
+// Any k: slots rolled, each pair placed as soon as its rank is known (keeps the
+// registers few for large k).  Slot j of the block's token `lane` is read from
+// ids[lane * ids_stride + j] and its gate from gates[lane * ids_stride + j]
+// (gates only needed with row_gate): LDS copies of the block's ids and gates
+// when they fit, else topk_idx / topk_w themselves.
+__device__ __forceinline__ void scatter_block_any(int64_t b, const int32_t* ids, int ids_stride,
+                                                  const float* gates, int64_t T,
                                                   int k, int E, int nbits, const int32_t* base,
                                                   const int32_t* kept, const int32_t* offsets,
                                                   int shared, int32_t* __restrict__ row_token,
@@ -228,18 +267,48 @@ __device__ __forceinline__ void scatter_block_any(int64_t b, const int32_t* __re
   const int64_t t = b * kGateTokens + lane;
   const bool valid = t < T;
   const uint64_t live = __ballot(valid) & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)));
+  const int32_t* my = ids + lane * ids_stride;
+  const float* myg = gates ? gates + lane * ids_stride : nullptr;
   for (int i = 0; i < k; ++i) {
-    const int ei = valid ? topk_idx[t * k + i] : 0;
+    const int ei = valid ? my[i] : 0;
     int rank = 0;
-    for (int j = 0; j < k; ++j) {
-      const int v = valid ? topk_idx[t * k + j] : 0;
-      rank += lower_matches(v, ei, nbits, live);
-    }
+    for (int j = 0; j < k; ++j) rank += lower_matches(valid ? my[j] : 0, ei, nbits, live);
     if (valid)
-      place_pair(t, i, k, ei, rank, E, base, kept, offsets, row_gate ? topk_w[t * k + i] : 0.f,
-                 row_token, row_slot, inv, row_gate);
+      place_pair(t, i, k, ei, rank, E, base, kept, offsets, myg ? myg[i] : 0.f, row_token,
+                 row_slot, inv, row_gate);
   }
   if (valid && shared) place_shared(t, E, offsets, row_token, row_slot, row_gate);
+}
+
+// Copy the ids (and, with wdst set, the gates) of 64-token block b (64 x k,
+// k <= kIdsK) into a wave's LDS area, row stride kIdsK + 1 (odd: the per-slot
+// reads of 64 lanes spread over banks).
+constexpr int kIdsK = 8;
+__device__ __forceinline__ void stage_ids(int64_t b, const int32_t* __restrict__ topk_idx,
+                                          const float* __restrict__ topk_w, int64_t T, int k,
+                                          int32_t* dst, float* wdst) {
+  const int lane = threadIdx.x & 63;
+  const int64_t f0 = b * kGateTokens * k;
+  const int64_t fend = T * k;
+  // all loads first (one latency), then the LDS stores
+  int iv[kIdsK];
+  float wv[kIdsK];
+#pragma unroll
+  for (int c = 0; c < kIdsK; ++c) {
+    const int f = lane + c * 64;
+    const bool in = f < kGateTokens * k && f0 + f < fend;
+    iv[c] = in ? topk_idx[f0 + f] : 0;
+    wv[c] = (in && wdst) ? topk_w[f0 + f] : 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < kIdsK; ++c) {
+    const int f = lane + c * 64;
+    if (f < kGateTokens * k) {
+      const int r = f / k, j = f - r * k;
+      dst[r * (kIdsK + 1) + j] = iv[c];
+      if (wdst) wdst[r * (kIdsK + 1) + j] = wv[c];
+    }
+  }
 }
 
 template <int KM>
@@ -256,8 +325,15 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(
     scatter_block_few<KM>(b, mine, wsel, T, k, E, nbits, base + b * E, kept, offsets, shared,
                           row_token, row_slot, inv, nullptr);
   } else {
-    scatter_block_any(b, topk_idx, nullptr, T, k, E, nbits, base + b * E, kept, offsets, shared,
-                      row_token, row_slot, inv, nullptr);
+    __shared__ int32_t sids[kGateTokens * (kIdsK + 1)];
+    if (k <= kIdsK) {
+      stage_ids(b, topk_idx, nullptr, T, k, sids, nullptr);
+      scatter_block_any(b, sids, kIdsK + 1, nullptr, T, k, E, nbits, base + b * E, kept,
+                        offsets, shared, row_token, row_slot, inv, nullptr);
+    } else {
+      scatter_block_any(b, topk_idx + b * kGateTokens * k, k, nullptr, T, k, E, nbits,
+                        base + b * E, kept, offsets, shared, row_token, row_slot, inv, nullptr);
+    }
   }
 }
 
@@ -270,17 +346,20 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(
 template <int KM>
 __global__ __launch_bounds__(1024) void dispatch_one_block_kernel(DispatchArgs a) {
   __shared__ int32_t sbase[kDispatchLdsBases];
-  __shared__ int32_t sh[kMaxExperts];
+  __shared__ int32_t sh[2 * kMaxExperts];
   __shared__ int32_t wsum[kMaxExperts / 64];
   __shared__ double wsd[kMaxExperts / 64];
   __shared__ int32_t skept[kMaxExperts];
   __shared__ int32_t soff[kMaxExperts + 2];
+  __shared__ int32_t sids[KM <= 4 ? 1 : kMaxExperts / 64][KM <= 4 ? 1 : kGateTokens * (kIdsK + 1)];
+  __shared__ float sgts[KM <= 4 ? 1 : kMaxExperts / 64][KM <= 4 ? 1 : kGateTokens * (kIdsK + 1)];
   const int tid = threadIdx.x, wave = tid >> 6;
   const int E = a.E, nb = a.nb;
   constexpr int kWaves = kMaxExperts / 64;
-  // few slots: the ids and gates of the wave's first two 64-token blocks do
-  // not depend on the scan, so their loads go out first and overlap it
-  constexpr int PF = KM <= 4 ? 2 : 0;
+  // few slots: the ids and gates of the wave's first 64-token blocks (up to 8
+  // ids per lane) do not depend on the scan, so their loads go out first and
+  // overlap it
+  constexpr int PF = KM == 1 ? 8 : KM == 2 ? 4 : KM == 4 ? 2 : 0;
   constexpr int KP = KM <= 4 ? KM : 1;
   int mine[PF > 0 ? PF : 1][KP];
   float wsel[PF > 0 ? PF : 1][KP];
@@ -291,8 +370,8 @@ __global__ __launch_bounds__(1024) void dispatch_one_block_kernel(DispatchArgs a
   if (a.mean_prob || a.balance)
     load_stats(a.stat_part, nb, E, a.T, a.mean_prob, a.balance, wsd);
 
-  scan_hist(a.hist, nb, E, a.T, a.capacity, a.shared, sbase, a.counts, a.kept, a.offsets, skept,
-            soff, sh, wsum);
+  scan_hist<true>(a.hist, nb, E, a.T, a.capacity, a.shared, sbase, a.counts, a.kept, a.offsets,
+                  skept, soff, sh, wsum);
   build_tile_list(soff, E + (a.shared ? 1 : 0), a.BM, a.tiles, a.ntiles, wsum);
 
   int nbits = 1;
@@ -311,9 +390,19 @@ __global__ __launch_bounds__(1024) void dispatch_one_block_kernel(DispatchArgs a
                             a.shared, a.row_token, a.row_slot, a.inv, a.row_gate);
     }
   } else {
-    for (int b = wave; b < nb; b += kWaves)
-      scatter_block_any(b, a.topk_idx, a.topk_w, a.T, a.k, E, nbits, sbase + b * E, skept, soff,
-                        a.shared, a.row_token, a.row_slot, a.inv, a.row_gate);
+    for (int b = wave; b < nb; b += kWaves) {
+      if (a.k <= kIdsK) {
+        stage_ids(b, a.topk_idx, a.topk_w, a.T, a.k, sids[wave], sgts[wave]);
+        scatter_block_any(b, sids[wave], kIdsK + 1, sgts[wave], a.T, a.k, E, nbits,
+                          sbase + b * E, skept, soff, a.shared, a.row_token, a.row_slot, a.inv,
+                          a.row_gate);
+      } else {
+        const int64_t f0 = static_cast<int64_t>(b) * kGateTokens * a.k;
+        scatter_block_any(b, a.topk_idx + f0, a.k, a.topk_w + f0, a.T, a.k, E, nbits,
+                          sbase + b * E, skept, soff, a.shared, a.row_token, a.row_slot, a.inv,
+                          a.row_gate);
+      }
+    }
   }
 }
 

@@ -80,19 +80,17 @@ RoutePlan route_plan(const moe_config* c) {
   p.k = c->top_k;
   p.renorm = c->renormalize;
   p.nb = static_cast<int>(ceil_div(c->T, kGateTokens));
-  // bf16 layers whose experts fit one score tile (E <= 64): one K chunk, and
-  // the gate runs inside the score kernel.  Otherwise split d so the score
-  // kernel has >= ~256 blocks, each K slice of a block keeping >= 2 K steps.
+  // Split d so the score kernel has >= ~256 blocks, each K slice of a block
+  // keeping >= 2 K steps.  bf16 layers whose experts fit one score tile
+  // (E <= 64) and that gain nothing from a split run the gate inside the score
+  // kernel (one launch).
   const int TE = c->n_experts <= 16 ? 16 : 64;
   const int QK = 16 / (TE / 16);
-  p.fused = c->dtype == MOE_BF16 && c->n_experts <= 64;
-  int S = 1;
-  if (!p.fused) {
-    const int64_t base_blocks = ceil_div(c->T, 64) * ceil_div(c->n_experts, TE);
-    S = static_cast<int>(std::max<int64_t>(1, ceil_div(256, std::max<int64_t>(1, base_blocks))));
-    S = std::min(S, std::max(1, c->d_model / (QK * 64)));
-    S = std::min(S, 16);
-  }
+  const int64_t base_blocks = ceil_div(c->T, 64) * ceil_div(c->n_experts, TE);
+  int S = static_cast<int>(std::max<int64_t>(1, ceil_div(256, std::max<int64_t>(1, base_blocks))));
+  S = std::min(S, std::max(1, c->d_model / (QK * 64)));
+  S = std::min(S, 16);
+  p.fused = c->dtype == MOE_BF16 && c->n_experts <= 64 && S == 1;
   p.kchunk = static_cast<int>(align_up(ceil_div(c->d_model, S), 32));
   p.S = static_cast<int>(ceil_div(c->d_model, p.kchunk));
   // gate: 16 lanes per token up to 256 experts (DPP-only reductions), else 64

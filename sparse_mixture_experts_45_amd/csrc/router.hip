@@ -64,14 +64,15 @@ __device__ __forceinline__ void group_argmax(float& bv, int& be) {
 // ---------------------------------------------------------------------------
 // Gate of one block of kGateTokens tokens, kRw waves of kGateTokens / kRw
 // tokens.  A token's E scores are spread over LPT lanes (16, or 64 for E > 256),
-// VPL values per lane: expert e = s + v * LPT for lane sub-index s.  Max, sum
-// and each of the k argmax rounds are all-reduces inside the LPT group, so
-// every lane of the group ends with identical values and lane s keeps the
-// selections of rounds s, s + LPT, ...  Ties pick the lower expert index.
-// Per-block sums of the probabilities (fp64) are reduced in a fixed order; the
-// per-block count of (token, slot) pairs per expert uses LDS integer atomics,
-// whose result does not depend on their order.  `logit(tl, e)` gives the raw
-// score (bias excluded) of local token tl and expert e.
+// VPL consecutive experts per lane: lane sub-index s holds experts s * VPL + v,
+// so the scores of a lane load as vectors.  Max, sum and each of the k argmax
+// rounds are all-reduces inside the LPT group, so every lane of the group ends
+// with identical values and lane s keeps the selections of rounds s, s + LPT,
+// ...  Ties pick the lower expert index.  Per-block sums of the probabilities
+// (fp64) are reduced in a fixed order; the per-block count of (token, slot)
+// pairs per expert uses LDS integer atomics, whose result does not depend on
+// their order.  `load(tl, e0, l)` fills l[v] with the raw score (bias excluded)
+// of local token tl and expert e0 + v (entries past E are ignored).
 // ---------------------------------------------------------------------------
 template <int EM>
 struct GateSmem {  // EM: largest expert count the block handles
@@ -79,8 +80,8 @@ struct GateSmem {  // EM: largest expert count the block handles
   int32_t hcnt[EM];
 };
 
-template <int LPT, int VPL, int EM, class Logit>
-__device__ __forceinline__ void gate_block(Logit logit, GateSmem<EM>& sm, int64_t blk,
+template <int LPT, int VPL, int EM, class Load>
+__device__ __forceinline__ void gate_block(Load load, GateSmem<EM>& sm, int64_t blk,
                                            const float* __restrict__ bg, int64_t T, int E,
                                            int k, int renorm, int32_t* __restrict__ topk_idx,
                                            float* __restrict__ topk_w, float* __restrict__ probs,
@@ -93,6 +94,7 @@ __device__ __forceinline__ void gate_block(Logit logit, GateSmem<EM>& sm, int64_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s = lane & (LPT - 1);
   const int grp = lane / LPT;
+  const int e0 = s * VPL;
   for (int e = tid; e < E; e += kRw * 64) sm.hcnt[e] = 0;
   __syncthreads();
 
@@ -108,14 +110,16 @@ __device__ __forceinline__ void gate_block(Logit logit, GateSmem<EM>& sm, int64_
     const bool vt = local < TPW && t < T;
     float l[VPL];
 #pragma unroll
+    for (int v = 0; v < VPL; ++v) l[v] = -INFINITY;
+    if (vt && e0 < E) load(tl, e0, l);
+#pragma unroll
     for (int v = 0; v < VPL; ++v) {
-      const int e = s + v * LPT;
-      float z = -INFINITY;
+      const int e = e0 + v;
       if (vt && e < E) {
-        z = logit(tl, e);
-        if (bg) z += bg[e];
+        if (bg) l[v] += bg[e];
+      } else {
+        l[v] = -INFINITY;
       }
-      l[v] = z;
     }
     float m = l[0];
 #pragma unroll
@@ -131,7 +135,7 @@ __device__ __forceinline__ void gate_block(Logit logit, GateSmem<EM>& sm, int64_
     sum = group_sum<LPT>(sum);
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-      const int e = s + v * LPT;
+      const int e = e0 + v;
       const float p = pz[v] / sum;
       if (vt && e < E) {
         if (probs) probs[t * E + e] = p;
@@ -154,15 +158,15 @@ __device__ __forceinline__ void gate_block(Logit logit, GateSmem<EM>& sm, int64_
       int be = 0x7fffffff;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const int e = s + v * LPT;
-        if (e < E && !((taken >> v) & 1u) && (l[v] > bv || (l[v] == bv && e < be))) {
+        // ascending v: on equal scores the lower expert stays
+        if (!((taken >> v) & 1u) && l[v] > bv) {
           bv = l[v];
-          be = e;
+          be = e0 + v;
         }
       }
       group_argmax<LPT>(bv, be);
-      if ((be & (LPT - 1)) == s) {
-        const int v = be / LPT;
+      if (be / VPL == s) {
+        const int v = be % VPL;
 #pragma unroll
         for (int vv = 0; vv < VPL; ++vv)
           if (vv == v) taken |= 1u << vv;
@@ -197,7 +201,7 @@ __device__ __forceinline__ void gate_block(Logit logit, GateSmem<EM>& sm, int64_
     if (grp == 0 && (wave >> 2) == round) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const int e = s + v * LPT;
+        const int e = e0 + v;
         if (e < E) sm.red_d[wave & 3][e] = round ? sm.red_d[wave & 3][e] + sacc[v] : sacc[v];
       }
     }
@@ -445,9 +449,14 @@ __global__ __launch_bounds__(kRw * 64) void router_scores_bf16_kernel(
   __syncthreads();
   if constexpr (FUSE) {
     __shared__ GateSmem<TE> gsm;
-    gate_block<LPT, VPL>([&](int tl, int ee) { return red[ee >> 4][tl * 16 + (ee & 15)]; }, gsm,
-                         blockIdx.x, bg, T, E, k, renorm, topk_idx, topk_w, probs, stat_part,
-                         hist);
+    // VPL divides 16: a lane's experts sit in one 16-expert column block
+    gate_block<LPT, VPL>(
+        [&](int tl, int ee0, float (&l)[VPL]) {
+          const float* src = &red[ee0 >> 4][tl * 16 + (ee0 & 15)];
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) l[v] = src[v];
+        },
+        gsm, blockIdx.x, bg, T, E, k, renorm, topk_idx, topk_w, probs, stat_part, hist);
   } else {
     for (int i = tid; i < kRtM * TE; i += kRw * 64) {
       const int tl = i / TE, el = i % TE;
@@ -471,11 +480,40 @@ __global__ __launch_bounds__(kRw * 64) void router_gate_kernel(
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kGateTokens;
   const int64_t n = T * E;
   gate_block<LPT, VPL>(
-      [&](int tl, int e) {
-        const int64_t i = (t0 + tl) * E + e;
-        float z = part[i];
-        for (int sp = 1; sp < S; ++sp) z += part[sp * n + i];
-        return z;
+      [&](int tl, int ee0, float (&l)[VPL]) {
+        const int64_t i = (t0 + tl) * E + ee0;
+        if (VPL % 4 == 0 && (E & 3) == 0 && ee0 + VPL <= E) {
+          // whole lane in range and 16-byte aligned: vector loads, chunks in order
+#pragma unroll
+          for (int v = 0; v < VPL; v += 4) {
+            const float4 z = *reinterpret_cast<const float4*>(part + i + v);
+            l[v] = z.x;
+            l[v + 1] = z.y;
+            l[v + 2] = z.z;
+            l[v + 3] = z.w;
+          }
+#pragma unroll 4
+          for (int sp = 1; sp < S; ++sp) {
+#pragma unroll
+            for (int v = 0; v < VPL; v += 4) {
+              const float4 z = *reinterpret_cast<const float4*>(part + sp * n + i + v);
+              l[v] += z.x;
+              l[v + 1] += z.y;
+              l[v + 2] += z.z;
+              l[v + 3] += z.w;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) {
+            if (ee0 + v < E) {
+              float z = part[i + v];
+#pragma unroll 4
+              for (int sp = 1; sp < S; ++sp) z += part[sp * n + i + v];
+              l[v] = z;
+            }
+          }
+        }
       },
       gsm, blockIdx.x, bg, T, E, k, renorm, topk_idx, topk_w, probs, stat_part, hist);
 }
