@@ -87,6 +87,10 @@ typedef struct {
   int32_t *kept;     /* [E] pairs that survived the capacity limit */
   float *mean_prob;  /* [E] mean router probability over tokens (NaN if T = 0) */
   float *balance;    /* [1] unbiased variance of mean_prob over experts (NaN if E = 1) */
+  float *cv2;        /* [1] squared coefficient of variation of counts: unbiased variance
+                        over experts / mean^2, in fp64 (NaN if E = 1 or no pairs);
+                        invest-in.ai "Common Usage Examples" (cv_squared of expert
+                        counts), matteuscruz "Load balancing" */
 } moe_stats;
 
 /* Workspace bytes that every entry point below accepts for this config

@@ -58,6 +58,8 @@ def _load():
             f.restype = C.c_int
         lib.orc_threads.argtypes = []
         lib.orc_threads.restype = C.c_int
+        lib.orc_cv2.argtypes = [P, C.c_int32]
+        lib.orc_cv2.restype = C.c_double
         _lib = lib
     return _lib
 
@@ -96,7 +98,15 @@ def route(shape, inp, *, with_probs: bool = True) -> dict:
     if rc != 0:
         raise ValueError("orc_route failed")
     r["balance"] = float(r["balance"][0])
+    r["cv2"] = cv2(r["counts"])
     return r
+
+
+def cv2(counts) -> float:
+    """Squared coefficient of variation of per-expert counts (unbiased variance / mean^2)."""
+    lib = _load()
+    c = np.ascontiguousarray(counts, dtype=np.int32)
+    return float(lib.orc_cv2(_p(c), C.c_int32(len(c))))
 
 
 def dispatch(shape, topk_idx: np.ndarray, keep: np.ndarray) -> dict:

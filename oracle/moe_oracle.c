@@ -344,3 +344,20 @@ int orc_expert_row(const orc_config *c, const void *x, const void *W1, const voi
 
 /* Threads the parallel loops above use. */
 int orc_threads(void) { return omp_get_max_threads(); }
+
+/*
+ * Squared coefficient of variation of the per-expert counts (invest-in.ai
+ * "Common Usage Examples": cv_squared of the expert counts; matteuscruz "Load
+ * balancing": the coefficient of variation of expert load): the unbiased
+ * variance over the E experts divided by the squared mean.  0/0 gives NaN when
+ * E = 1 or there are no pairs.
+ */
+double orc_cv2(const int32_t *counts, int32_t E) {
+  double mean = 0.0;
+  for (int32_t e = 0; e < E; ++e) mean += (double)counts[e];
+  mean /= (double)E;
+  double var = 0.0;
+  for (int32_t e = 0; e < E; ++e) var += ((double)counts[e] - mean) * ((double)counts[e] - mean);
+  var /= (double)(E - 1);
+  return var / (mean * mean);
+}

@@ -50,7 +50,7 @@ class moe_weights(C.Structure):
 
 class moe_stats(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("topk_idx", "topk_w", "counts", "kept",
-                                          "mean_prob", "balance")]
+                                          "mean_prob", "balance", "cv2")]
 
 
 _lib = None
@@ -173,6 +173,6 @@ def moe_forward(cfg, weights: dict, x, y, stats: Optional[dict] = None, ws=None,
     wp, wn = _ws(ws)
     w = _weights(weights)
     st = moe_stats(*[_ptr((stats or {}).get(n)) for n in
-                     ("topk_idx", "topk_w", "counts", "kept", "mean_prob", "balance")])
+                      ("topk_idx", "topk_w", "counts", "kept", "mean_prob", "balance", "cv2")])
     _check("moe_forward", library().moe_forward(
         C.byref(cfg), C.byref(w), _ptr(x), _ptr(y), C.byref(st), wp, wn, _stream(stream)))

@@ -101,4 +101,17 @@ __device__ inline void load_stats(const double* __restrict__ stat_part, int nb, 
   }
 }
 
+// Squared coefficient of variation of the per-expert counts: unbiased variance
+// over the E experts divided by the squared mean, in fp64 (integer counts make
+// the mean exact; 0/0 gives NaN for E = 1 or no pairs).  Thread e < E passes
+// counts[e].  Called by every thread of the block.
+__device__ inline void counts_cv2(int cnt, int E, float* __restrict__ cv2, double* wsd) {
+  const int e = threadIdx.x;
+  const double c = e < E ? static_cast<double>(cnt) : 0.0;
+  const double mean = block_sum_d(c, wsd) / static_cast<double>(E);
+  const double dv = e < E ? c - mean : 0.0;
+  const double var = block_sum_d(dv * dv, wsd) / static_cast<double>(E - 1);
+  if (e == 0) cv2[0] = static_cast<float>(var / (mean * mean));
+}
+
 }  // namespace moe

@@ -51,14 +51,15 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
 // offsets = exclusive scan of kept, offsets[E] = routed rows, offsets[E + 1] =
 // routed + shared rows.  With INLDS, base, skept and soff are LDS and base
 // (nb * E entries) is first filled with the histogram.  sh: 2 * kMaxExperts
-// ints of LDS.  Integer sums: exact in any order.  Ends with a barrier.
+// ints of LDS.  Integer sums: exact in any order.  Ends with a barrier and
+// returns counts[tid] to threads tid < E.
 template <bool INLDS>
-__device__ __forceinline__ void scan_hist(const int32_t* __restrict__ ghist, int nb, int E,
-                                          int64_t T, int capacity, int shared, int32_t* base,
-                                          int32_t* __restrict__ counts,
-                                          int32_t* __restrict__ kept,
-                                          int32_t* __restrict__ offsets, int32_t* skept,
-                                          int32_t* soff, int32_t* sh, int32_t* wsum) {
+__device__ __forceinline__ int scan_hist(const int32_t* __restrict__ ghist, int nb, int E,
+                                         int64_t T, int capacity, int shared, int32_t* base,
+                                         int32_t* __restrict__ counts,
+                                         int32_t* __restrict__ kept,
+                                         int32_t* __restrict__ offsets, int32_t* skept,
+                                         int32_t* soff, int32_t* sh, int32_t* wsum) {
   const int tid = threadIdx.x;
   if constexpr (INLDS) {
     // coalesced copy; all of a thread's loads are issued before the stores
@@ -107,10 +108,10 @@ __device__ __forceinline__ void scan_hist(const int32_t* __restrict__ ghist, int
       run += h;
     }
   }
-  int kp = 0;
+  int kp = 0, cnt = 0;
   if (tid < E) {
     const int s1 = tid + 1 < E ? sh[(tid + 1) * P] : total;
-    const int cnt = s1 - sh[tid * P];
+    cnt = s1 - sh[tid * P];
     kp = capacity < 0 ? cnt : min(cnt, capacity);
     counts[tid] = cnt;
     kept[tid] = kp;
@@ -132,16 +133,19 @@ __device__ __forceinline__ void scan_hist(const int32_t* __restrict__ ghist, int
     }
   }
   __syncthreads();
+  return cnt;  // counts[tid] for tid < E
 }
 
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     const int32_t* __restrict__ hist, int nb, int E, int64_t T, int capacity, int shared,
     int32_t* __restrict__ base, int32_t* __restrict__ counts, int32_t* __restrict__ kept,
-    int32_t* __restrict__ offsets) {
+    int32_t* __restrict__ offsets, float* __restrict__ cv2) {
   __shared__ int32_t sh[2 * kMaxExperts];
   __shared__ int32_t wsum[kMaxExperts / 64];
-  scan_hist<false>(hist, nb, E, T, capacity, shared, base, counts, kept, offsets, nullptr, nullptr,
-                   sh, wsum);
+  __shared__ double wsd[kMaxExperts / 64];
+  const int cnt = scan_hist<false>(hist, nb, E, T, capacity, shared, base, counts, kept, offsets,
+                                   nullptr, nullptr, sh, wsum);
+  if (cv2) counts_cv2(cnt, E, cv2, wsd);
 }
 
 // Expert ids (and, with topk_w set, gates) of the pairs of 64-token block b,
@@ -370,8 +374,9 @@ __global__ __launch_bounds__(1024) void dispatch_one_block_kernel(DispatchArgs a
   if (a.mean_prob || a.balance)
     load_stats(a.stat_part, nb, E, a.T, a.mean_prob, a.balance, wsd);
 
-  scan_hist<true>(a.hist, nb, E, a.T, a.capacity, a.shared, sbase, a.counts, a.kept, a.offsets,
-                  skept, soff, sh, wsum);
+  const int cnt = scan_hist<true>(a.hist, nb, E, a.T, a.capacity, a.shared, sbase, a.counts,
+                                  a.kept, a.offsets, skept, soff, sh, wsum);
+  if (a.cv2) counts_cv2(cnt, E, a.cv2, wsd);
   build_tile_list(soff, E + (a.shared ? 1 : 0), a.BM, a.tiles, a.ntiles, wsum);
 
   int nbits = 1;
@@ -419,10 +424,10 @@ hipError_t launch_dispatch_one_block(const DispatchArgs& a, hipStream_t st) {
 hipError_t launch_dispatch(int64_t T, int E, int k, int capacity, int shared, int nb,
                            const int32_t* topk_idx, bool need_hist, int32_t* hist, int32_t* base,
                            int32_t* counts, int32_t* kept, int32_t* offsets, int32_t* row_token,
-                           int32_t* row_slot, int32_t* inv, hipStream_t st) {
+                           int32_t* row_slot, int32_t* inv, float* cv2, hipStream_t st) {
   if (need_hist && nb > 0) dispatch_hist_kernel<<<nb, 256, 0, st>>>(topk_idx, T, k, E, hist);
   dispatch_scan_kernel<<<1, kMaxExperts, 0, st>>>(hist, nb, E, T, capacity, shared, base, counts,
-                                                  kept, offsets);
+                                                  kept, offsets, cv2);
   if (nb > 0) {
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;

@@ -74,7 +74,7 @@ struct DispatchArgs {
   float* row_gate;
   RowTile* tiles;
   int32_t* ntiles;
-  float *mean_prob, *balance;  // optional
+  float *mean_prob, *balance, *cv2;  // optional
 };
 
 // per-block bases of the single-block dispatch live in LDS: nb * E must fit
@@ -89,7 +89,7 @@ hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const flo
 hipError_t launch_dispatch(int64_t T, int E, int k, int capacity, int shared, int nb,
                            const int32_t* topk_idx, bool need_hist, int32_t* hist, int32_t* base,
                            int32_t* counts, int32_t* kept, int32_t* offsets, int32_t* row_token,
-                           int32_t* row_slot, int32_t* inv, hipStream_t st);
+                           int32_t* row_slot, int32_t* inv, float* cv2, hipStream_t st);
 
 hipError_t launch_dispatch_one_block(const DispatchArgs& a, hipStream_t st);
 

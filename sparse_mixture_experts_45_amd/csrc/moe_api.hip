@@ -229,7 +229,7 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t*
                                     cfg->shared_d_ff > 0, L.rp.nb, topk_idx, true,
                                     reinterpret_cast<int32_t*>(at(ws, L.hist)),
                                     reinterpret_cast<int32_t*>(at(ws, L.base)), counts, kept,
-                                    offsets, row_token, row_slot, inv,
+                                    offsets, row_token, row_slot, inv, nullptr,
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -317,12 +317,13 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     d.ntiles = reinterpret_cast<int32_t*>(at(ws, L.ntiles));
     d.mean_prob = o.mean_prob;
     d.balance = o.balance;
+    d.cv2 = o.cv2;
     if ((s = hip_status(launch_dispatch_one_block(d, st))) != MOE_OK) return s;
   } else if ((s = hip_status(launch_dispatch(cfg->T, cfg->n_experts, cfg->top_k, cfg->capacity,
                                              cfg->shared_d_ff > 0, L.rp.nb, topk_idx, false,
                                              hist, reinterpret_cast<int32_t*>(at(ws, L.base)),
                                              counts, kept, offsets, row_token, row_slot, inv,
-                                             st))) != MOE_OK) {
+                                             o.cv2, st))) != MOE_OK) {
     return s;
   }
   if (cfg->T == 0) return MOE_OK;

@@ -43,11 +43,13 @@ def gpu_forward(shape, dev, ws=None):
               counts=torch.empty(E, dtype=torch.int32, device="cuda"),
               kept=torch.empty(E, dtype=torch.int32, device="cuda"),
               mean_prob=torch.empty(E, dtype=torch.float32, device="cuda"),
-              balance=torch.empty(1, dtype=torch.float32, device="cuda"))
+              balance=torch.empty(1, dtype=torch.float32, device="cuda"),
+              cv2=torch.empty(1, dtype=torch.float32, device="cuda"))
     moe.moe_forward(c, dev, dev["x"], y, st, ws)
     torch.cuda.synchronize()
     out = {key: v.cpu().numpy() for key, v in st.items()}
     out["balance"] = float(out["balance"][0])
+    out["cv2"] = float(out["cv2"][0])
     out["y"] = y.float().cpu().numpy().astype(np.float64)
     out["y_raw"] = y
     return out
@@ -81,6 +83,7 @@ def check_routing(shape, g, ref):
     assert np.array_equal(g["kept"], ref["kept"])
     if shape.T == 0:
         assert np.all(np.isnan(g["mean_prob"]))
+        assert np.isnan(g["cv2"]) and np.isnan(ref["cv2"])   # no pairs: zero mean count
         return
     mp_ref = ref["mean_prob"]
     rel = np.abs(g["mean_prob"] - mp_ref) / np.abs(mp_ref)
@@ -90,6 +93,11 @@ def check_routing(shape, g, ref):
     else:
         b, br = g["balance"], ref["balance"]
         assert abs(b - br) <= max(BALANCE_ABS, BALANCE_REL * abs(br)), (b, br)
+    # cv^2 of the integer counts: fp64 on both sides, the GPU rounds once to fp32
+    if np.isnan(ref["cv2"]):
+        assert np.isnan(g["cv2"])
+    else:
+        assert abs(g["cv2"] - ref["cv2"]) <= 1e-6 * max(1.0, abs(ref["cv2"])), (g["cv2"], ref["cv2"])
 
 
 def device_inputs(inp):

@@ -331,6 +331,30 @@ def test_uniform_router_gives_zero_balance():
     assert np.all(r["topk_idx"] == [0, 1])
 
 
+@pytest.mark.parametrize("k,expect", [(1, 5.0), (2, 1.875)])
+def test_cv2_of_forced_routing(k, expect):
+    """All T tokens forced onto experts 0..k-1 of E = 5: counts are T on k experts and 0
+    elsewhere, so cv^2 = unbiased variance / mean^2 is E (k = 1) or 30/16 (k = 2) exactly."""
+    shape = small(T=25, E=5, k=k, router_bias="none")
+    inp = make_inputs(shape, 15, margin=0)
+    inp["bg"] = np.array([50.0, 40.0, 0.0, 0.0, 0.0], np.float32)
+    r = oracle.route(shape, inp)
+    assert r["counts"].tolist() == [shape.T] * k + [0] * (shape.E - k)
+    assert r["cv2"] == expect
+
+
+def test_cv2_is_zero_when_every_expert_is_chosen():
+    shape = small(T=13, E=4, k=4)
+    r = oracle.route(shape, make_inputs(shape, 21))
+    assert r["counts"].tolist() == [13] * 4 and r["cv2"] == 0.0
+
+
+def test_cv2_undefined_cases():
+    assert np.isnan(oracle.cv2([7]))          # one expert: no variance
+    assert np.isnan(oracle.cv2([0, 0, 0]))    # no pairs: zero mean
+    assert oracle.cv2([1, 2, 3]) == 0.25      # variance 1 (ddof 1), mean 2
+
+
 def test_one_token_statistics_by_hand():
     """T = 1: mean_prob is the token's softmax; balance its unbiased variance."""
     g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
