@@ -5,7 +5,8 @@ benchmark.  It only draws and stores numbers: it holds none of the layer's
 arithmetic.  The one calculation it does is the input-conditioning filter
 that redraws token rows whose top-(k+1) router scores sit closer together
 than a fixed margin, so that any correct fp32 evaluation of the router picks
-the same experts in the same slot order.
+the same experts in the same slot order (for expert-choice routing: token
+rows at a near-tie on some expert's top-C boundary of router probabilities).
 
 Workloads are the five layer shapes named after what they are:
 
@@ -18,6 +19,9 @@ Workloads are the five layer shapes named after what they are:
   capacity floor(1.25*T/E)=160, router bias = log of a Zipf(1.1) law
 * ``deepseek_e256_top8``  T=512,  d=7168, d_ff=2048,  E=256, k=8, GELU, bf16,
   plus one always-on shared expert with d_ff=2048
+* ``expert_choice_t8192_e64`` T=8192, d=1024, d_ff=4096, E=64, GELU, bf16,
+  expert-choice routing: each expert takes its top 256 tokens (k = 2 read as
+  the capacity factor)
 
 Distributions: x ~ N(0,1); router and expert weights ~ N(0, 1/fan_in)
 (std = fan_in**-0.5); biases ~ N(0, 0.01) read as variance 0.01 (std 0.1).
@@ -40,7 +44,8 @@ import numpy as np
 
 __all__ = [
     "LayerShape", "WORKLOADS", "WORKLOAD_ORDER", "workload", "make_inputs",
-    "f32_to_bf16_bits", "bf16_bits_to_f32", "random_rows", "MARGIN",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "random_rows", "MARGIN", "EC_MARGIN",
+    "ec_tokens_per_expert",
 ]
 
 MARGIN = 1e-3
@@ -50,6 +55,7 @@ _TAG_X, _TAG_X_REDRAW, _TAG_WG, _TAG_BG = 1, 2, 3, 4
 _TAG_W1, _TAG_B1, _TAG_W2, _TAG_B2 = 5, 6, 7, 8
 _TAG_WS1, _TAG_BS1, _TAG_WS2, _TAG_BS2 = 9, 10, 11, 12
 _TAG_ROWS = 13
+_TAG_X_REDRAW_EC = 14
 
 
 @dataclass(frozen=True)
@@ -67,6 +73,8 @@ class LayerShape:
     router_bias: str = "none"  # "none" | "normal" | "zipf1.1"
     renormalize: int = 1
     expert_bias: bool = True
+    routing: str = "token"     # "token": each token takes its top-k experts;
+                               # "expert": each expert takes its top-C tokens
 
     def with_(self, **kw) -> "LayerShape":
         return replace(self, **kw)
@@ -91,6 +99,10 @@ WORKLOADS = {
                                       router_bias="zipf1.1"),
     "deepseek_e256_top8": LayerShape("deepseek_e256_top8", T=512, d=7168, F=2048,
                                      E=256, k=8, Fs=2048),
+    # expert-choice routing on the Switch-style shape: each of the 64 experts
+    # takes its top floor(T*k/E) = 256 tokens (capacity factor k = 2)
+    "expert_choice_t8192_e64": LayerShape("expert_choice_t8192_e64", T=8192, d=1024,
+                                          F=4096, E=64, k=2, routing="expert"),
 }
 WORKLOAD_ORDER = ["tiny_f32", "page1_b4s512", "mixtral_t4096",
                   "switch_e64_top1_cap", "deepseek_e256_top8"]
@@ -173,6 +185,39 @@ def _margin_ok(xr64: np.ndarray, Wg64: np.ndarray, bg64, k: int, E: int, margin:
     return np.all(gaps >= margin, axis=1)
 
 
+def ec_tokens_per_expert(shape: LayerShape) -> int:
+    """Tokens each expert takes under expert-choice routing: the capacity when one
+    is given, else floor(T*k/E) (k read as the capacity factor); at most T."""
+    c = shape.capacity if shape.capacity >= 0 else (shape.T * shape.k) // shape.E
+    return min(c, shape.T)
+
+
+EC_MARGIN = 1e-6
+
+
+def _ec_boundary_ties(x64, Wg64, bg64, C: int, margin: float):
+    """Token rows at a near-tie on some expert's top-C boundary: for every expert,
+    the fp64 router probabilities of the C-th and (C+1)-th largest tokens closer
+    than `margin` (absolute; an fp32 evaluation is far more precise)."""
+    T = x64.shape[0]
+    if C <= 0 or C >= T:
+        return np.zeros(0, dtype=np.int64)
+    s = x64 @ Wg64.T
+    if bg64 is not None:
+        s = s + bg64
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    bad = set()
+    for e in range(p.shape[1]):
+        col = p[:, e]
+        order = np.argsort(-col, kind="stable")
+        a, b = order[C - 1], order[C]
+        if col[a] - col[b] < margin:
+            bad.update((int(a), int(b)))
+    return np.array(sorted(bad), dtype=np.int64)
+
+
 def make_inputs(shape: LayerShape, seed: int, *, margin: float = MARGIN,
                 threads: Optional[int] = None) -> dict:
     """Draw every input of one layer call.
@@ -204,7 +249,26 @@ def make_inputs(shape: LayerShape, seed: int, *, margin: float = MARGIN,
 
     x = _normal(seed, _TAG_X, 0, (s.T, s.d), 1.0, dt)
     redrawn = 0
-    if margin > 0 and s.T > 0:
+    if margin > 0 and s.T > 0 and s.routing == "expert":
+        # expert choice: redraw the token rows that sit at a near-tie on some
+        # expert's top-C boundary until no boundary is that close
+        Wg64 = Wg.astype(np.float64)
+        bg64 = None if bg is None else bg.astype(np.float64)
+        C = ec_tokens_per_expert(s)
+        attempt = np.zeros(s.T, dtype=np.int64)
+        for _ in range(1000):
+            bad = _ec_boundary_ties(_to_f64(x, dt), Wg64, bg64, C, EC_MARGIN)
+            if bad.size == 0:
+                break
+            for t in bad:
+                attempt[t] += 1
+                row = _rng(seed, _TAG_X_REDRAW_EC, t, attempt[t]).standard_normal(
+                    (s.d,), dtype=np.float32)
+                x[t] = f32_to_bf16_bits(row) if dt == "bf16" else row
+                redrawn += 1
+        else:  # pragma: no cover
+            raise RuntimeError("expert-choice margin filter did not settle")
+    elif margin > 0 and s.T > 0:
         Wg64 = Wg.astype(np.float64)
         bg64 = None if bg is None else bg.astype(np.float64)
         ok = _margin_ok(_to_f64(x, dt), Wg64, bg64, s.k, s.E, margin)

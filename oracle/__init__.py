@@ -60,6 +60,8 @@ def _load():
         lib.orc_threads.restype = C.c_int
         lib.orc_cv2.argtypes = [P, C.c_int32]
         lib.orc_cv2.restype = C.c_double
+        lib.orc_ec_select.argtypes = [C.POINTER(_Cfg), P, P, P, C.c_int64, P, P]
+        lib.orc_ec_select.restype = C.c_int
         _lib = lib
     return _lib
 
@@ -165,6 +167,45 @@ def forward(shape, inp, tokens=None) -> dict:
     rt = route(shape, inp)
     rt["y"] = experts(shape, inp, rt, tokens)
     return rt
+
+
+def ec_capacity(shape) -> int:
+    """Tokens each expert takes under expert-choice routing: the capacity when one is
+    set, else floor(T * k / E) (k read as the capacity factor); at most T."""
+    c = shape.capacity if shape.capacity >= 0 else (shape.T * shape.k) // shape.E
+    return min(c, shape.T)
+
+
+def ec_route(shape, inp) -> dict:
+    """Expert-choice routing: sel[T, E] (1 where expert e took token t), the fp64
+    router probabilities p[T, E], per-expert counts and the load statistics."""
+    lib = _load()
+    T, E = shape.T, shape.E
+    Ce = ec_capacity(shape)
+    r = dict(sel=np.zeros((T, E), np.int32), p=np.zeros((T, E), np.float64), C=Ce)
+    if lib.orc_ec_select(C.byref(_cfg(shape)), _p(inp["x"]), _p(inp["Wg"]), _p(inp["bg"]),
+                         Ce, _p(r["sel"]), _p(r["p"])) != 0:
+        raise ValueError("orc_ec_select failed")
+    r["counts"] = r["sel"].sum(axis=0).astype(np.int32)
+    r["kept"] = r["counts"].copy()
+    # load statistics of the same softmax (orc_route's definition)
+    st = route(shape, inp, with_probs=False)
+    r["mean_prob"], r["balance"] = st["mean_prob"], st["balance"]
+    r["cv2"] = cv2(r["counts"])
+    return r
+
+
+def ec_forward(shape, inp, tokens=None) -> dict:
+    """Expert-choice layer: y[t] = sum over the experts that took t, in expert order,
+    of p[t, e] E_e(x_t), plus the shared expert; for ``tokens`` (all if None)."""
+    r = ec_route(shape, inp)
+    E = shape.E
+    # the token's candidate slots are all E experts in order; untaken ones are
+    # masked off, so the sum runs over the taking experts in expert order
+    slots = dict(topk_idx=np.tile(np.arange(E, dtype=np.int32), (shape.T, 1)),
+                 topk_w=r["p"], keep=r["sel"])
+    r["y"] = experts(shape.with_(k=E), inp, slots, tokens)
+    return r
 
 
 def combine(shape, y_rows: np.ndarray, inv: np.ndarray, offsets: np.ndarray) -> np.ndarray:

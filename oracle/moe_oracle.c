@@ -38,6 +38,10 @@
  *                 balance = unbiased variance of mean_prob over experts
  *                 ("Load Balancing: The Hidden Challenge", moe_loss:
  *                 torch.std(...) ** 2)
+ *   expert choice each expert takes the C tokens of largest p_e, lower token
+ *                 index first among equals; a token's output is the sum over
+ *                 the experts that took it, in expert order, of p_e E_e(x)
+ *                 (matteuscruz "Load balancing", expert choice routing)
  *
  * Precision: everything is fp64 except one decision: the top-k selection is
  * taken on the scores rounded to fp32, the precision the GPU router decides in.
@@ -360,4 +364,72 @@ double orc_cv2(const int32_t *counts, int32_t E) {
   for (int32_t e = 0; e < E; ++e) var += ((double)counts[e] - mean) * ((double)counts[e] - mean);
   var /= (double)(E - 1);
   return var / (mean * mean);
+}
+
+/* one (key, token) pair of an expert's ranking */
+typedef struct {
+  float key;
+  int64_t t;
+} orc_rank;
+
+/* descending key, then ascending token */
+static int orc_rank_cmp(const void *a, const void *b) {
+  const orc_rank *x = (const orc_rank *)a, *y = (const orc_rank *)b;
+  if (x->key != y->key) return x->key > y->key ? -1 : 1;
+  return x->t < y->t ? -1 : (x->t > y->t ? 1 : 0);
+}
+
+/*
+ * Expert-choice routing (matteuscruz "Load balancing": each expert selects its
+ * top tokens instead of each token its top experts).  p[t*E + e] gets the fp64
+ * router probabilities (softmax over experts, as in orc_route); expert e takes
+ * the C tokens with the largest p[., e], the decision taken on p rounded to
+ * fp32 (the precision the GPU decides in), lower token index first among
+ * equals; sel[t*E + e] = 1 for the taken pairs, else 0.  C is clamped to [0, T].
+ * Returns 0, or -1 on bad arguments.
+ */
+int orc_ec_select(const orc_config *c, const void *x, const float *Wg, const float *bg,
+                  int64_t C, int32_t *sel, double *p) {
+  if (!c || c->E < 1 || c->d < 1 || c->T < 0 || C < 0) return -1;
+  const int64_t T = c->T;
+  const int32_t E = c->E;
+  if (C > T) C = T;
+#pragma omp parallel
+  {
+    double *l = (double *)malloc(sizeof(double) * E);
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      scores(c, x, Wg, bg, t, l);
+      double m = l[0];
+      for (int32_t e = 1; e < E; ++e) m = l[e] > m ? l[e] : m;
+      double z = 0.0;
+      for (int32_t e = 0; e < E; ++e) {
+        p[t * E + e] = exp(l[e] - m);
+        z += p[t * E + e];
+      }
+      for (int32_t e = 0; e < E; ++e) {
+        p[t * E + e] /= z;
+        sel[t * E + e] = 0;
+      }
+    }
+    free(l);
+  }
+  int bad = 0;
+#pragma omp parallel
+  {
+    orc_rank *r = (orc_rank *)malloc(sizeof(orc_rank) * (T > 0 ? T : 1));
+    if (!r) bad = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int32_t e = 0; e < E; ++e) {
+      if (!r) continue;
+      for (int64_t t = 0; t < T; ++t) {
+        r[t].key = (float)p[t * E + e];
+        r[t].t = t;
+      }
+      qsort(r, (size_t)T, sizeof(orc_rank), orc_rank_cmp);
+      for (int64_t i = 0; i < C; ++i) sel[r[i].t * E + e] = 1;
+    }
+    free(r);
+  }
+  return bad ? -1 : 0;
 }

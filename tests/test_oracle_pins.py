@@ -389,3 +389,76 @@ def test_gelu_and_relu_special_values():
     assert np.allclose(y, Fn.gelu(z).numpy(), rtol=0, atol=1e-15)
     yr = oracle.forward(shape.with_(act="relu"), inp)["y"][:, 0]
     assert yr.tolist() == [0.0, 1.0, 0.0, 3.5, 0.0]
+
+
+# ---------------------------------------------------------- expert choice
+def test_ec_each_expert_takes_exactly_C_tokens():
+    """Perfect load balance by construction: every expert takes min(C, T) tokens."""
+    for cap, expect in [(-1, (40 * 2) // 6), (5, 5), (100, 40), (0, 0)]:
+        shape = small(routing="expert", capacity=cap)
+        r = oracle.ec_route(shape, make_inputs(shape, 30))
+        assert r["C"] == expect
+        assert r["counts"].tolist() == [expect] * shape.E
+        if expect:
+            assert r["cv2"] == 0.0
+        else:
+            assert np.isnan(r["cv2"])
+
+
+def test_ec_uniform_probabilities_take_the_lowest_tokens():
+    """W_g = 0, no bias: every probability is 1/E, so each expert's top-C is the
+    first C tokens (lower token index first among equals)."""
+    shape = small(T=20, E=4, k=1, routing="expert", router_bias="none", capacity=6)
+    inp = make_inputs(shape, 31, margin=0)
+    inp["Wg"] = np.zeros_like(inp["Wg"])
+    r = oracle.ec_route(shape, inp)
+    assert np.all(r["p"] == 0.25)
+    assert np.all(r["sel"][:6] == 1) and np.all(r["sel"][6:] == 0)
+
+
+def test_ec_with_every_token_is_the_dense_soft_mixture():
+    """C = T: every expert takes every token, so y = sum_e p_e E_e(x), the layer that
+    token-choice routing gives with k = E and no renormalisation."""
+    shape = small(T=24, E=5, k=2, routing="expert", capacity=24, Fs=8)
+    inp = make_inputs(shape, 32, margin=0)
+    r = oracle.ec_forward(shape, inp)
+    assert np.all(r["sel"] == 1)
+    tc = oracle.forward(shape.with_(routing="token", k=shape.E, renormalize=0, capacity=-1), inp)
+    assert np.allclose(r["y"], tc["y"], rtol=1e-12, atol=1e-13)
+
+
+def test_ec_dense_masked_brute_force():
+    """numpy fp64: every expert on every token, masked to the pairs the experts took
+    and weighted by the router probability; the selection re-derived from a stable
+    sort of the fp32-rounded probabilities."""
+    shape = small(T=30, d=20, F=28, E=6, k=2, routing="expert", capacity=7)
+    inp = make_inputs(shape, 33)
+    r = oracle.ec_forward(shape, inp)
+    x = inp["x"].astype(np.float64)
+    s_ = x @ inp["Wg"].T.astype(np.float64) + inp["bg"].astype(np.float64)
+    p = np.exp(s_ - s_.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    assert np.allclose(r["p"], p, rtol=0, atol=1e-15)
+    for e in range(shape.E):
+        take = np.argsort(-p[:, e].astype(np.float32), kind="stable")[:7]
+        assert sorted(np.nonzero(r["sel"][:, e])[0].tolist()) == sorted(take.tolist())
+    gelu = np.vectorize(lambda z: 0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0))))
+    allout = np.stack([gelu(x @ inp["W1"][e].T.astype(np.float64) + inp["b1"][e])
+                       @ inp["W2"][e].T.astype(np.float64) + inp["b2"][e]
+                       for e in range(shape.E)], axis=1)          # [T, E, d]
+    y = np.einsum("te,ted->td", r["sel"] * p, allout)
+    assert np.allclose(r["y"], y, rtol=1e-12, atol=1e-12)
+    # a token nobody took gets exactly zero
+    none = np.nonzero(r["sel"].sum(axis=1) == 0)[0]
+    assert len(none) > 0 and np.all(r["y"][none] == 0.0)
+
+
+def test_ec_one_expert_is_the_plain_mlp():
+    """E = 1 and C = T: p = 1, so the layer is the textbook two-layer MLP."""
+    shape = small(T=9, E=1, k=1, routing="expert", capacity=9)
+    inp = make_inputs(shape, 34, margin=0)
+    r = oracle.ec_forward(shape, inp)
+    x = torch.from_numpy(inp["x"]).double()
+    ref = Fn.linear(Fn.gelu(Fn.linear(x, widen(inp["W1"][0], "f32"), widen(inp["b1"][0], "f32"))),
+                    widen(inp["W2"][0], "f32"), widen(inp["b2"][0], "f32"))
+    assert np.allclose(r["y"], ref.numpy(), rtol=1e-12, atol=1e-13)
