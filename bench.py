@@ -102,6 +102,51 @@ def stored_traffic(workload):
     return rec["traffic_bytes_per_call"]
 
 
+def layer_config(moe, torch, shape):
+    tdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    return moe.config(shape.T, shape.d, shape.F, shape.E, shape.k, act=shape.act, dtype=tdt,
+                      capacity=shape.capacity, renormalize=bool(shape.renormalize),
+                      shared_d_ff=shape.Fs, routing=shape.routing)
+
+
+def ffn_call(moe, torch, shape, dev, stream=None):
+    """Arguments of one moe_expert_ffn call over the rows this layer groups:
+    moe_route + moe_dispatch under token choice; under expert choice, the
+    selection moe_forward reports (ec_idx: E x C tokens, ascending per expert;
+    ec_w: their gates) as rows e*C + j, as moe_forward itself groups them."""
+    T, k, E = shape.T, shape.k, shape.E
+    i32 = dict(dtype=torch.int32, device="cuda")
+    cfg = layer_config(moe, torch, shape)
+    ws = moe.workspace(cfg)
+    if shape.routing == "expert":
+        C = min(shape.capacity if shape.capacity >= 0 else T * k // E, T)
+        y = torch.empty((T, shape.d), dtype=dev["x"].dtype, device="cuda")
+        ec_idx = torch.empty((E, C), **i32)
+        ec_w = torch.empty((E, C), dtype=torch.float32, device="cuda")
+        moe.moe_forward(cfg, dev, dev["x"], y, dict(ec_idx=ec_idx, ec_w=ec_w), ws, stream=stream)
+        nrows = E * C + (T if shape.Fs else 0)
+        row_token = torch.empty(nrows, **i32)
+        row_token[:E * C] = ec_idx.view(-1)
+        if shape.Fs:
+            row_token[E * C:] = torch.arange(T, **i32)
+        offsets = torch.arange(E + 2, **i32) * C
+        offsets[E + 1] = nrows
+        row_slot, topk_w = None, ec_w.view(-1)
+    else:
+        nrows = T * k + (T if shape.Fs else 0)
+        topk_idx, inv = torch.empty((T, k), **i32), torch.empty((T, k), **i32)
+        topk_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        counts, kept = torch.empty(E, **i32), torch.empty(E, **i32)
+        offsets = torch.empty(E + 2, **i32)
+        row_token, row_slot = torch.empty(nrows, **i32), torch.empty(nrows, **i32)
+        moe.moe_route(cfg, dev["x"], dev["Wg"], dev["bg"], topk_idx, topk_w, None, None, None,
+                      ws, stream=stream)
+        moe.moe_dispatch(cfg, topk_idx, counts, kept, offsets, row_token, row_slot, inv, ws,
+                         stream=stream)
+    y_rows = torch.empty((max(nrows, 1), shape.d), dtype=torch.float32, device="cuda")
+    return (cfg, dev["x"], dev, offsets, row_token, row_slot, topk_w, y_rows, ws)
+
+
 def traffic_probe(args):
     import torch
     import sparse_mixture_experts_45_amd as moe
@@ -115,23 +160,9 @@ def traffic_probe(args):
     del a, b
     shape = workload(args.workload)
     dev = to_device(make_inputs(shape, args.seed), "cuda")
-    tdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
-    cfg = moe.config(shape.T, shape.d, shape.F, shape.E, shape.k, act=shape.act, dtype=tdt,
-                     capacity=shape.capacity, renormalize=bool(shape.renormalize),
-                     shared_d_ff=shape.Fs)
-    ws = moe.workspace(cfg)
-    T, k, E = shape.T, shape.k, shape.E
-    nrows = T * k + (T if shape.Fs else 0)
-    i32 = dict(dtype=torch.int32, device="cuda")
-    topk_idx, inv = torch.empty((T, k), **i32), torch.empty((T, k), **i32)
-    topk_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    counts, kept, offsets = torch.empty(E, **i32), torch.empty(E, **i32), torch.empty(E + 2, **i32)
-    row_token, row_slot = torch.empty(nrows, **i32), torch.empty(nrows, **i32)
-    y_rows = torch.empty((nrows, shape.d), dtype=torch.float32, device="cuda")
-    moe.moe_route(cfg, dev["x"], dev["Wg"], dev["bg"], topk_idx, topk_w, None, None, None, ws)
-    moe.moe_dispatch(cfg, topk_idx, counts, kept, offsets, row_token, row_slot, inv, ws)
+    fargs = ffn_call(moe, torch, shape, dev)
     for _ in range(5):
-        moe.moe_expert_ffn(cfg, dev["x"], dev, offsets, row_token, row_slot, topk_w, y_rows, ws)
+        moe.moe_expert_ffn(*fargs)
     torch.cuda.synchronize()
     print("traffic probe done:", shape.name, flush=True)
 
@@ -227,12 +258,17 @@ def cpu_baseline(shape, inp, seconds):
     the batch when one pass is shorter than `seconds`, until about `seconds` of work."""
     import oracle
     t0 = time.perf_counter()
-    rt = oracle.route(shape, inp, with_probs=False)
+    if shape.routing == "expert":
+        sel = oracle.ec_route(shape, inp)
+        experts = lambda toks: oracle.ec_experts(shape, inp, sel, toks)  # noqa: E731
+    else:
+        rt = oracle.route(shape, inp, with_probs=False)
+        experts = lambda toks: oracle.experts(shape, inp, rt, toks)  # noqa: E731
     t_route = time.perf_counter() - t0
     # calibrate on a few tokens, then size the sample to ~`seconds`
     n0 = min(shape.T, 8)
     t1 = time.perf_counter()
-    oracle.experts(shape, inp, rt, np.arange(n0))
+    experts(np.arange(n0))
     per_tok = (time.perf_counter() - t1) / max(n0, 1)
     per_tok_all = per_tok + t_route / max(shape.T, 1)
     # one pass over the whole batch when it fits the budget, else the prefix that does;
@@ -242,7 +278,7 @@ def cpu_baseline(shape, inp, seconds):
     while True:
         toks = np.arange(chunk)
         t2 = time.perf_counter()
-        oracle.experts(shape, inp, rt, toks)
+        experts(toks)
         t_exp += time.perf_counter() - t2
         done += chunk
         if chunk < shape.T or t_exp + t_route * done / max(shape.T, 1) >= seconds:
@@ -283,9 +319,7 @@ def main():
     inp = make_inputs(shape, args.seed)
     dev = to_device(inp, "cuda")
     tdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
-    cfg = moe.config(shape.T, shape.d, shape.F, shape.E, shape.k, act=shape.act, dtype=tdt,
-                     capacity=shape.capacity, renormalize=bool(shape.renormalize),
-                     shared_d_ff=shape.Fs)
+    cfg = layer_config(moe, torch, shape)
     ws = moe.workspace(cfg)
     T, k, E = shape.T, shape.k, shape.E
     x = dev["x"]
@@ -331,24 +365,10 @@ def main():
     hit = int((kept > 0).sum())
 
     # ---- expert grouped GEMM (one moe_expert_ffn call) timed with HIP events
-    topk_idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    topk_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    nrows = T * k + (T if shape.Fs else 0)
-    counts = torch.empty(E, dtype=torch.int32, device="cuda")
-    kept_t = torch.empty(E, dtype=torch.int32, device="cuda")
-    offsets = torch.empty(E + 2, dtype=torch.int32, device="cuda")
-    row_token = torch.empty(nrows, dtype=torch.int32, device="cuda")
-    row_slot = torch.empty(nrows, dtype=torch.int32, device="cuda")
-    inv = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    y_rows = torch.empty((nrows, shape.d), dtype=torch.float32, device="cuda")
     with torch.cuda.stream(stream):
-        moe.moe_route(cfg, x, dev["Wg"], dev["bg"], topk_idx, topk_w, None, None, None, ws,
-                      stream=stream)
-        moe.moe_dispatch(cfg, topk_idx, counts, kept_t, offsets, row_token, row_slot, inv, ws,
-                         stream=stream)
+        fargs = ffn_call(moe, torch, shape, dev, stream=stream)
         for _ in range(3):
-            moe.moe_expert_ffn(cfg, x, dev, offsets, row_token, row_slot, topk_w, y_rows, ws,
-                               stream=stream)
+            moe.moe_expert_ffn(*fargs, stream=stream)
     torch.cuda.synchronize()
     # one moe_expert_ffn call (tile list, up GEMM, down GEMM) replayed from a
     # graph, so the events bracket the three kernels without host launch gaps
@@ -356,8 +376,7 @@ def main():
     if args.graph:
         ffn_graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(ffn_graph, stream=stream):
-            moe.moe_expert_ffn(cfg, x, dev, offsets, row_token, row_slot, topk_w, y_rows, ws,
-                               stream=stream)
+            moe.moe_expert_ffn(*fargs, stream=stream)
         torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
@@ -367,8 +386,7 @@ def main():
             if ffn_graph is not None:
                 ffn_graph.replay()
             else:
-                moe.moe_expert_ffn(cfg, x, dev, offsets, row_token, row_slot, topk_w, y_rows,
-                                   ws, stream=stream)
+                moe.moe_expert_ffn(*fargs, stream=stream)
             b.record(stream)
     torch.cuda.synchronize()
     ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
@@ -400,7 +418,8 @@ def main():
         "data": "synthetic (seeded; random-init weights)",
         "config": {"workload": shape.name, "tokens": T, "d_model": shape.d, "d_ff": shape.F,
                    "n_experts": E, "top_k": k, "capacity": shape.capacity,
-                   "shared_d_ff": shape.Fs, "act": shape.act, "hip_graph": bool(graph),
+                   "shared_d_ff": shape.Fs, "act": shape.act, "routing": shape.routing,
+                   "hip_graph": bool(graph),
                    "kept_rows": kept_rows, "experts_hit": hit},
         "layer_tflops": round(flop / (ms_per_step * 1e-3) / 1e12, 2),
         "roofline": roof,

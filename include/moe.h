@@ -36,8 +36,12 @@
  *    moe_workspace_bytes(cfg) bytes (one size serves every entry point).  Its
  *    contents need no initialisation and are garbage after the call.
  *  - Limits: 1 <= n_experts <= 1024, 1 <= top_k <= min(n_experts, 32),
- *    d_model, d_ff and shared_d_ff multiples of 8, T * (top_k + 1) < 2^31,
- *    x / weight / y pointers 16-byte aligned.
+ *    d_model, d_ff and shared_d_ff multiples of 8, T * (top_k + 1) < 2^31
+ *    (under MOE_ROUTE_EXPERT: E * C + T < 2^31), x / weight / y pointers
+ *    16-byte aligned.
+ *  - moe_route, moe_dispatch and moe_combine take token-choice configs only
+ *    (MOE_ERR_UNSUPPORTED under MOE_ROUTE_EXPERT); moe_expert_ffn and
+ *    moe_forward take both.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -60,6 +64,20 @@ typedef enum {
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 enum { MOE_ACT_GELU = 0 /* 0.5 z (1 + erf(z / sqrt 2)) */, MOE_ACT_RELU = 1 };
 
+/*
+ * Routing direction.
+ *  MOE_ROUTE_TOKEN: each token takes its top-k experts (the layer above).
+ *  MOE_ROUTE_EXPERT: expert-choice routing (matteuscruz "Mixture of Experts",
+ *    "Load balancing", expert choice routing): each expert takes the C tokens
+ *    with the highest router probability p[t, e], C = capacity when
+ *    capacity >= 0, else floor(T * top_k / E) (top_k read as the capacity
+ *    factor), at most T; among equal fp32 probabilities the lower token index
+ *    wins.  y[t] = sum over the experts that took t, in ascending expert order,
+ *    of p[t, e] E_e(x_t) (+ S(x_t)); renormalize is ignored.  A token may be
+ *    taken by any number of experts, including none.
+ */
+enum { MOE_ROUTE_TOKEN = 0, MOE_ROUTE_EXPERT = 1 };
+
 typedef struct {
   int64_t T;           /* tokens (batch * seq_len, flattened) */
   int32_t d_model;     /* d */
@@ -71,6 +89,7 @@ typedef struct {
   int32_t capacity;    /* < 0: unlimited; else max kept rows per routed expert */
   int32_t renormalize; /* 1: g_i = p_i / sum p over the top-k; 0: g_i = p_i */
   int32_t shared_d_ff; /* hidden size of the always-on shared expert, 0 = none */
+  int32_t routing;     /* MOE_ROUTE_TOKEN or MOE_ROUTE_EXPERT */
 } moe_config;
 
 typedef struct {
@@ -81,16 +100,22 @@ typedef struct {
 
 /* Optional per-call outputs of moe_forward; every member may be NULL. */
 typedef struct {
-  int32_t *topk_idx; /* [T, k] chosen experts */
-  float *topk_w;     /* [T, k] gates */
-  int32_t *counts;   /* [E] routed (token, slot) pairs per expert */
-  int32_t *kept;     /* [E] pairs that survived the capacity limit */
+  int32_t *topk_idx; /* [T, k] chosen experts; must be NULL under MOE_ROUTE_EXPERT */
+  float *topk_w;     /* [T, k] gates; must be NULL under MOE_ROUTE_EXPERT */
+  int32_t *counts;   /* [E] routed (token, slot) pairs per expert (C each under
+                        MOE_ROUTE_EXPERT) */
+  int32_t *kept;     /* [E] pairs that survived the capacity limit (C each under
+                        MOE_ROUTE_EXPERT) */
   float *mean_prob;  /* [E] mean router probability over tokens (NaN if T = 0) */
   float *balance;    /* [1] unbiased variance of mean_prob over experts (NaN if E = 1) */
   float *cv2;        /* [1] squared coefficient of variation of counts: unbiased variance
                         over experts / mean^2, in fp64 (NaN if E = 1 or no pairs);
                         invest-in.ai "Common Usage Examples" (cv_squared of expert
                         counts), matteuscruz "Load balancing" */
+  int32_t *ec_idx;   /* [E, C] under MOE_ROUTE_EXPERT: the tokens expert e took, ascending;
+                        must be NULL under MOE_ROUTE_TOKEN */
+  float *ec_w;       /* [E, C] under MOE_ROUTE_EXPERT: their gates p[t, e] (fp32);
+                        must be NULL under MOE_ROUTE_TOKEN */
 } moe_stats;
 
 /* Workspace bytes that every entry point below accepts for this config
@@ -139,6 +164,11 @@ moe_status moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, int32_t 
  *   x [T, d]; offsets, row_token, row_slot as produced by moe_dispatch;
  *   topk_w [T, k] fp32; y_rows [T*k + (shared_d_ff ? T : 0), d] fp32 out (only
  *   the first offsets[E+1] rows are written).
+ * Under MOE_ROUTE_EXPERT the routed rows are moe_forward's selection: row
+ * e*C + j is token ec_idx[e, j] with gate_r = topk_w[r] = ec_w[e, j]
+ * (topk_w [E*C] fp32), offsets[e] = e*C, offsets[E] = E*C, offsets[E+1] =
+ * E*C (+ T with a shared expert, whose rows E*C + t are token t); row_slot is
+ * not read (may be NULL); y_rows has E*C (+ T) rows.
  */
 moe_status moe_expert_ffn(const moe_config *cfg, const void *x, const moe_weights *w,
                           const int32_t *offsets, const int32_t *row_token,
@@ -157,7 +187,9 @@ moe_status moe_combine(const moe_config *cfg, const float *y_rows, const int32_t
 
 /*
  * The whole layer: route, dispatch, expert MLPs, combine.  y [T, d] out in
- * cfg->dtype; stats may be NULL or have NULL members.
+ * cfg->dtype; stats may be NULL or have NULL members (topk_idx and topk_w must
+ * be NULL under MOE_ROUTE_EXPERT, ec_idx and ec_w under MOE_ROUTE_TOKEN, else
+ * MOE_ERR_INVALID_ARG).
  */
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
                        moe_stats *stats, void *ws, size_t ws_bytes, void *stream);

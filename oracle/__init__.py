@@ -195,16 +195,22 @@ def ec_route(shape, inp) -> dict:
     return r
 
 
-def ec_forward(shape, inp, tokens=None) -> dict:
-    """Expert-choice layer: y[t] = sum over the experts that took t, in expert order,
-    of p[t, e] E_e(x_t), plus the shared expert; for ``tokens`` (all if None)."""
-    r = ec_route(shape, inp)
+def ec_experts(shape, inp, r: dict, tokens=None) -> np.ndarray:
+    """Expert-choice outputs from a selection ``r`` (ec_route's): y[t] = sum over the
+    experts that took t, in expert order, of p[t, e] E_e(x_t), plus the shared
+    expert; for ``tokens`` (all if None)."""
     E = shape.E
     # the token's candidate slots are all E experts in order; untaken ones are
     # masked off, so the sum runs over the taking experts in expert order
     slots = dict(topk_idx=np.tile(np.arange(E, dtype=np.int32), (shape.T, 1)),
                  topk_w=r["p"], keep=r["sel"])
-    r["y"] = experts(shape.with_(k=E), inp, slots, tokens)
+    return experts(shape.with_(k=E), inp, slots, tokens)
+
+
+def ec_forward(shape, inp, tokens=None) -> dict:
+    """Expert-choice layer: selection, statistics and outputs for ``tokens``."""
+    r = ec_route(shape, inp)
+    r["y"] = ec_experts(shape, inp, r, tokens)
     return r
 
 

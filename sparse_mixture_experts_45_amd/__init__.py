@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "MOE_F32", "MOE_BF16", "MOE_ACT_GELU", "MOE_ACT_RELU", "MoeError", "moe_config",
+    "MOE_F32", "MOE_BF16", "MOE_ACT_GELU", "MOE_ACT_RELU", "MOE_ROUTE_TOKEN",
+    "MOE_ROUTE_EXPERT", "MoeError", "moe_config",
     "moe_weights", "moe_stats", "config", "library", "moe_workspace_bytes", "moe_route",
     "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_status_string",
     "workspace", "LIB_PATH",
@@ -25,6 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_GELU, MOE_ACT_RELU = 0, 1
+MOE_ROUTE_TOKEN, MOE_ROUTE_EXPERT = 0, 1
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 
@@ -40,7 +42,7 @@ class moe_config(C.Structure):
     _fields_ = [("T", C.c_int64), ("d_model", C.c_int32), ("d_ff", C.c_int32),
                 ("n_experts", C.c_int32), ("top_k", C.c_int32), ("act", C.c_int32),
                 ("dtype", C.c_int32), ("capacity", C.c_int32), ("renormalize", C.c_int32),
-                ("shared_d_ff", C.c_int32)]
+                ("shared_d_ff", C.c_int32), ("routing", C.c_int32)]
 
 
 class moe_weights(C.Structure):
@@ -50,7 +52,8 @@ class moe_weights(C.Structure):
 
 class moe_stats(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("topk_idx", "topk_w", "counts", "kept",
-                                          "mean_prob", "balance", "cv2")]
+                                          "mean_prob", "balance", "cv2", "ec_idx",
+                                          "ec_w")]
 
 
 _lib = None
@@ -88,11 +91,12 @@ def moe_status_string(status: int) -> str:
 
 def config(T: int, d_model: int, d_ff: int, n_experts: int, top_k: int, *, act: str = "gelu",
            dtype=torch.bfloat16, capacity: int = -1, renormalize: bool = True,
-           shared_d_ff: int = 0) -> moe_config:
+           shared_d_ff: int = 0, routing: str = "token") -> moe_config:
     dt = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}[dtype]
     a = {"gelu": MOE_ACT_GELU, "relu": MOE_ACT_RELU}[act]
+    r = {"token": MOE_ROUTE_TOKEN, "expert": MOE_ROUTE_EXPERT}[routing]
     return moe_config(int(T), int(d_model), int(d_ff), int(n_experts), int(top_k), a, dt,
-                      int(capacity), int(bool(renormalize)), int(shared_d_ff))
+                      int(capacity), int(bool(renormalize)), int(shared_d_ff), r)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -173,6 +177,7 @@ def moe_forward(cfg, weights: dict, x, y, stats: Optional[dict] = None, ws=None,
     wp, wn = _ws(ws)
     w = _weights(weights)
     st = moe_stats(*[_ptr((stats or {}).get(n)) for n in
-                      ("topk_idx", "topk_w", "counts", "kept", "mean_prob", "balance", "cv2")])
+                      ("topk_idx", "topk_w", "counts", "kept", "mean_prob", "balance", "cv2",
+                       "ec_idx", "ec_w")])
     _check("moe_forward", library().moe_forward(
         C.byref(cfg), C.byref(w), _ptr(x), _ptr(y), C.byref(st), wp, wn, _stream(stream)))

@@ -9,20 +9,6 @@
 
 namespace moe {
 
-template <typename T>
-__device__ __forceinline__ void store4(T* p, float4 v);
-template <>
-__device__ __forceinline__ void store4<float>(float* p, float4 v) {
-  *reinterpret_cast<float4*>(p) = v;
-}
-template <>
-__device__ __forceinline__ void store4<bf16>(bf16* p, float4 v) {
-  uint2 u;
-  u.x = static_cast<uint32_t>(f32_to_bf16(v.x)) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
-  u.y = static_cast<uint32_t>(f32_to_bf16(v.z)) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
-  *reinterpret_cast<uint2*>(p) = u;
-}
-
 // One thread per 4 columns of one token; the grid is (T, ceil(d / 1024)) so a
 // wide row is spread over several blocks.  The token's row indices are uniform
 // over the block; all k (+1) row loads are issued before the additions, which

@@ -88,10 +88,7 @@ struct GemmArgs {
   const void* A;         // up: x [T, K]; down: H [rows, lda]
   int64_t lda;
   const int32_t* row_token;
-  const int32_t* row_slot;
-  const float* topk_w;
   const float* row_gate;  // gate of each row (1 for shared rows), built with the tile list
-  int k;
   const void* W;         // routed weights [E, N, K]
   const void* Wsh;       // shared weights [Ns, Ks]
   const void* bias;      // routed [E, N] or NULL
@@ -163,12 +160,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
 
   if (!UP) {
     for (int m = tid; m < BM; m += NT) {
-      float gv = 0.f;
-      if (m < rows) {
-        const int r = row0 + m;
-        gv = sh ? 1.0f : a.topk_w[static_cast<int64_t>(a.row_token[r]) * a.k + a.row_slot[r]];
-      }
-      gate_s[m] = gv;
+      gate_s[m] = m < rows ? a.row_gate[row0 + m] : 0.f;
     }
   }
 
@@ -602,7 +594,9 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
   }
 }
 
-// Row tiles of BM rows per group, groups in order, from the dispatch offsets.
+// Row tiles of BM rows per group, groups in order, from the dispatch offsets,
+// and each row's gate: topk_w[token, slot] (k > 0) or topk_w[row] (k = 0,
+// one gate per routed row); 1 for the shared expert's rows.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            int G, int BM, int E, int k,
                                                            const int32_t* __restrict__ row_token,
@@ -614,10 +608,11 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   __shared__ int32_t wsum[kMaxExperts / 64];
   build_tile_list(offsets, G, BM, tiles, ntiles, wsum);
   const int g = threadIdx.x;
-  // gate of every row: topk_w of its (token, slot); 1 for the shared expert's rows
   const int routed = offsets[E], nrows = offsets[G];
   for (int r = g; r < nrows; r += kMaxExperts)
-    row_gate[r] = r < routed ? topk_w[static_cast<int64_t>(row_token[r]) * k + row_slot[r]] : 1.0f;
+    row_gate[r] = r >= routed ? 1.0f
+                  : k > 0     ? topk_w[static_cast<int64_t>(row_token[r]) * k + row_slot[r]]
+                              : topk_w[r];
 }
 
 static GemmArgs up_args(const FfnArgs& f, int BN) {
@@ -629,10 +624,7 @@ static GemmArgs up_args(const FfnArgs& f, int BN) {
   u.A = f.x;
   u.lda = f.d;
   u.row_token = f.row_token;
-  u.row_slot = f.row_slot;
-  u.topk_w = f.topk_w;
   u.row_gate = f.row_gate;
-  u.k = f.k;
   u.W = f.W1;
   u.Wsh = f.Ws1;
   u.bias = f.b1;
@@ -722,7 +714,8 @@ static void run_dma(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
 hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const int G = f.E + (f.Fs > 0 ? 1 : 0);
   if (!f.tiles_ready)
-    build_tiles_kernel<<<1, kMaxExperts, 0, st>>>(f.offsets, G, gp.BM, f.E, f.k, f.row_token,
+    build_tiles_kernel<<<1, kMaxExperts, 0, st>>>(f.offsets, G, gp.BM, f.E,
+                                                  f.row_gates ? 0 : f.k, f.row_token,
                                                   f.row_slot, f.topk_w, f.tiles, f.ntiles,
                                                   f.row_gate);
   switch (gp.shape) {

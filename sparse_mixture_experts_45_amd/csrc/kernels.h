@@ -13,6 +13,7 @@ struct RoutePlan {
   int S, kchunk;  // router score split over d: S chunks of kchunk columns
   int lpt, vpl;   // gate: lanes per token (16 or 64), values per lane
   int fused;      // scores and gate in one kernel (bf16, E <= 64, S = 1)
+  int64_t ps_t, ps_e;  // element strides of the optional probabilities output
   int nb;         // gate blocks = ceil(T / kGateTokens)
 };
 
@@ -60,6 +61,7 @@ struct FfnArgs {
   int32_t* ntiles;   // [1]
   float* row_gate;   // [rows_max]
   int tiles_ready;   // tiles, ntiles and row_gate already written by the dispatch
+  int row_gates;     // topk_w holds one gate per routed row (expert choice)
 };
 
 // Everything the single-block dispatch reads and writes.
@@ -92,6 +94,27 @@ hipError_t launch_dispatch(int64_t T, int E, int k, int capacity, int shared, in
                            int32_t* row_slot, int32_t* inv, float* cv2, hipStream_t st);
 
 hipError_t launch_dispatch_one_block(const DispatchArgs& a, hipStream_t st);
+
+// Everything the expert-choice selection and its finishing block read and write.
+struct EcArgs {
+  int64_t T;
+  int E, Ce, W, shared, BM, nb;  // Ce tokens per expert; W = ceil(T / 32) bitmap words
+  int32_t *row_token, *offsets, *counts, *kept;  // counts, kept optional
+  float* row_gate;
+  uint32_t* sel;   // [E, W] selection bitmap
+  int32_t* pre;    // [E, W] taken tokens before each word
+  RowTile* tiles;
+  int32_t* ntiles;
+  const double* stat_part;     // [nb, E] gate-block probability sums
+  float *mean_prob, *balance, *cv2;  // optional
+  int32_t* ec_idx;  // optional [E, Ce] copy of row_token's routed rows
+  float* ec_w;      // optional [E, Ce] copy of their gates
+};
+
+hipError_t launch_expert_choice(const EcArgs& a, const float* probsT, hipStream_t st);
+hipError_t launch_combine_ec(int64_t T, int d, int E, int Ce, int shared, int dtype,
+                             const float* y_rows, const uint32_t* sel, const int32_t* pre,
+                             void* y, hipStream_t st);
 
 hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& a, hipStream_t st);
 

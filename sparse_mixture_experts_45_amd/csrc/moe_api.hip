@@ -11,10 +11,28 @@ namespace {
 struct Layout {
   RoutePlan rp;
   GemmPlan gp;
-  int64_t rows_max;  // T*k + (Fs ? T : 0)
+  int64_t rows_max;  // routed rows (T*k, or E*C under expert choice) + (Fs ? T : 0)
+  int64_t ec_C;      // tokens per expert under expert choice
+  int ec_W;          // 32-token words of the expert-choice bitmaps
   size_t part, stat, hist, base, topk_idx, topk_w, counts, kept, offsets, row_token, row_slot,
-      inv, tiles, ntiles, row_gate, H, y_rows, total;
+      inv, tiles, ntiles, row_gate, probsT, sel, pre, H, y_rows, total;
 };
+
+bool expert_choice(const moe_config* c) { return c->routing == MOE_ROUTE_EXPERT; }
+
+// Tokens each expert takes under expert choice: the capacity if set, else
+// floor(T * k / E); at most T.
+int64_t ec_capacity(const moe_config* c) {
+  const int64_t C = c->capacity >= 0 ? c->capacity : c->T * c->top_k / c->n_experts;
+  return std::min<int64_t>(C, c->T);
+}
+
+// Routed (expert, token) rows the expert MLPs can receive.
+int64_t routed_rows_max(const moe_config* c) {
+  if (expert_choice(c)) return int64_t(c->n_experts) * ec_capacity(c);
+  const int64_t pairs = c->T * c->top_k;
+  return c->capacity >= 0 ? std::min<int64_t>(pairs, int64_t(c->n_experts) * c->capacity) : pairs;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -27,8 +45,14 @@ moe_status check_config(const moe_config* c) {
   if (c->act != MOE_ACT_GELU && c->act != MOE_ACT_RELU) return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (c->routing != MOE_ROUTE_TOKEN && c->routing != MOE_ROUTE_EXPERT) return MOE_ERR_INVALID_ARG;
   if (c->top_k > c->n_experts) return MOE_ERR_INVALID_ARG;
   if (c->n_experts + (c->shared_d_ff > 0 ? 1 : 0) > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (expert_choice(c)) {
+    // the gate runs with k = 1; k only sets the default C
+    if (c->n_experts * ec_capacity(c) + c->T >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+  }
   if (c->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
   if (c->T * (c->top_k + 1) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -36,15 +60,17 @@ moe_status check_config(const moe_config* c) {
 
 GemmPlan gemm_plan(const moe_config* c) {
   GemmPlan g{};
-  const int64_t pairs = c->T * c->top_k;
-  const int64_t rmax = c->capacity >= 0 ? std::min<int64_t>(pairs, int64_t(c->n_experts) * c->capacity)
-                                        : pairs;
+  const int64_t rmax = routed_rows_max(c);
   const int64_t avg = rmax / c->n_experts;
   const bool k64 = c->d_model % 64 == 0 && c->d_ff % 64 == 0 && c->shared_d_ff % 64 == 0;
+  // expert choice gives every expert exactly C rows: whole 256-row tiles pay
+  // when their padding is at most 1/8 of the rows
+  const int64_t C = expert_choice(c) ? ec_capacity(c) : 0;
+  const bool ec_whole = C >= 256 && (ceil_div(C, 256) * 256 - C) * 8 <= C;
   if (c->dtype == MOE_F32) {
     g.shape = kGemmF32;
     g.BM = 64;
-  } else if (k64 && avg >= 768) {
+  } else if (k64 && (avg >= 768 || ec_whole)) {
     g.shape = kGemmDmaLarge;
     g.BM = kDmaLarge.BM;
   } else if (k64 && avg >= 256) {
@@ -77,9 +103,16 @@ RoutePlan route_plan(const moe_config* c) {
   p.T = c->T;
   p.d = c->d_model;
   p.E = c->n_experts;
-  p.k = c->top_k;
-  p.renorm = c->renormalize;
+  p.k = expert_choice(c) ? 1 : c->top_k;
+  p.renorm = expert_choice(c) ? 0 : c->renormalize;
   p.nb = static_cast<int>(ceil_div(c->T, kGateTokens));
+  if (expert_choice(c)) {  // probabilities [E, T]: one expert's are contiguous
+    p.ps_t = 1;
+    p.ps_e = c->T;
+  } else {  // [T, E] row-major
+    p.ps_t = c->n_experts;
+    p.ps_e = 1;
+  }
   // Split d so the score kernel has >= ~256 blocks, each K slice of a block
   // keeping >= 2 K steps.  bf16 layers whose experts fit one score tile
   // (E <= 64) and that gain nothing from a split run the gate inside the score
@@ -106,8 +139,11 @@ Layout layout(const moe_config* c) {
   Layout L{};
   L.rp = route_plan(c);
   L.gp = gemm_plan(c);
-  const int64_t T = c->T, E = c->n_experts, k = c->top_k;
-  L.rows_max = T * k + (c->shared_d_ff > 0 ? T : 0);
+  const int64_t T = c->T, E = c->n_experts, k = L.rp.k;
+  const bool ec = expert_choice(c);
+  L.ec_C = ec ? ec_capacity(c) : 0;
+  L.ec_W = ec ? static_cast<int>(ceil_div(T, 32)) : 0;
+  L.rows_max = routed_rows_max(c) + (c->shared_d_ff > 0 ? T : 0);
   const size_t elt = c->dtype == MOE_BF16 ? 2 : 4;
   const int64_t ldh = std::max(c->d_ff, c->shared_d_ff);
   const int64_t nb = L.rp.nb;
@@ -127,11 +163,14 @@ Layout layout(const moe_config* c) {
   L.kept = take(sizeof(int32_t) * E);
   L.offsets = take(sizeof(int32_t) * (E + 2));
   L.row_token = take(sizeof(int32_t) * L.rows_max);
-  L.row_slot = take(sizeof(int32_t) * L.rows_max);
-  L.inv = take(sizeof(int32_t) * T * k);
+  L.row_slot = take(sizeof(int32_t) * (ec ? 0 : L.rows_max));
+  L.inv = take(sizeof(int32_t) * (ec ? 0 : T * k));
   L.tiles = take(sizeof(RowTile) * L.gp.tiles_max);
   L.ntiles = take(sizeof(int32_t));
   L.row_gate = take(sizeof(float) * L.rows_max);
+  L.probsT = take(sizeof(float) * (ec ? E * T : 0));
+  L.sel = take(sizeof(uint32_t) * E * L.ec_W);
+  L.pre = take(sizeof(int32_t) * E * L.ec_W);
   L.H = take(elt * L.rows_max * ldh);
   L.y_rows = take(sizeof(float) * L.rows_max * c->d_model);
   L.total = o;
@@ -189,7 +228,58 @@ moe_status run_ffn(const moe_config* c, const Layout& L, const void* x, const mo
   f.ntiles = reinterpret_cast<int32_t*>(at(ws, L.ntiles));
   f.row_gate = reinterpret_cast<float*>(at(ws, L.row_gate));
   f.tiles_ready = tiles_ready ? 1 : 0;
+  f.row_gates = expert_choice(c) ? 1 : 0;
   return hip_status(launch_ffn(L.gp, f, st));
+}
+
+// Expert-choice layer: the router writes the probabilities expert-major, each
+// expert selects its C tokens, the expert MLPs run over the E * C rows (+ the
+// shared expert's T), and the combine walks the selection bitmaps.
+moe_status forward_expert_choice(const moe_config* c, const Layout& L, const moe_weights* w,
+                                 const void* x, void* y, const moe_stats& o, void* ws,
+                                 hipStream_t st) {
+  moe_status s;
+  float* probsT = reinterpret_cast<float*>(at(ws, L.probsT));
+  double* stat_part = reinterpret_cast<double*>(at(ws, L.stat));
+  // the gate's top-1 and histogram go to scratch; only probsT and stat_part are used
+  if ((s = hip_status(launch_router(L.rp, x, c->dtype, w->Wg, w->bg,
+                                    reinterpret_cast<float*>(at(ws, L.part)),
+                                    reinterpret_cast<int32_t*>(at(ws, L.topk_idx)),
+                                    reinterpret_cast<float*>(at(ws, L.topk_w)), probsT, stat_part,
+                                    reinterpret_cast<int32_t*>(at(ws, L.hist)), nullptr, nullptr,
+                                    st))) != MOE_OK)
+    return s;
+  EcArgs a{};
+  a.T = c->T;
+  a.E = c->n_experts;
+  a.Ce = static_cast<int>(L.ec_C);
+  a.W = L.ec_W;
+  a.shared = c->shared_d_ff > 0;
+  a.BM = L.gp.BM;
+  a.nb = L.rp.nb;
+  a.row_token = reinterpret_cast<int32_t*>(at(ws, L.row_token));
+  a.offsets = reinterpret_cast<int32_t*>(at(ws, L.offsets));
+  a.counts = o.counts;
+  a.kept = o.kept;
+  a.row_gate = reinterpret_cast<float*>(at(ws, L.row_gate));
+  a.sel = reinterpret_cast<uint32_t*>(at(ws, L.sel));
+  a.pre = reinterpret_cast<int32_t*>(at(ws, L.pre));
+  a.tiles = reinterpret_cast<RowTile*>(at(ws, L.tiles));
+  a.ntiles = reinterpret_cast<int32_t*>(at(ws, L.ntiles));
+  a.stat_part = stat_part;
+  a.mean_prob = o.mean_prob;
+  a.balance = o.balance;
+  a.cv2 = o.cv2;
+  a.ec_idx = o.ec_idx;
+  a.ec_w = o.ec_w;
+  if ((s = hip_status(launch_expert_choice(a, probsT, st))) != MOE_OK) return s;
+  if (c->T == 0) return MOE_OK;
+  float* y_rows = reinterpret_cast<float*>(at(ws, L.y_rows));
+  if ((s = run_ffn(c, L, x, w, a.offsets, a.row_token, nullptr, nullptr, y_rows, ws, st, true)) !=
+      MOE_OK)
+    return s;
+  return hip_status(launch_combine_ec(c->T, c->d_model, c->n_experts, a.Ce, a.shared, c->dtype,
+                                      y_rows, a.sel, a.pre, y, st));
 }
 
 }  // namespace
@@ -206,6 +296,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const float* Wg, cons
                      float* balance, void* ws, size_t ws_bytes, void* stream) {
   moe_status s = check_config(cfg);
   if (s != MOE_OK) return s;
+  if (expert_choice(cfg)) return MOE_ERR_UNSUPPORTED;
   if (cfg->T > 0 && (!x || !Wg || !topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
   if (cfg->T > 0 && (!aligned16(x) || !aligned16(Wg))) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(cfg);
@@ -221,6 +312,7 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t*
                         int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
   moe_status s = check_config(cfg);
   if (s != MOE_OK) return s;
+  if (expert_choice(cfg)) return MOE_ERR_UNSUPPORTED;
   if (!counts || !kept || !offsets) return MOE_ERR_INVALID_ARG;
   if (cfg->T > 0 && (!topk_idx || !row_token || !row_slot || !inv)) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(cfg);
@@ -240,7 +332,9 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const moe_weight
   moe_status s = check_config(cfg);
   if (s != MOE_OK) return s;
   if ((s = check_weights(cfg, w)) != MOE_OK) return s;
-  if (!offsets || (cfg->T > 0 && (!x || !row_token || !row_slot || !topk_w || !y_rows)))
+  // expert choice: one gate per routed row, no slots
+  if (!offsets || (cfg->T > 0 && (!x || !row_token || !topk_w || !y_rows)) ||
+      (cfg->T > 0 && !expert_choice(cfg) && !row_slot))
     return MOE_ERR_INVALID_ARG;
   if (cfg->T > 0 && !aligned16(x)) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(cfg);
@@ -254,6 +348,7 @@ moe_status moe_combine(const moe_config* cfg, const float* y_rows, const int32_t
                        const int32_t* offsets, void* y, void* stream) {
   moe_status s = check_config(cfg);
   if (s != MOE_OK) return s;
+  if (expert_choice(cfg)) return MOE_ERR_UNSUPPORTED;
   if (cfg->T > 0 && (!y_rows || !inv || !offsets || !y)) return MOE_ERR_INVALID_ARG;
   if (cfg->T > 0 && (!aligned16(y_rows) || !aligned16(y))) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_combine(cfg->T, cfg->d_model, cfg->n_experts, cfg->top_k,
@@ -272,6 +367,11 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   moe_stats none{};
   const moe_stats& o = stats ? *stats : none;
+  if (expert_choice(cfg)) {
+    if (o.topk_idx || o.topk_w) return MOE_ERR_INVALID_ARG;
+    return forward_expert_choice(cfg, L, w, x, y, o, ws, st);
+  }
+  if (o.ec_idx || o.ec_w) return MOE_ERR_INVALID_ARG;
 
   int32_t* topk_idx = o.topk_idx ? o.topk_idx : reinterpret_cast<int32_t*>(at(ws, L.topk_idx));
   float* topk_w = o.topk_w ? o.topk_w : reinterpret_cast<float*>(at(ws, L.topk_w));

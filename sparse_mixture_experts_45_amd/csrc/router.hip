@@ -85,6 +85,7 @@ __device__ __forceinline__ void gate_block(Load load, GateSmem<EM>& sm, int64_t 
                                            const float* __restrict__ bg, int64_t T, int E,
                                            int k, int renorm, int32_t* __restrict__ topk_idx,
                                            float* __restrict__ topk_w, float* __restrict__ probs,
+                                           int64_t ps_t, int64_t ps_e,
                                            double* __restrict__ stat_part,
                                            int32_t* __restrict__ hist) {
   constexpr int TPW = kGateTokens / kRw;  // tokens per wave
@@ -138,7 +139,7 @@ __device__ __forceinline__ void gate_block(Load load, GateSmem<EM>& sm, int64_t 
       const int e = e0 + v;
       const float p = pz[v] / sum;
       if (vt && e < E) {
-        if (probs) probs[t * E + e] = p;
+        if (probs) probs[t * ps_t + e * ps_e] = p;
         sacc[v] += static_cast<double>(p);
       }
     }
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(kRw * 64) void router_scores_bf16_kernel(
     const bf16* __restrict__ x, const float* __restrict__ Wg, const float* __restrict__ bg,
     int64_t T, int d, int E, int kchunk, float* __restrict__ part, int k, int renorm,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ probs,
-    double* __restrict__ stat_part, int32_t* __restrict__ hist) {
+    int64_t ps_t, int64_t ps_e, double* __restrict__ stat_part, int32_t* __restrict__ hist) {
   constexpr int NE = TE / 16;   // expert blocks
   constexpr int QK = kRw / NE;  // K slices
   constexpr int G = 2;          // K steps in flight per wave
@@ -456,7 +457,8 @@ __global__ __launch_bounds__(kRw * 64) void router_scores_bf16_kernel(
 #pragma unroll
           for (int v = 0; v < VPL; ++v) l[v] = src[v];
         },
-        gsm, blockIdx.x, bg, T, E, k, renorm, topk_idx, topk_w, probs, stat_part, hist);
+        gsm, blockIdx.x, bg, T, E, k, renorm, topk_idx, topk_w, probs, ps_t, ps_e, stat_part,
+        hist);
   } else {
     for (int i = tid; i < kRtM * TE; i += kRw * 64) {
       const int tl = i / TE, el = i % TE;
@@ -475,7 +477,8 @@ template <int LPT, int VPL>
 __global__ __launch_bounds__(kRw * 64) void router_gate_kernel(
     const float* __restrict__ part, int S, const float* __restrict__ bg, int64_t T, int E, int k,
     int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ probs, double* __restrict__ stat_part, int32_t* __restrict__ hist) {
+    float* __restrict__ probs, int64_t ps_t, int64_t ps_e, double* __restrict__ stat_part,
+    int32_t* __restrict__ hist) {
   __shared__ GateSmem<kMaxExperts> gsm;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kGateTokens;
   const int64_t n = T * E;
@@ -515,7 +518,7 @@ __global__ __launch_bounds__(kRw * 64) void router_gate_kernel(
           }
         }
       },
-      gsm, blockIdx.x, bg, T, E, k, renorm, topk_idx, topk_w, probs, stat_part, hist);
+      gsm, blockIdx.x, bg, T, E, k, renorm, topk_idx, topk_w, probs, ps_t, ps_e, stat_part, hist);
 }
 
 // Load statistics from the per-block probability sums, one block.
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(1024) void router_stats_kernel(const double* __rest
 #define MOE_FUSED(TE_, VPL_)                                                                    \
   router_scores_bf16_kernel<TE_, true, 16, VPL_><<<g1, kRw * 64, 0, st>>>(                     \
       static_cast<const bf16*>(x), Wg, bg, p.T, p.d, p.E, p.kchunk, part, p.k, p.renorm,       \
-      topk_idx, topk_w, probs, stat_part, hist)
+      topk_idx, topk_w, probs, p.ps_t, p.ps_e, stat_part, hist)
 
 hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const float* Wg,
                          const float* bg, float* part, int32_t* topk_idx, float* topk_w,
@@ -552,11 +555,11 @@ hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const flo
         if (TE == 16)
           router_scores_bf16_kernel<16, false, 16, 1><<<g1, kRw * 64, 0, st>>>(
               static_cast<const bf16*>(x), Wg, bg, p.T, p.d, p.E, p.kchunk, part, p.k,
-              p.renorm, topk_idx, topk_w, probs, stat_part, hist);
+              p.renorm, topk_idx, topk_w, probs, p.ps_t, p.ps_e, stat_part, hist);
         else
           router_scores_bf16_kernel<64, false, 16, 1><<<g1, kRw * 64, 0, st>>>(
               static_cast<const bf16*>(x), Wg, bg, p.T, p.d, p.E, p.kchunk, part, p.k,
-              p.renorm, topk_idx, topk_w, probs, stat_part, hist);
+              p.renorm, topk_idx, topk_w, probs, p.ps_t, p.ps_e, stat_part, hist);
       } else {
         if (TE == 16)
           router_scores_f32_kernel<16><<<g1, 256, 0, st>>>(static_cast<const float*>(x), Wg,
@@ -568,7 +571,8 @@ hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const flo
       const unsigned nb = static_cast<unsigned>(p.nb);
 #define MOE_GATE(L, V)                                                                         \
   router_gate_kernel<L, V><<<nb, kRw * 64, 0, st>>>(part, p.S, bg, p.T, p.E, p.k, p.renorm,    \
-                                                    topk_idx, topk_w, probs, stat_part, hist)
+                                                    topk_idx, topk_w, probs, p.ps_t, p.ps_e,     \
+                                                    stat_part, hist)
       if (p.lpt == 16) {
         switch (p.vpl) {
           case 1: MOE_GATE(16, 1); break;

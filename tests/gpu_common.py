@@ -29,7 +29,8 @@ def torch_dtype(shape):
 def cfg_of(shape, T=None):
     return moe.config(shape.T if T is None else T, shape.d, shape.F, shape.E, shape.k,
                       act=shape.act, dtype=torch_dtype(shape), capacity=shape.capacity,
-                      renormalize=bool(shape.renormalize), shared_d_ff=shape.Fs)
+                      renormalize=bool(shape.renormalize), shared_d_ff=shape.Fs,
+                      routing=shape.routing)
 
 
 def gpu_forward(shape, dev, ws=None):
@@ -53,6 +54,58 @@ def gpu_forward(shape, dev, ws=None):
     out["y"] = y.float().cpu().numpy().astype(np.float64)
     out["y_raw"] = y
     return out
+
+
+def gpu_forward_ec(shape, dev, C, ws=None):
+    """moe_forward under expert-choice routing with its statistics and the
+    selection (ec_idx, ec_w) requested; returns numpy outputs."""
+    T, E = shape.T, shape.E
+    c = cfg_of(shape)
+    ws = moe.workspace(c) if ws is None else ws
+    y = torch.empty((T, shape.d), dtype=torch_dtype(shape), device="cuda")
+    st = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+              kept=torch.empty(E, dtype=torch.int32, device="cuda"),
+              mean_prob=torch.empty(E, dtype=torch.float32, device="cuda"),
+              balance=torch.empty(1, dtype=torch.float32, device="cuda"),
+              cv2=torch.empty(1, dtype=torch.float32, device="cuda"),
+              ec_idx=torch.full((E, max(C, 1)), -7, dtype=torch.int32, device="cuda"),
+              ec_w=torch.empty((E, max(C, 1)), dtype=torch.float32, device="cuda"))
+    moe.moe_forward(c, dev, dev["x"], y, st, ws)
+    torch.cuda.synchronize()
+    out = {key: v.cpu().numpy() for key, v in st.items()}
+    out["ec_idx"], out["ec_w"] = out["ec_idx"][:, :C], out["ec_w"][:, :C]
+    out["balance"] = float(out["balance"][0])
+    out["cv2"] = float(out["cv2"][0])
+    out["y"] = y.float().cpu().numpy().astype(np.float64)
+    out["y_raw"] = y
+    return out
+
+
+def check_ec_selection(shape, g, ref):
+    """Selection bit-exact (tokens of each expert, ascending), gates within
+    PROBS_ABS of the fp64 probabilities, counts = kept = C, and the load
+    statistics as under token choice."""
+    C, E = ref["C"], shape.E
+    want = np.array([np.nonzero(ref["sel"][:, e])[0] for e in range(E)],
+                    dtype=np.int64).reshape(E, C)
+    assert np.array_equal(g["ec_idx"], want)
+    if C:
+        err = float(np.max(np.abs(g["ec_w"] - ref["p"][want, np.arange(E)[:, None]])))
+        assert err <= PROBS_ABS, err
+    assert np.all(g["counts"] == C) and np.all(g["kept"] == C)
+    check_stats(shape, g, ref)
+
+
+def check_y_tokens(shape, got, ref):
+    """Per token: rows the reference sets to zero are exactly zero on the GPU;
+    the others are within 5x the layer tolerance of the reference row."""
+    nz = np.linalg.norm(ref, axis=1)
+    assert np.all(got[nz == 0] == 0.0)
+    tol = 5 * (Y_F32_REL_L2 if shape.dtype == "f32" else Y_BF16_REL_L2)
+    m = nz > 0
+    if m.any():
+        r = np.linalg.norm(got[m] - ref[m], axis=1) / nz[m]
+        assert float(r.max()) <= tol, float(r.max())
 
 
 def rel_l2(a, b):
@@ -81,6 +134,11 @@ def check_routing(shape, g, ref):
         assert err <= TOPK_W_ABS, err
     assert np.array_equal(g["counts"], ref["counts"])
     assert np.array_equal(g["kept"], ref["kept"])
+    check_stats(shape, g, ref)
+
+
+def check_stats(shape, g, ref):
+    """mean_prob, balance and cv^2 against the oracle."""
     if shape.T == 0:
         assert np.all(np.isnan(g["mean_prob"]))
         assert np.isnan(g["cv2"]) and np.isnan(ref["cv2"])   # no pairs: zero mean count

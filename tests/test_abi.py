@@ -92,3 +92,37 @@ def test_null_pointers_and_workspace_rejected_before_launch(lib):
     # dispatch needs its output arrays
     assert lib.moe_dispatch(C.byref(c), fake, None, None, None, None, None, None, fake, n,
                             None) == -1
+
+
+def test_expert_choice_config_checks(lib):
+    bad = cfg()
+    bad.routing = 2
+    assert lib.moe_workspace_bytes(C.byref(bad)) == 0
+    # top_k only sets the default C under expert choice: no top-k limit
+    ec = cfg(n_experts=64, top_k=40, routing="expert")
+    assert lib.moe_workspace_bytes(C.byref(ec)) > 0
+    assert moe.moe_workspace_bytes(cfg(T=4096, routing="expert")) > \
+        moe.moe_workspace_bytes(cfg(T=128, routing="expert"))
+    fake = C.c_void_p(0x10000)  # never dereferenced: checks fail first
+    c = cfg(routing="expert")
+    n = lib.moe_workspace_bytes(C.byref(c))
+    # the staged entry points take token-choice configs only
+    assert lib.moe_route(C.byref(c), fake, fake, None, fake, fake, None, None, None, fake, n,
+                         None) == -2
+    assert lib.moe_dispatch(C.byref(c), fake, fake, fake, fake, fake, fake, fake, fake, n,
+                            None) == -2
+    assert lib.moe_combine(C.byref(c), fake, fake, fake, fake, None) == -2
+    w = moe.moe_weights(Wg=fake, W1=fake, W2=fake)
+    # moe_expert_ffn takes them: its gates come one per row, row_slot is not needed,
+    # but rows and gates are
+    assert lib.moe_expert_ffn(C.byref(c), fake, C.byref(w), fake, None, None, fake, fake, fake,
+                              n, None) == -1
+    assert lib.moe_expert_ffn(C.byref(c), fake, C.byref(w), fake, fake, None, None, fake, fake,
+                              n, None) == -1
+    # top-k outputs do not exist under expert choice, nor the selection under token choice
+    st = moe.moe_stats(topk_idx=fake)
+    assert lib.moe_forward(C.byref(c), C.byref(w), fake, fake, C.byref(st), fake, n, None) == -1
+    ct = cfg()
+    st = moe.moe_stats(ec_idx=fake)
+    assert lib.moe_forward(C.byref(ct), C.byref(w), fake, fake, C.byref(st), fake,
+                           lib.moe_workspace_bytes(C.byref(ct)), None) == -1
