@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the sparse-MoE layer forward (test infrastructure only).
+"""fp64 CPU oracle of the sparse-MoE layer, forward and backward (test infrastructure only).
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
 package; the product path never imports it.  The arithmetic lives in
@@ -27,6 +27,16 @@ class _Cfg(C.Structure):
     _fields_ = [("T", C.c_int64), ("d", C.c_int32), ("F", C.c_int32), ("E", C.c_int32),
                 ("k", C.c_int32), ("act", C.c_int32), ("dtype", C.c_int32),
                 ("capacity", C.c_int32), ("renormalize", C.c_int32), ("Fs", C.c_int32)]
+
+
+class _Weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("Wg", "bg", "W1", "b1", "W2", "b2", "Ws1", "bs1",
+                                          "Ws2", "bs2")]
+
+
+class _Grads(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("dx", "dWg", "dbg", "dW1", "db1", "dW2", "db2",
+                                          "dWs1", "dbs1", "dWs2", "dbs2")]
 
 
 def build() -> str:
@@ -62,6 +72,15 @@ def _load():
         lib.orc_cv2.restype = C.c_double
         lib.orc_ec_select.argtypes = [C.POINTER(_Cfg), P, P, P, C.c_int64, P, P]
         lib.orc_ec_select.restype = C.c_int
+        W, G = C.POINTER(_Weights), C.POINTER(_Grads)
+        lib.orc_backward.argtypes = [C.POINTER(_Cfg), P, W, P, C.c_double, P, P, P, P, G]
+        lib.orc_backward_tokens.argtypes = [C.POINTER(_Cfg), P, W, P, C.c_double, P, P, P, P,
+                                            P, C.c_int64, P, P, P]
+        lib.orc_backward_expert_entries.argtypes = [C.POINTER(_Cfg), P, W, P, P, P, P,
+                                                    C.c_int32, C.c_int32, P, C.c_int32, P,
+                                                    P, P, P, P]
+        for f in (lib.orc_backward, lib.orc_backward_tokens, lib.orc_backward_expert_entries):
+            f.restype = C.c_int
         _lib = lib
     return _lib
 
@@ -230,3 +249,82 @@ def combine(shape, y_rows: np.ndarray, inv: np.ndarray, offsets: np.ndarray) -> 
         base = int(offsets[E])
         y += yr[base:base + T]
     return y
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (token choice): gradients of L = sum_t <dy_t, y_t> + alpha * balance
+# with the top-k selection and the capacity drops held fixed.
+
+
+def _weights(inp) -> _Weights:
+    return _Weights(*[_p(inp.get(n)) for n in ("Wg", "bg", "W1", "b1", "W2", "b2", "Ws1",
+                                                "bs1", "Ws2", "bs2")])
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def backward(shape, inp, dy, alpha: float = 0.0, rt: Optional[dict] = None) -> dict:
+    """Every gradient, fp64, summed over tokens in token order (small shapes):
+    dx [T, d], dWg [E, d], dbg [E], dW1 [E, F, d], db1 [E, F], dW2 [E, d, F],
+    db2 [E, d], and with a shared expert dWs1 [Fs, d], dbs1 [Fs], dWs2 [d, Fs],
+    dbs2 [d].  dy [T, d] (any float dtype, widened exactly)."""
+    rt = route(shape, inp, with_probs=False) if rt is None else rt
+    T, d, E, F, Fs = shape.T, shape.d, shape.E, shape.F, shape.Fs
+    z = np.zeros
+    g = dict(dx=z((T, d)), dWg=z((E, d)), dbg=z(E), dW1=z((E, F, d)), db1=z((E, F)),
+             dW2=z((E, d, F)), db2=z((E, d)))
+    if Fs:
+        g.update(dWs1=z((Fs, d)), dbs1=z(Fs), dWs2=z((d, Fs)), dbs2=z(d))
+    gr = _Grads(*[_p(g.get(n[0])) for n in _Grads._fields_])
+    w = _weights(inp)
+    dy64 = _f64(dy)
+    rc = _load().orc_backward(C.byref(_cfg(shape)), _p(inp["x"]), C.byref(w), _p(dy64),
+                              float(alpha), _p(np.ascontiguousarray(rt["topk_idx"], np.int32)),
+                              _p(_f64(rt["topk_w"])),
+                              _p(np.ascontiguousarray(rt["keep"], np.int32)),
+                              _p(_f64(rt["mean_prob"])), C.byref(gr))
+    if rc != 0:
+        raise ValueError("orc_backward failed")
+    return g
+
+
+def backward_tokens(shape, inp, dy, tokens, alpha: float = 0.0, rt: Optional[dict] = None):
+    """dx [n, d], router-score gradient dl [n, E] and gate gradient dg [n, k] of
+    the listed tokens."""
+    rt = route(shape, inp, with_probs=False) if rt is None else rt
+    toks = np.ascontiguousarray(tokens, dtype=np.int64)
+    n = len(toks)
+    out = dict(dx=np.zeros((n, shape.d)), dl=np.zeros((n, shape.E)), dg=np.zeros((n, shape.k)))
+    w = _weights(inp)
+    dy64 = _f64(dy)
+    rc = _load().orc_backward_tokens(
+        C.byref(_cfg(shape)), _p(inp["x"]), C.byref(w), _p(dy64), float(alpha),
+        _p(np.ascontiguousarray(rt["topk_idx"], np.int32)), _p(_f64(rt["topk_w"])),
+        _p(np.ascontiguousarray(rt["keep"], np.int32)), _p(_f64(rt["mean_prob"])), _p(toks), n,
+        _p(out["dx"]), _p(out["dl"]), _p(out["dg"]))
+    if rc != 0:
+        raise ValueError("orc_backward_tokens failed")
+    return out
+
+
+def backward_expert_entries(shape, inp, dy, e: int, f_list, j_list, rt: Optional[dict] = None):
+    """Entries of expert e's weight gradients (e = -1: the shared expert):
+    dW1 [nf, nj] = dW1[e][f_list][:, j_list], db1 [nf], dW2 [nj, nf] =
+    dW2[e][j_list][:, f_list], db2 [nj]."""
+    rt = route(shape, inp, with_probs=False) if rt is None else rt
+    fl = np.ascontiguousarray(f_list, np.int32)
+    jl = np.ascontiguousarray(j_list, np.int32)
+    out = dict(dW1=np.zeros((len(fl), len(jl))), db1=np.zeros(len(fl)),
+               dW2=np.zeros((len(jl), len(fl))), db2=np.zeros(len(jl)))
+    w = _weights(inp)
+    dy64 = _f64(dy)
+    rc = _load().orc_backward_expert_entries(
+        C.byref(_cfg(shape)), _p(inp["x"]), C.byref(w), _p(dy64),
+        _p(np.ascontiguousarray(rt["topk_idx"], np.int32)), _p(_f64(rt["topk_w"])),
+        _p(np.ascontiguousarray(rt["keep"], np.int32)), int(e), len(fl), _p(fl), len(jl),
+        _p(jl), _p(out["dW1"]), _p(out["db1"]), _p(out["dW2"]), _p(out["db2"]))
+    if rc != 0:
+        raise ValueError("orc_backward_expert_entries failed")
+    return out
