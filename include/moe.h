@@ -194,6 +194,63 @@ moe_status moe_combine(const moe_config *cfg, const float *y_rows, const int32_t
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
                        moe_stats *stats, void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Training: forward that keeps what the backward needs, and the backward.
+ *
+ * The backward returns the gradients of
+ *     L = sum_t <dy_t, y_t> + aux_coef * balance
+ * (dy: the upstream gradient of y; balance: the moe_stats statistic, the
+ * unbiased variance over experts of the mean router probability, which the
+ * pages add to the task loss with a small coefficient: botmartz "Load
+ * Balancing: The Hidden Challenge", total_loss = task_loss + 0.01 *
+ * balance_loss; roadtointelligence "Keeping the experts busy"; matteuscruz
+ * "Load balancing").  The top-k selection and the capacity drops are held
+ * fixed, as autograd treats them: a dropped slot gets no gate gradient but
+ * still counts in the renormalisation sum.  With E = 1 the balance term has
+ * no gradient.  Token choice only (MOE_ERR_UNSUPPORTED under
+ * MOE_ROUTE_EXPERT).
+ */
+
+/* Gradients written by moe_backward; each member may be NULL (not computed).
+ * Each has the layout and dtype of its tensor: dx [T, d] and the expert weight
+ * and bias gradients in cfg->dtype, dWg [E, d] and dbg [E] fp32.  The shared
+ * expert's members must be NULL when shared_d_ff = 0.  dx must be 16-byte
+ * aligned.  Gradients overwrite (they are not accumulated into). */
+typedef struct {
+  void *dx;
+  float *dWg, *dbg;
+  void *dW1, *db1, *dW2, *db2;
+  void *dWs1, *dbs1, *dWs2, *dbs2;
+} moe_grads;
+
+/* Workspace bytes of moe_forward_train + moe_backward (0 on an invalid or
+ * expert-choice config).  Besides the forward's buffers it holds the
+ * pre-activations, the softmax, transposed copies of the expert weights and of
+ * the grouped activations (each expert's rows padded to a multiple of 64). */
+size_t moe_train_workspace_bytes(const moe_config *cfg);
+
+/*
+ * moe_forward that also leaves in ws what moe_backward reads: the routing,
+ * the grouping, the softmax [T, E], the pre-activations z and hidden
+ * activations h of every row, and the gated expert outputs.  Same arguments
+ * and outputs as moe_forward; ws must have moe_train_workspace_bytes(cfg)
+ * bytes and stay untouched until the moe_backward call that consumes it.
+ */
+moe_status moe_forward_train(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
+                             moe_stats *stats, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of the moe_forward_train call that filled ws (same cfg, w and x).
+ *   dy [T, d] in cfg->dtype (16-byte aligned); aux_coef: the balance term's
+ *   coefficient (0 = none; NaN is rejected); grads: see moe_grads.
+ * Enqueued on `stream` after that forward; ws is garbage afterwards (run
+ * moe_forward_train again before another backward).  With T = 0 the requested
+ * parameter gradients are zero.
+ */
+moe_status moe_backward(const moe_config *cfg, const moe_weights *w, const void *x,
+                        const void *dy, float aux_coef, moe_grads *grads, void *ws,
+                        size_t ws_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *moe_status_string(moe_status s);
 

@@ -19,7 +19,8 @@ __all__ = [
     "MOE_ROUTE_EXPERT", "MoeError", "moe_config",
     "moe_weights", "moe_stats", "config", "library", "moe_workspace_bytes", "moe_route",
     "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_status_string",
-    "workspace", "LIB_PATH",
+    "workspace", "LIB_PATH", "moe_grads", "moe_train_workspace_bytes", "moe_forward_train",
+    "moe_backward", "train_workspace",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.so")
@@ -50,6 +51,11 @@ class moe_weights(C.Structure):
                                           "Ws1", "bs1", "Ws2", "bs2")]
 
 
+class moe_grads(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("dx", "dWg", "dbg", "dW1", "db1", "dW2", "db2",
+                                          "dWs1", "dbs1", "dWs2", "dbs2")]
+
+
 class moe_stats(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("topk_idx", "topk_w", "counts", "kept",
                                           "mean_prob", "balance", "cv2", "ec_idx",
@@ -77,7 +83,13 @@ def library() -> C.CDLL:
         lib.moe_combine.argtypes = [CP, P, P, P, P, P]
         lib.moe_forward.argtypes = [CP, C.POINTER(moe_weights), P, P, C.POINTER(moe_stats),
                                     P, S, P]
-        for f in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward"):
+        lib.moe_train_workspace_bytes.argtypes = [CP]
+        lib.moe_train_workspace_bytes.restype = S
+        lib.moe_forward_train.argtypes = lib.moe_forward.argtypes
+        lib.moe_backward.argtypes = [CP, C.POINTER(moe_weights), P, P, C.c_float,
+                                     C.POINTER(moe_grads), P, S, P]
+        for f in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
+                  "moe_forward_train", "moe_backward"):
             getattr(lib, f).restype = C.c_int
         lib.moe_status_string.argtypes = [C.c_int]
         lib.moe_status_string.restype = C.c_char_p
@@ -181,3 +193,42 @@ def moe_forward(cfg, weights: dict, x, y, stats: Optional[dict] = None, ws=None,
                        "ec_idx", "ec_w")])
     _check("moe_forward", library().moe_forward(
         C.byref(cfg), C.byref(w), _ptr(x), _ptr(y), C.byref(st), wp, wn, _stream(stream)))
+
+
+def moe_train_workspace_bytes(cfg: moe_config) -> int:
+    return int(library().moe_train_workspace_bytes(C.byref(cfg)))
+
+
+def train_workspace(cfg: moe_config, device="cuda") -> torch.Tensor:
+    """A uint8 device tensor of moe_train_workspace_bytes(cfg) bytes."""
+    n = moe_train_workspace_bytes(cfg)
+    if n == 0:
+        raise MoeError("moe_train_workspace_bytes", -1)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _stats(stats: Optional[dict]) -> moe_stats:
+    return moe_stats(*[_ptr((stats or {}).get(n)) for n in
+                       ("topk_idx", "topk_w", "counts", "kept", "mean_prob", "balance", "cv2",
+                        "ec_idx", "ec_w")])
+
+
+def moe_forward_train(cfg, weights: dict, x, y, stats: Optional[dict] = None, ws=None,
+                      stream=None):
+    wp, wn = _ws(ws)
+    w = _weights(weights)
+    st = _stats(stats)
+    _check("moe_forward_train", library().moe_forward_train(
+        C.byref(cfg), C.byref(w), _ptr(x), _ptr(y), C.byref(st), wp, wn, _stream(stream)))
+
+
+def moe_backward(cfg, weights: dict, x, dy, grads: dict, aux_coef: float = 0.0, ws=None,
+                 stream=None):
+    """grads: tensors keyed dx, dWg, dbg, dW1, db1, dW2, db2, dWs1, dbs1, dWs2, dbs2
+    (missing keys are not computed)."""
+    wp, wn = _ws(ws)
+    w = _weights(weights)
+    g = moe_grads(*[_ptr(grads.get(n)) for n, _ in moe_grads._fields_])
+    _check("moe_backward", library().moe_backward(
+        C.byref(cfg), C.byref(w), _ptr(x), _ptr(dy), float(aux_coef), C.byref(g), wp, wn,
+        _stream(stream)))

@@ -1,0 +1,572 @@
+// Backward pass of the token-choice layer: gradients of
+//   L = sum_t <dy_t, y_t> + alpha * balance
+// with the top-k selection and the capacity drops fixed (the training side of
+// the layer: botmartz "Load Balancing: The Hidden Challenge", total loss = task
+// loss + 0.01 * balance loss; roadtointelligence "Keeping the experts busy";
+// matteuscruz "Load balancing").
+//
+// Per kept (token, slot) row r of expert e with gate g, pre-activation z and
+// hidden h = act(z) (both kept by the training forward), and the shared rows
+// (gate 1):
+//   dz_r   = g (dy_t W2[e]) * act'(z)        input-gradient GEMM pass (gemm.hip)
+//   dX_r   = dz_r W1[e]                       same pass, second GEMM
+//   dx_t   = sum over t's rows of dX_r + sum_e dl[t, e] W_g[e]       dx_kernel
+//   dW1[e] = sum_r dz_r^T x_t,  dW2[e] = sum_r (g dy_t)^T h_r        wgrad_kernel
+//   db1[e] = sum_r dz_r,        db2[e] = sum_r g dy_t                seg_sum_kernel
+//   dg     = <dy_t, o_r> = <dy_t, y_rows[r]> / g                     gate_grad_kernel
+//   dp     = renormalisation backward of dg, plus the balance term,
+//   dl     = p (dp - <p, dp>)                                       router_bwd_kernel
+//   dW_g   = dl^T x, db_g = sum_t dl                                 router_wgrad_*
+//
+// The GEMMs need K-contiguous operands: the input-gradient pass multiplies by
+// the transposed expert weights (transpose_kernel), and the weight-gradient
+// GEMMs contract over an expert's rows, so their operands are transposed with
+// each expert's rows padded to a multiple of 64 columns (gather_transpose_kernel;
+// padding columns are zero, so every group's K is a whole number of K steps).
+#include "kernels.h"
+#include "block_ops.h"
+#include "mfma.h"
+
+namespace moe {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// out[b][c][r] = in[b][r][c]; 64 x 64 tiles through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in,
+                                                        T* __restrict__ out, int R, int C) {
+  __shared__ T tile[64][65];
+  const int64_t off = static_cast<int64_t>(blockIdx.z) * R * C;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < R && c < C) tile[i][tx] = in[off + static_cast<int64_t>(r) * C + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < C && r < R) out[off + static_cast<int64_t>(c) * R + r] = tile[tx][i];
+  }
+}
+
+// Padded column offsets of the G row groups: poff[g + 1] = poff[g] + the
+// group's rows rounded up to 64.
+__global__ __launch_bounds__(kMaxExperts) void poff_kernel(const int32_t* __restrict__ offsets,
+                                                           int G, int32_t* __restrict__ poff) {
+  __shared__ int32_t wsum[kMaxExperts / 64];
+  const int g = threadIdx.x;
+  const int w = g < G ? (offsets[g + 1] - offsets[g] + 63) / 64 * 64 : 0;
+  int total;
+  const int start = block_excl_scan(w, wsum, total);
+  if (g < G) poff[g] = start;
+  if (g == 0) poff[G] = total;
+}
+
+// out[c][poff[g] + j] = scale * src[row][c] for the j-th row of group g (row =
+// row_token[offsets[g] + j] when gathering, else offsets[g] + j; scale =
+// row_gate of that grouped row when given, else 1); zero in the padding
+// columns.  A block covers 64 padded columns (inside one group, as every group
+// spans a multiple of 64) and 64 values of c.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_transpose_kernel(
+    const T* __restrict__ src, int64_t lds, int C, const int32_t* __restrict__ row_token,
+    const float* __restrict__ row_gate, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ poff, int G, T* __restrict__ out, int64_t ldo) {
+  __shared__ T tile[64][65];
+  const int col0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  if (col0 >= poff[G]) return;
+  int lo = 0, hi = G;  // poff[lo] <= col0 < poff[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (poff[mid] <= col0) lo = mid;
+    else hi = mid;
+  }
+  const int j0 = col0 - poff[lo], base = offsets[lo], rows = offsets[lo + 1] - base;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int j = j0 + i, c = c0 + tx;
+    float v = 0.f;
+    if (j < rows && c < C) {
+      const int r = base + j;
+      const int64_t srow = row_token ? row_token[r] : r;
+      v = to_f32<T>(src[srow * lds + c]);
+      if (row_gate) v *= row_gate[r];
+    }
+    tile[i][tx] = from_f32<T>(v);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i;
+    if (c < C) out[static_cast<int64_t>(c) * ldo + col0 + tx] = tile[tx][i];
+  }
+}
+
+// Bias gradients: out_g[c] = sum of in[c][poff[g] .. poff[g + 1]) for group g
+// (routed groups g < E write out + g * C, the shared group out_sh, with Cs
+// values).  One wave per (c, g), lanes strided over the segment.
+template <typename T>
+__global__ __launch_bounds__(256) void seg_sum_kernel(const T* __restrict__ in, int64_t ldi,
+                                                      const int32_t* __restrict__ poff, int E,
+                                                      int C, int Cs, T* __restrict__ out,
+                                                      T* __restrict__ out_sh) {
+  const int g = blockIdx.y, c = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int Cg = g < E ? C : Cs;
+  T* o = g < E ? (out ? out + static_cast<int64_t>(g) * C : nullptr) : out_sh;
+  if (c >= Cg || !o) return;
+  const T* row = in + static_cast<int64_t>(c) * ldi;
+  float s = 0.f;
+  for (int col = poff[g] + lane; col < poff[g + 1]; col += 64) s += to_f32<T>(row[col]);
+  s = wave_sum<T>(s);
+  if (lane == 0) o[c] = from_f32<T>(s);
+}
+
+struct WgradArgs {
+  const void* A;  // [M, lda]: group g's K columns start at poff[g0 + gi]
+  int64_t lda;
+  const void* B;  // [N, ldb]
+  int64_t ldb;
+  const int32_t* poff;
+  int g0;         // first group of this launch
+  int M, N, tiles_m, tiles_n;
+  void* C;        // [groups, M, N]
+};
+
+// C_gi[m][n] = sum over group g0 + gi's K columns of A[m][k] B[n][k]: the
+// weight gradients, contracting over the rows each expert received.  Every
+// group's K is a multiple of 64 (zero padded); K = 0 writes zeros.  Register-
+// staged tiles with a padded LDS row; MFMA 32x32.
+template <typename T, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(WM* WN * 64) void wgrad_kernel(WgradArgs a) {
+  using M = Mfma<T>;
+  constexpr int NT = WM * WN * 64;
+  constexpr int CH = 16 / sizeof(T);
+  constexpr int LDK = BK + CH;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MI = WTM / 32, NI = WTN / 32;
+  constexpr int CPR = BK / CH;
+  constexpr int ACH = BM * CPR / NT, BCH = BN * CPR / NT;
+  static_assert(ACH >= 1 && BCH >= 1 && BM * CPR % NT == 0 && BN * CPR % NT == 0, "loader");
+  __shared__ __align__(16) T As[BM * LDK];
+  __shared__ __align__(16) T Bs[BN * LDK];
+
+  const int per = a.tiles_m * a.tiles_n;
+  const int gi = blockIdx.x / per, rem = blockIdx.x % per;
+  const int mt = rem / a.tiles_n, nt = rem % a.tiles_n;
+  const int g = a.g0 + gi;
+  const int k0 = a.poff[g], K = a.poff[g + 1] - k0;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const T* asrc[ACH];
+  int aoff[ACH], akc[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int c = tid + i * NT, r = c / CPR;
+    akc[i] = (c % CPR) * CH;
+    aoff[i] = r * LDK + akc[i];
+    asrc[i] = m0 + r < a.M ? static_cast<const T*>(a.A) + static_cast<int64_t>(m0 + r) * a.lda + k0
+                           : nullptr;
+  }
+  const T* bsrc[BCH];
+  int boff[BCH], bkc[BCH];
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) {
+    const int c = tid + i * NT, r = c / CPR;
+    bkc[i] = (c % CPR) * CH;
+    boff[i] = r * LDK + bkc[i];
+    bsrc[i] = n0 + r < a.N ? static_cast<const T*>(a.B) + static_cast<int64_t>(n0 + r) * a.ldb + k0
+                           : nullptr;
+  }
+  uint4 ra[ACH], rb[BCH];
+  auto gload = [&](int kk0) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+      ra[i] = asrc[i] ? *reinterpret_cast<const uint4*>(asrc[i] + kk0 + akc[i])
+                      : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < BCH; ++i)
+      rb[i] = bsrc[i] ? *reinterpret_cast<const uint4*>(bsrc[i] + kk0 + bkc[i])
+                      : make_uint4(0, 0, 0, 0);
+  };
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  if (K > 0) gload(0);
+  for (int kk0 = 0; kk0 < K; kk0 += BK) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) *reinterpret_cast<uint4*>(&As[aoff[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) *reinterpret_cast<uint4*>(&Bs[boff[i]]) = rb[i];
+    __syncthreads();
+    if (kk0 + BK < K) gload(kk0 + BK);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += M::kStep) {
+      const int kl = kk + (lane >> 5) * M::kVec;
+      typename M::frag fa[MI], fb[NI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        fa[i] = M::load(&As[(wm * WTM + i * 32 + (lane & 31)) * LDK + kl]);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        fb[j] = M::load(&Bs[(wn * WTN + j * 32 + (lane & 31)) * LDK + kl]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[i][j] = M::op(fa[i], fb[j], acc[i][j]);
+    }
+  }
+  T* Cg = static_cast<T*>(a.C) + static_cast<int64_t>(gi) * a.M * a.N;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int n = n0 + wn * WTN + j * 32 + (lane & 31);
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = m0 + wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+        if (m < a.M) Cg[static_cast<int64_t>(m) * a.N + n] = from_f32<T>(acc[i][j][q]);
+      }
+  }
+}
+
+// dg[t * k + i] = <dy_t, y_rows[r]> / gate_r for the pair's row r = inv[t * k + i]
+// (the expert output before gating); 0 for a dropped pair or a zero gate.  One
+// wave per pair.
+template <typename T>
+__global__ __launch_bounds__(256) void gate_grad_kernel(const T* __restrict__ dy,
+                                                        const float* __restrict__ y_rows,
+                                                        const int32_t* __restrict__ inv,
+                                                        const float* __restrict__ row_gate,
+                                                        int64_t pairs, int k, int d,
+                                                        float* __restrict__ dg) {
+  const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (pair >= pairs) return;
+  const int r = inv[pair];
+  const int64_t t = pair / k;
+  float s = 0.f;
+  if (r >= 0) {
+    const float* yr = y_rows + static_cast<int64_t>(r) * d;
+    const T* dyt = dy + t * d;
+    for (int c = lane * 4; c < d; c += 256) {
+      const float4 v = *reinterpret_cast<const float4*>(yr + c);
+      s += v.x * to_f32<T>(dyt[c]) + v.y * to_f32<T>(dyt[c + 1]) + v.z * to_f32<T>(dyt[c + 2]) +
+           v.w * to_f32<T>(dyt[c + 3]);
+    }
+  }
+  s = wave_sum<T>(s);
+  if (lane == 0) {
+    const float g = r >= 0 ? row_gate[r] : 0.f;
+    dg[pair] = g != 0.f ? s / g : 0.f;
+  }
+}
+
+// aux_dp[e] = alpha * 2 (m_e - mean m) / ((E - 1) T): the balance term's
+// gradient with respect to each token's probability of expert e, m_e the mean
+// probability (from the gate's fp64 per-block sums); 0 when alpha = 0 or E = 1.
+__global__ __launch_bounds__(kMaxExperts) void aux_prep_kernel(const double* __restrict__ stat_part,
+                                                               int nb, int E, int64_t T,
+                                                               float alpha,
+                                                               float* __restrict__ aux_dp) {
+  __shared__ double wsd[kMaxExperts / 64];
+  const int e = threadIdx.x;
+  double m = 0.0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) m += stat_part[static_cast<int64_t>(b) * E + e];
+    m /= static_cast<double>(T);
+  }
+  const double mbar = block_sum_d(m, wsd) / E;
+  if (e < E)
+    aux_dp[e] = (E > 1 && alpha != 0.f)
+                    ? static_cast<float>(alpha * 2.0 * (m - mbar) / ((E - 1) * static_cast<double>(T)))
+                    : 0.f;
+}
+
+// One 64-lane block per token: dp over the experts (renormalisation backward of
+// the gate gradients on the k chosen experts, plus aux_dp), then the softmax
+// backward dl = p (dp - <p, dp>).
+__global__ __launch_bounds__(64) void router_bwd_kernel(const float* __restrict__ probs,
+                                                        const int32_t* __restrict__ topk_idx,
+                                                        const float* __restrict__ topk_w,
+                                                        const float* __restrict__ dg,
+                                                        const float* __restrict__ aux_dp, int E,
+                                                        int k, int renorm, float* __restrict__ dl) {
+  __shared__ float dp[kMaxExperts];
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* p = probs + t * E;
+  for (int e = lane; e < E; e += 64) dp[e] = aux_dp[e];
+  int ei = 0;
+  float pi = 0.f, gi = 0.f, dgi = 0.f;
+  if (lane < k) {
+    ei = topk_idx[t * k + lane];
+    pi = p[ei];
+    gi = topk_w[t * k + lane];
+    dgi = dg[t * k + lane];
+  }
+  const float S = wave_sum<float>(pi), dot = wave_sum<float>(dgi * gi);
+  __syncthreads();
+  if (lane < k) dp[ei] += renorm ? (dgi - dot) / S : dgi;  // the k experts are distinct
+  __syncthreads();
+  float s = 0.f;
+  for (int e = lane; e < E; e += 64) s += p[e] * dp[e];
+  s = wave_sum<float>(s);
+  for (int e = lane; e < E; e += 64) dl[t * E + e] = p[e] * (dp[e] - s);
+}
+
+// part[s][e][j] = sum over the tokens of chunk s of dl[t][e] x[t][j]; column
+// j = d is the bias (x = 1).  Eight experts per block; the dl loads are uniform.
+template <typename T>
+__global__ __launch_bounds__(256) void router_wgrad_part_kernel(const T* __restrict__ x,
+                                                                const float* __restrict__ dl,
+                                                                int64_t Tn, int d, int E,
+                                                                int64_t chunk,
+                                                                float* __restrict__ part) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  const int e0 = blockIdx.y * 8;
+  const int64_t s = blockIdx.z, t0 = s * chunk, t1 = min(Tn, t0 + chunk);
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  for (int64_t t = t0; t < t1; ++t) {
+    const float xv = j < d ? to_f32<T>(x[t * d + j]) : (j == d ? 1.f : 0.f);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (e0 + q < E) acc[q] += dl[t * E + e0 + q] * xv;
+  }
+  if (j <= d)
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (e0 + q < E) part[(s * E + e0 + q) * (d + 1) + j] = acc[q];
+}
+
+// dWg[e][j] (j < d) and dbg[e] (j = d) = sum over the chunks, in chunk order.
+__global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __restrict__ part,
+                                                               int S, int d, int E,
+                                                               float* __restrict__ dWg,
+                                                               float* __restrict__ dbg) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n = static_cast<int64_t>(E) * (d + 1);
+  if (i >= n) return;
+  float v = 0.f;
+  for (int s = 0; s < S; ++s) v += part[s * n + i];
+  const int e = static_cast<int>(i / (d + 1)), j = static_cast<int>(i % (d + 1));
+  if (j < d) {
+    if (dWg) dWg[static_cast<int64_t>(e) * d + j] = v;
+  } else if (dbg) {
+    dbg[e] = v;
+  }
+}
+
+// dx[t] = sum over t's kept slots of dX[inv[t, i]] (+ the shared row) +
+// sum_e dl[t][e] W_g[e].  Eight tokens per block share the W_g loads; a thread
+// owns 4 columns.
+constexpr int kDxTokens = 8;
+template <typename T>
+__global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dX,
+                                                 const int32_t* __restrict__ inv,
+                                                 const int32_t* __restrict__ offsets,
+                                                 const float* __restrict__ dl,
+                                                 const float* __restrict__ Wg, int64_t Tn, int d,
+                                                 int E, int k, int shared, T* __restrict__ dx) {
+  __shared__ float sdl[kDxTokens][kMaxExperts];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kDxTokens;
+  for (int i = threadIdx.x; i < kDxTokens * E; i += 256) {
+    const int tt = i / E, e = i % E;
+    sdl[tt][e] = t0 + tt < Tn ? dl[(t0 + tt) * E + e] : 0.f;
+  }
+  __syncthreads();
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c >= d) return;
+  float4 acc[kDxTokens];
+#pragma unroll
+  for (int tt = 0; tt < kDxTokens; ++tt) acc[tt] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int e = 0; e < E; ++e) {
+    const float4 w = *reinterpret_cast<const float4*>(Wg + static_cast<int64_t>(e) * d + c);
+#pragma unroll
+    for (int tt = 0; tt < kDxTokens; ++tt) {
+      const float l = sdl[tt][e];
+      acc[tt].x += l * w.x;
+      acc[tt].y += l * w.y;
+      acc[tt].z += l * w.z;
+      acc[tt].w += l * w.w;
+    }
+  }
+  const int rs0 = shared ? offsets[E] : 0;
+  for (int tt = 0; tt < kDxTokens; ++tt) {
+    const int64_t t = t0 + tt;
+    if (t >= Tn) break;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < k; ++i) {
+      const int r = inv[t * k + i];
+      if (r < 0) continue;
+      const float4 u = *reinterpret_cast<const float4*>(dX + static_cast<int64_t>(r) * d + c);
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
+    if (shared) {
+      const float4 u = *reinterpret_cast<const float4*>(dX + (rs0 + t) * d + c);
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
+    v.x += acc[tt].x;
+    v.y += acc[tt].y;
+    v.z += acc[tt].z;
+    v.w += acc[tt].w;
+    store4<T>(dx + t * d + c, v);
+  }
+}
+
+// Zero fill (used where a gradient is zero by definition, e.g. T = 0).
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int64_t words) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < words;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0u;
+}
+
+template <typename T>
+void run_transpose(const void* in, void* out, int B, int R, int C, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(ceil_div(C, 64)), static_cast<unsigned>(ceil_div(R, 64)),
+                  static_cast<unsigned>(B));
+  transpose_kernel<T><<<grid, 256, 0, st>>>(static_cast<const T*>(in), static_cast<T*>(out), R, C);
+}
+
+template <typename T>
+void run_wgrad(const WgradArgs& w, int groups, hipStream_t st) {
+  if (groups <= 0 || w.M <= 0 || w.N <= 0) return;
+  constexpr bool B16 = sizeof(T) == 2;
+  constexpr int BM = B16 ? 128 : 64, BN = B16 ? 128 : 64, BK = B16 ? 64 : 32;
+  WgradArgs a = w;
+  a.tiles_m = static_cast<int>(ceil_div(a.M, BM));
+  a.tiles_n = static_cast<int>(ceil_div(a.N, BN));
+  const int64_t blocks = static_cast<int64_t>(groups) * a.tiles_m * a.tiles_n;
+  wgrad_kernel<T, BM, BN, BK, 2, 2><<<static_cast<unsigned>(blocks), 256, 0, st>>>(a);
+}
+
+template <typename T>
+void run_bwd(const BwdArgs& b, int part, hipStream_t st) {
+  const int ldh = b.F > b.Fs ? b.F : b.Fs;
+  const int G = b.E + (b.Fs > 0 ? 1 : 0);
+  if (part == kBwdWeights) {
+    run_transpose<T>(b.W1, b.W1T, b.E, b.F, b.d, st);
+    run_transpose<T>(b.W2, b.W2T, b.E, b.d, b.F, st);
+    if (b.Fs > 0) {
+      run_transpose<T>(b.Ws1, b.Ws1T, 1, b.Fs, b.d, st);
+      run_transpose<T>(b.Ws2, b.Ws2T, 1, b.d, b.Fs, st);
+    }
+    return;
+  }
+  if (part == kBwdRouter) {
+    const int64_t pairs = b.T * b.k;
+    gate_grad_kernel<T><<<static_cast<unsigned>(ceil_div(pairs, 4)), 256, 0, st>>>(
+        static_cast<const T*>(b.dy), b.y_rows, b.inv, b.row_gate, pairs, b.k, b.d, b.dg);
+    aux_prep_kernel<<<1, kMaxExperts, 0, st>>>(b.stat_part, b.nb, b.E, b.T, b.alpha, b.aux_dp);
+    router_bwd_kernel<<<static_cast<unsigned>(b.T), 64, 0, st>>>(
+        b.probs, b.topk_idx, b.topk_w, b.dg, b.aux_dp, b.E, b.k, b.renorm, b.dl);
+    if (b.dWg || b.dbg) {
+      const dim3 grid(static_cast<unsigned>(ceil_div(b.d + 1, 256)),
+                      static_cast<unsigned>(ceil_div(b.E, 8)), static_cast<unsigned>(b.wg_split));
+      router_wgrad_part_kernel<T><<<grid, 256, 0, st>>>(static_cast<const T*>(b.x), b.dl, b.T,
+                                                        b.d, b.E, b.wg_chunk, b.wg_part);
+      const int64_t n = static_cast<int64_t>(b.E) * (b.d + 1);
+      router_wgrad_sum_kernel<<<static_cast<unsigned>(ceil_div(n, 256)), 256, 0, st>>>(
+          b.wg_part, b.wg_split, b.d, b.E, b.dWg, b.dbg);
+    }
+    return;
+  }
+  if (part == kBwdDx) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(b.T, kDxTokens)),
+                    static_cast<unsigned>(ceil_div(b.d, 1024)));
+    dx_kernel<T><<<grid, 256, 0, st>>>(b.dX, b.inv, b.offsets, b.dl, b.Wg, b.T, b.d, b.E, b.k,
+                                       b.Fs > 0, static_cast<T*>(b.dx));
+    return;
+  }
+  // kBwdExpertWeights: transposed operands, weight GEMMs, bias sums
+  poff_kernel<<<1, kMaxExperts, 0, st>>>(b.offsets, G, b.poff);
+  const unsigned pcols = static_cast<unsigned>(b.Rp / 64);
+  auto gt = [&](const void* src, int64_t lds, int C, const int32_t* rt, const float* gate,
+                void* out) {
+    const dim3 grid(pcols, static_cast<unsigned>(ceil_div(C, 64)));
+    gather_transpose_kernel<T><<<grid, 256, 0, st>>>(static_cast<const T*>(src), lds, C, rt, gate,
+                                                     b.offsets, b.poff, G,
+                                                     static_cast<T*>(out), b.Rp);
+  };
+  const bool w1 = b.dW1 || b.dWs1 || b.db1 || b.dbs1;
+  const bool w2 = b.dW2 || b.dWs2 || b.db2 || b.dbs2;
+  if (w1) {
+    gt(b.Z, ldh, ldh, nullptr, nullptr, b.ZT);        // dz^T
+    if (b.dW1 || b.dWs1) gt(b.x, b.d, b.d, b.row_token, nullptr, b.XT);  // x rows^T
+  }
+  if (w2) {
+    gt(b.dy, b.d, b.d, b.row_token, b.row_gate, b.DT);  // (gate dy)^T
+    if (b.dW2 || b.dWs2) gt(b.H, ldh, ldh, nullptr, nullptr, b.HT);  // h^T
+  }
+  WgradArgs w{};
+  w.poff = b.poff;
+  if (b.dW1) {  // dW1[e] [F, d] = dz^T x
+    w.A = b.ZT, w.lda = b.Rp, w.B = b.XT, w.ldb = b.Rp, w.g0 = 0, w.M = b.F, w.N = b.d;
+    w.C = b.dW1;
+    run_wgrad<T>(w, b.E, st);
+  }
+  if (b.dWs1 && b.Fs > 0) {
+    w.A = b.ZT, w.lda = b.Rp, w.B = b.XT, w.ldb = b.Rp, w.g0 = b.E, w.M = b.Fs, w.N = b.d;
+    w.C = b.dWs1;
+    run_wgrad<T>(w, 1, st);
+  }
+  if (b.dW2) {  // dW2[e] [d, F] = (gate dy)^T h
+    w.A = b.DT, w.lda = b.Rp, w.B = b.HT, w.ldb = b.Rp, w.g0 = 0, w.M = b.d, w.N = b.F;
+    w.C = b.dW2;
+    run_wgrad<T>(w, b.E, st);
+  }
+  if (b.dWs2 && b.Fs > 0) {
+    w.A = b.DT, w.lda = b.Rp, w.B = b.HT, w.ldb = b.Rp, w.g0 = b.E, w.M = b.d, w.N = b.Fs;
+    w.C = b.dWs2;
+    run_wgrad<T>(w, 1, st);
+  }
+  if (b.db1 || b.dbs1)
+    seg_sum_kernel<T><<<dim3(static_cast<unsigned>(ceil_div(ldh, 4)), G), 256, 0, st>>>(
+        static_cast<const T*>(b.ZT), b.Rp, b.poff, b.E, b.F, b.Fs, static_cast<T*>(b.db1),
+        static_cast<T*>(b.dbs1));
+  if (b.db2 || b.dbs2)
+    seg_sum_kernel<T><<<dim3(static_cast<unsigned>(ceil_div(b.d, 4)), G), 256, 0, st>>>(
+        static_cast<const T*>(b.DT), b.Rp, b.poff, b.E, b.d, b.d, static_cast<T*>(b.db2),
+        static_cast<T*>(b.dbs2));
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs& b, int part, hipStream_t st) {
+  if (b.dtype == MOE_BF16) run_bwd<bf16>(b, part, st);
+  else run_bwd<float>(b, part, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
+  const int64_t words = static_cast<int64_t>(bytes / 4);
+  if (words > 0)
+    zero_kernel<<<static_cast<unsigned>(std::min<int64_t>(ceil_div(words, 256), 4096)), 256, 0,
+                  st>>>(static_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
+}  // namespace moe

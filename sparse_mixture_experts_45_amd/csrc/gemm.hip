@@ -25,43 +25,12 @@
 
 #include "kernels.h"
 #include "block_ops.h"
+#include "mfma.h"
 
 namespace moe {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 constexpr int kXcd = 8;
 constexpr int kBand = 8;
-
-template <typename T>
-struct Mfma;
-
-// v_mfma_f32_32x32x16_bf16: lane l supplies row (l % 32), k = (l / 32) * 8 + 0..7
-template <>
-struct Mfma<bf16> {
-  static constexpr int kStep = 16;
-  static constexpr int kVec = 8;
-  typedef bf16x8_t frag;
-  static __device__ __forceinline__ frag load(const bf16* p) {
-    return *reinterpret_cast<const bf16x8_t*>(p);
-  }
-  static __device__ __forceinline__ f32x16 op(frag a, frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-// v_mfma_f32_32x32x2f32: lane l supplies row (l % 32), k = l / 32
-template <>
-struct Mfma<float> {
-  static constexpr int kStep = 2;
-  static constexpr int kVec = 1;
-  typedef float frag;
-  static __device__ __forceinline__ frag load(const float* p) { return *p; }
-  static __device__ __forceinline__ f32x16 op(frag a, frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-  }
-};
 
 // erf by Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26:
 // erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
@@ -81,6 +50,28 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752440f));
 }
 
+// its derivative: Phi(z) + z phi(z) = 0.5 (1 + erf(z / sqrt 2)) + z exp(-z^2 / 2) / sqrt(2 pi)
+__device__ __forceinline__ float gelu_erf_grad(float z) {
+  return 0.5f * (1.0f + erf_as(z * 0.70710678118654752440f)) +
+         z * 0.39894228040143267794f * __expf(-0.5f * z * z);
+}
+
+// What a grouped-GEMM launch computes (C = A B^T over row tiles):
+//   kUp       A = x rows gathered by row_token; out (layer dtype) = act(C + b1)
+//   kUpTrain  as kUp, and the pre-activation C + b1 also to aux (same layout)
+//   kDown     A = contiguous rows; out (fp32) = gate * (C + b2), gate = row_gate
+//             of the row (1 when row_gate is null)
+//   kDz       A = upstream-gradient rows gathered by row_token; out holds the
+//             pre-activation z on entry and gets gate * C * act'(z) (in place)
+enum GemmMode { kUp = 0, kDown = 1, kDz = 2, kUpTrain = 3 };
+template <int MODE>
+struct ModeOf {
+  static constexpr bool gather = MODE != kDown;
+  static constexpr bool gated = MODE == kDown || MODE == kDz;
+  static constexpr bool out_f32 = MODE == kDown;
+  static constexpr bool fwd_act = MODE == kUp || MODE == kUpTrain;
+};
+
 struct GemmArgs {
   const RowTile* tiles;
   const int32_t* ntiles;
@@ -95,7 +86,8 @@ struct GemmArgs {
   const void* bias_sh;   // shared [Ns] or NULL
   int N, K, Ns, Ks;
   int n_tiles_n;         // N tiles per row tile (over max(N, Ns))
-  void* out;             // up: H (T) ; down: y_rows (float)
+  void* out;             // up: H (T) ; down: y_rows (float); dz: z in, dz out (T)
+  void* aux;             // up (train): the pre-activations (T), same layout as out
   int64_t ldo;
   int act;
 };
@@ -121,9 +113,10 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int pid, int tota
 // Generic kernel: any K that is a multiple of 8 (bf16) or 4 (fp32); tiles are
 // staged through registers with zero fill beyond K and beyond the tile rows.
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool UP>
+template <typename T, int BM, int BN, int BK, int WM, int WN, int MODE>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
   using M = Mfma<T>;
+  using MD = ModeOf<MODE>;
   constexpr int NT = WM * WN * 64;
   constexpr int CH = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int LDK = BK + CH;        // padded LDS row (breaks bank conflicts)
@@ -158,9 +151,9 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  if (!UP) {
+  if constexpr (MD::gated) {
     for (int m = tid; m < BM; m += NT) {
-      gate_s[m] = m < rows ? a.row_gate[row0 + m] : 0.f;
+      gate_s[m] = m < rows ? (a.row_gate ? a.row_gate[row0 + m] : 1.f) : 0.f;
     }
   }
 
@@ -174,7 +167,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
     aoff[i] = r * LDK + akc[i];
     asrc[i] = nullptr;
     if (r < rows) {
-      const int64_t arow = UP ? static_cast<int64_t>(a.row_token[row0 + r]) : (row0 + r);
+      const int64_t arow = MD::gather ? static_cast<int64_t>(a.row_token[row0 + r]) : (row0 + r);
       asrc[i] = static_cast<const T*>(a.A) + arow * a.lda;
     }
   }
@@ -251,9 +244,15 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
         if (m >= rows) continue;
         const float z = acc[i][j][q] + bv;
         const int64_t o = static_cast<int64_t>(row0 + m) * a.ldo + n;
-        if (UP) {
+        if constexpr (MD::fwd_act) {
           const float h = (a.act == MOE_ACT_RELU) ? fmaxf(z, 0.f) : gelu_erf(z);
           static_cast<T*>(a.out)[o] = from_f32<T>(h);
+          if constexpr (MODE == kUpTrain) static_cast<T*>(a.aux)[o] = from_f32<T>(z);
+        } else if constexpr (MODE == kDz) {
+          T* zp = static_cast<T*>(a.out) + o;
+          const float pre = to_f32<T>(*zp);
+          const float da = (a.act == MOE_ACT_RELU) ? (pre > 0.f ? 1.f : 0.f) : gelu_erf_grad(pre);
+          *zp = from_f32<T>(gate_s[m] * z * da);
         } else {
           static_cast<float*>(a.out)[o] = gate_s[m] * z;
         }
@@ -319,8 +318,9 @@ __device__ __forceinline__ void sched_steps() {
 // next tile (its token rows, its gates) is already loaded; after the K loop
 // the next tile's first stages are issued before tile t's epilogue runs, so
 // load latency hides under the epilogue instead of idling the CU.
-template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, bool UP>
+template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int MODE>
 __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(GemmArgs a) {
+  using MD = ModeOf<MODE>;
   constexpr int NW = WM * WN;
   constexpr int NT = NW * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
   // token row (up-projection) or H row (down-projection) behind A row r
   auto arow_of = [&](const Tile& c, int r) -> int {
     const int rr = min(r, c.rows - 1);
-    return UP ? a.row_token[c.row0 + rr] : c.row0 + rr;
+    return MD::gather ? a.row_token[c.row0 + rr] : c.row0 + rr;
   };
   // Load instruction j of this wave fills tile rows (wave + j NW) RPI ...; the
   // first JA instructions hold A rows, the rest B rows.  Sources are kept as
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     return static_cast<uint32_t>(nn) * static_cast<uint32_t>(c.K * 2) + chunk * 16;
   };
   auto gate_of = [&](const Tile& c, int m) -> float {
-    return m < c.rows ? a.row_gate[c.row0 + m] : 0.f;
+    return m < c.rows ? (a.row_gate ? a.row_gate[c.row0 + m] : 1.f) : 0.f;
   };
 
   Tile cur = decode(t);
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
 #pragma unroll
   for (int j = 0; j < JPW; ++j)
     src[j] = j < JA ? a_off(j, arow_of(cur, (wave + j * NW) * RPI + lr)) : b_off(cur, j);
-  if (!UP) {
+  if constexpr (MD::gated) {
 #pragma unroll
     for (int g = 0; g < GPT; ++g)
       if (tid + g * NT < BM) gate_s[0][tid + g * NT] = gate_of(cur, tid + g * NT);
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
         // next tile's token rows and gates: loaded now, used after the K loop
 #pragma unroll
         for (int j = 0; j < JA; ++j) ntok[j] = arow_of(nxt, (wave + j * NW) * RPI + lr);
-        if (!UP) {
+        if constexpr (MD::gated) {
 #pragma unroll
           for (int g = 0; g < GPT; ++g)
             if (tid + g * NT < BM) ngate[g] = gate_of(nxt, tid + g * NT);
@@ -529,7 +529,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
 #pragma unroll
       for (int p = 0; p < NS - 1; ++p)
         if (p < KTn) issue(p, p * BK);
-      if (!UP) {
+      if constexpr (MD::gated) {
 #pragma unroll
         for (int g = 0; g < GPT; ++g)
           if (tid + g * NT < BM) gate_s[gb ^ 1][tid + g * NT] = ngate[g];
@@ -547,9 +547,12 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
       const int n = cur.n0 + ncol[j];
       bv[j] = (cur.bias && n < cur.N) ? bf16_to_f32(cur.bias[n].bits) : 0.f;
     }
-    constexpr int OE = UP ? 2 : 4;  // output element bytes
+    constexpr int OE = MD::out_f32 ? 4 : 2;  // output element bytes
     char* obase = static_cast<char*>(a.out) +
                   (static_cast<int64_t>(cur.row0) * a.ldo + cur.n0) * OE;
+    char* xbase = MODE == kUpTrain ? static_cast<char*>(a.aux) +
+                                         (static_cast<int64_t>(cur.row0) * a.ldo + cur.n0) * OE
+                                   : nullptr;
     const uint32_t ldo = static_cast<uint32_t>(a.ldo);
     auto epilogue = [&](auto checked, auto relu) {
       constexpr bool CHK = decltype(checked)::value;
@@ -561,15 +564,22 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
           const int m = wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
           if (CHK && m >= cur.rows) continue;
           const uint32_t orow = static_cast<uint32_t>(m) * ldo;
-          const float g = UP ? 1.f : gate_s[gb][m];
+          const float g = MD::gated ? gate_s[gb][m] : 1.f;
 #pragma unroll
           for (int j = 0; j < NI; ++j) {
             if (CHK && cur.n0 + ncol[j] >= cur.N) continue;
             const float z = acc[i][j][q] + bv[j];
             const uint32_t off = (orow + static_cast<uint32_t>(ncol[j])) * OE;
-            if constexpr (UP) {
+            if constexpr (MD::fwd_act) {
               const float h = RELU ? fmaxf(z, 0.f) : gelu_erf(z);
               *reinterpret_cast<uint16_t*>(obase + off) = f32_to_bf16(h);
+              if constexpr (MODE == kUpTrain)
+                *reinterpret_cast<uint16_t*>(xbase + off) = f32_to_bf16(z);
+            } else if constexpr (MODE == kDz) {
+              uint16_t* zp = reinterpret_cast<uint16_t*>(obase + off);
+              const float pre = bf16_to_f32(*zp);
+              const float da = RELU ? (pre > 0.f ? 1.f : 0.f) : gelu_erf_grad(pre);
+              *zp = f32_to_bf16(g * z * da);
             } else {
               *reinterpret_cast<float*>(obase + off) = g * z;
             }
@@ -580,7 +590,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
       }
     };
     const bool full = cur.rows == BM && cur.n0 + BN <= cur.N;
-    if (UP && a.act == MOE_ACT_RELU) {
+    if ((MD::fwd_act || MODE == kDz) && a.act == MOE_ACT_RELU) {
       if (full) epilogue(std::false_type{}, std::true_type{});
       else epilogue(std::true_type{}, std::true_type{});
     } else {
@@ -635,6 +645,7 @@ static GemmArgs up_args(const FfnArgs& f, int BN) {
   u.Ks = f.d;
   u.n_tiles_n = static_cast<int>(ceil_div(ldh, BN));
   u.out = f.H;
+  u.aux = f.Z;
   u.ldo = ldh;
   u.act = f.act;
   return u;
@@ -656,20 +667,22 @@ static GemmArgs down_args(const FfnArgs& f, int BN) {
   dn.n_tiles_n = static_cast<int>(ceil_div(f.d, BN));
   dn.out = f.y_rows;
   dn.ldo = f.d;
+  // the input-gradient pass multiplies by no gate (the gate sits in dz)
+  if (f.pass == kPassDgrad) dn.row_gate = nullptr;
   return dn;
 }
 
-template <typename T, int BM, int BNU, int BND, int BK, int WM, int WN>
+template <typename T, int BM, int BNU, int BND, int BK, int WM, int WN, int M1>
 static void run_generic(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const GemmArgs u = up_args(f, BNU);
   const int64_t gu = gp.tiles_max * u.n_tiles_n;
   if (gu > 0)
-    grouped_gemm_kernel<T, BM, BNU, BK, WM, WN, true>
+    grouped_gemm_kernel<T, BM, BNU, BK, WM, WN, M1>
         <<<static_cast<unsigned>(gu), WM * WN * 64, 0, st>>>(u);
   const GemmArgs dn = down_args(f, BND);
   const int64_t gd = gp.tiles_max * dn.n_tiles_n;
   if (gd > 0)
-    grouped_gemm_kernel<T, BM, BND, BK, WM, WN, false>
+    grouped_gemm_kernel<T, BM, BND, BK, WM, WN, kDown>
         <<<static_cast<unsigned>(gd), WM * WN * 64, 0, st>>>(dn);
 }
 
@@ -684,10 +697,10 @@ static int cu_count() {
 
 // Persistent launch: as many blocks as can be resident, capped by the tile
 // count; otherwise one block per tile.
-template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, bool UP>
+template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int MODE>
 static void launch_dma(const GemmArgs& g, int64_t tiles, hipStream_t st) {
   if (tiles <= 0) return;
-  auto kern = grouped_gemm_dma_kernel<BM, BN, BK, NS, WM, WN, OCC, PERSIST, UP>;
+  auto kern = grouped_gemm_dma_kernel<BM, BN, BK, NS, WM, WN, OCC, PERSIST, MODE>;
   const size_t lds = static_cast<size_t>(NS) * (BM + BN) * BK * 2;
   static int per_cu = [&] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -703,12 +716,30 @@ static void launch_dma(const GemmArgs& g, int64_t tiles, hipStream_t st) {
   kern<<<static_cast<unsigned>(grid), WM * WN * 64, lds, st>>>(g);
 }
 
-template <int BM, int BNU, int BND, int BK, int NS, int WM, int WN, int OCC, int PERSIST>
+template <int BM, int BNU, int BND, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int M1>
 static void run_dma(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const GemmArgs u = up_args(f, BNU);
-  launch_dma<BM, BNU, BK, NS, WM, WN, OCC, PERSIST, true>(u, gp.tiles_max * u.n_tiles_n, st);
+  launch_dma<BM, BNU, BK, NS, WM, WN, OCC, PERSIST, M1>(u, gp.tiles_max * u.n_tiles_n, st);
   const GemmArgs dn = down_args(f, BND);
-  launch_dma<BM, BND, BK, NS, WM, WN, OCC, PERSIST, false>(dn, gp.tiles_max * dn.n_tiles_n, st);
+  launch_dma<BM, BND, BK, NS, WM, WN, OCC, PERSIST, kDown>(dn, gp.tiles_max * dn.n_tiles_n, st);
+}
+
+// The two GEMMs of one pass over the grouped rows; M1 is the first GEMM's mode.
+template <int M1>
+static void run_pass(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
+  switch (gp.shape) {
+    case kGemmF32: run_generic<float, 64, 64, 64, 32, 2, 2, M1>(gp, f, st); break;
+    case kGemmBf16Large: run_generic<bf16, 128, 128, 128, 64, 2, 2, M1>(gp, f, st); break;
+    case kGemmBf16Mid: run_generic<bf16, 64, 128, 128, 64, 1, 4, M1>(gp, f, st); break;
+    case kGemmBf16Small: run_generic<bf16, 32, 128, 128, 64, 1, 4, M1>(gp, f, st); break;
+#define MOE_RUN_DMA(C) \
+  run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN, C.OCC, C.PERSIST, M1>(gp, f, st)
+    case kGemmDmaLarge: MOE_RUN_DMA(kDmaLarge); break;
+    case kGemmDmaMid: MOE_RUN_DMA(kDmaMid); break;
+    case kGemmDmaSmall: MOE_RUN_DMA(kDmaSmall); break;
+    default: MOE_RUN_DMA(kDmaSkinny); break;
+#undef MOE_RUN_DMA
+  }
 }
 
 hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
@@ -718,18 +749,10 @@ hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
                                                   f.row_gates ? 0 : f.k, f.row_token,
                                                   f.row_slot, f.topk_w, f.tiles, f.ntiles,
                                                   f.row_gate);
-  switch (gp.shape) {
-    case kGemmF32: run_generic<float, 64, 64, 64, 32, 2, 2>(gp, f, st); break;
-    case kGemmBf16Large: run_generic<bf16, 128, 128, 128, 64, 2, 2>(gp, f, st); break;
-    case kGemmBf16Mid: run_generic<bf16, 64, 128, 128, 64, 1, 4>(gp, f, st); break;
-    case kGemmBf16Small: run_generic<bf16, 32, 128, 128, 64, 1, 4>(gp, f, st); break;
-#define MOE_RUN_DMA(C) \
-  run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN, C.OCC, C.PERSIST>(gp, f, st)
-    case kGemmDmaLarge: MOE_RUN_DMA(kDmaLarge); break;
-    case kGemmDmaMid: MOE_RUN_DMA(kDmaMid); break;
-    case kGemmDmaSmall: MOE_RUN_DMA(kDmaSmall); break;
-    default: MOE_RUN_DMA(kDmaSkinny); break;
-#undef MOE_RUN_DMA
+  switch (f.pass) {
+    case kPassForward: run_pass<kUp>(gp, f, st); break;
+    case kPassForwardTrain: run_pass<kUpTrain>(gp, f, st); break;
+    default: run_pass<kDz>(gp, f, st); break;
   }
   return hipGetLastError();
 }

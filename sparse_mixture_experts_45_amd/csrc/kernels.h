@@ -48,6 +48,14 @@ struct GemmPlan {
   int64_t tiles_max;  // upper bound on row tiles over all groups
 };
 
+// Passes of the grouped-GEMM pair.  kPassDgrad is the input-gradient pass of
+// the backward, run with the forward's argument roles re-bound: x = dy
+// (gathered), W1 = W2 transposed [E, F, d], W2 = W1 transposed [E, d, F]
+// (likewise the shared expert's), no biases, Z = the forward's pre-activations
+// (overwritten with dz = gate * (dy W2) * act'(z)), y_rows = dz W1 per row
+// (fp32, no gate).
+enum { kPassForward = 0, kPassForwardTrain = 1, kPassDgrad = 2 };
+
 struct FfnArgs {
   int64_t T;
   int d, F, E, k, Fs, act, dtype;
@@ -62,6 +70,9 @@ struct FfnArgs {
   float* row_gate;   // [rows_max]
   int tiles_ready;   // tiles, ntiles and row_gate already written by the dispatch
   int row_gates;     // topk_w holds one gate per routed row (expert choice)
+  int pass;          // kPassForward, kPassForwardTrain (also keeps z in Z) or
+                     // kPassDgrad (the roles above)
+  void* Z;           // [rows_max, max(F, Fs)] pre-activations (train / dgrad)
 };
 
 // Everything the single-block dispatch reads and writes.
@@ -117,6 +128,45 @@ hipError_t launch_combine_ec(int64_t T, int d, int E, int Ce, int shared, int dt
                              void* y, hipStream_t st);
 
 hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& a, hipStream_t st);
+
+// Backward (token choice).  moe_backward enqueues, in order: kBwdWeights (the
+// transposed expert weights), kBwdRouter (gate gradients, the balance term,
+// router-score gradients dl, dW_g and db_g), the input-gradient GEMM pass
+// (launch_ffn with kPassDgrad), kBwdDx (dx), kBwdExpertWeights (transposed
+// activations, expert weight and bias gradients).
+enum { kBwdWeights = 0, kBwdRouter = 1, kBwdDx = 2, kBwdExpertWeights = 3 };
+struct BwdArgs {
+  int64_t T;
+  int d, F, E, k, Fs, dtype, renorm, nb;
+  float alpha;                  // coefficient of the balance term
+  const void *x, *dy;           // [T, d] layer dtype
+  const float* Wg;              // [E, d]
+  const void *W1, *W2, *Ws1, *Ws2;
+  void *W1T, *W2T, *Ws1T, *Ws2T;  // transposed weights [E, d, F], [E, F, d], [d, Fs], [Fs, d]
+  const float* probs;           // [T, E] the forward's softmax
+  const int32_t* topk_idx;      // [T, k]
+  const float* topk_w;          // [T, k]
+  const int32_t* inv;           // [T, k] row of each pair, -1 when dropped
+  const int32_t *offsets, *row_token;  // the forward's grouping
+  const float* row_gate;        // [rows] gate of each row (1 for shared rows)
+  const double* stat_part;      // [nb, E] the gate's per-block probability sums
+  const float* y_rows;          // [rows, d] the forward's gated expert outputs
+  float *dg, *dl, *aux_dp;      // scratch [T, k], [T, E], [E]
+  float* wg_part;               // scratch [wg_split, E, d + 1]
+  int wg_split;
+  int64_t wg_chunk;             // tokens per split
+  const float* dX;              // [rows, d] dz W1 per row (the dgrad pass's y_rows)
+  const void *Z, *H;            // [rows, ldh] dz (after the dgrad pass) and h
+  int32_t* poff;                // [G + 1] padded column offsets
+  int64_t Rp;                   // columns of the transposed buffers (multiple of 64)
+  void *ZT, *HT, *XT, *DT;      // [ldh, Rp], [ldh, Rp], [d, Rp], [d, Rp]
+  // outputs, NULL = not wanted
+  void* dx;
+  float *dWg, *dbg;
+  void *dW1, *db1, *dW2, *db2, *dWs1, *dbs1, *dWs2, *dbs2;
+};
+hipError_t launch_backward(const BwdArgs& b, int part, hipStream_t st);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 
 hipError_t launch_combine(int64_t T, int d, int E, int k, int shared, int dtype,
                           const float* y_rows, const int32_t* inv, const int32_t* offsets,

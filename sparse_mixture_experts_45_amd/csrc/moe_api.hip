@@ -16,6 +16,11 @@ struct Layout {
   int ec_W;          // 32-token words of the expert-choice bitmaps
   size_t part, stat, hist, base, topk_idx, topk_w, counts, kept, offsets, row_token, row_slot,
       inv, tiles, ntiles, row_gate, probsT, sel, pre, H, y_rows, total;
+  // training: what the forward keeps for the backward, and the backward's scratch
+  bool train;
+  int wg_split;
+  int64_t wg_chunk, Rp;
+  size_t Z, probs, dg, dl, aux_dp, wg_part, W1T, W2T, Ws1T, Ws2T, poff, ZT, HT, XT, DT;
 };
 
 bool expert_choice(const moe_config* c) { return c->routing == MOE_ROUTE_EXPERT; }
@@ -135,8 +140,9 @@ RoutePlan route_plan(const moe_config* c) {
   return p;
 }
 
-Layout layout(const moe_config* c) {
+Layout layout(const moe_config* c, bool train = false) {
   Layout L{};
+  L.train = train;
   L.rp = route_plan(c);
   L.gp = gemm_plan(c);
   const int64_t T = c->T, E = c->n_experts, k = L.rp.k;
@@ -173,6 +179,31 @@ Layout layout(const moe_config* c) {
   L.pre = take(sizeof(int32_t) * E * L.ec_W);
   L.H = take(elt * L.rows_max * ldh);
   L.y_rows = take(sizeof(float) * L.rows_max * c->d_model);
+  if (train) {
+    const int64_t d = c->d_model, F = c->d_ff, Fs = c->shared_d_ff;
+    const int64_t G = E + (Fs > 0 ? 1 : 0);
+    L.Z = take(elt * L.rows_max * ldh);
+    L.probs = take(sizeof(float) * T * E);
+    L.dg = take(sizeof(float) * T * k);
+    L.dl = take(sizeof(float) * T * E);
+    L.aux_dp = take(sizeof(float) * E);
+    // router weight gradient: enough token chunks for ~512 blocks
+    const int64_t col_blocks = ceil_div(d + 1, 256) * ceil_div(E, 8);
+    L.wg_split = static_cast<int>(std::max<int64_t>(
+        1, std::min<int64_t>(ceil_div(512, col_blocks), ceil_div(std::max<int64_t>(T, 1), 64))));
+    L.wg_chunk = ceil_div(std::max<int64_t>(T, 1), L.wg_split);
+    L.wg_part = take(sizeof(float) * L.wg_split * E * (d + 1));
+    L.W1T = take(elt * E * F * d);
+    L.W2T = take(elt * E * d * F);
+    L.Ws1T = take(elt * Fs * d);
+    L.Ws2T = take(elt * d * Fs);
+    L.poff = take(sizeof(int32_t) * (G + 1));
+    L.Rp = static_cast<int64_t>(align_up(L.rows_max + 64 * G, 64));
+    L.ZT = take(elt * ldh * L.Rp);
+    L.HT = take(elt * ldh * L.Rp);
+    L.XT = take(elt * d * L.Rp);
+    L.DT = take(elt * d * L.Rp);
+  }
   L.total = o;
   return L;
 }
@@ -199,7 +230,7 @@ moe_status check_weights(const moe_config* c, const moe_weights* w) {
 moe_status run_ffn(const moe_config* c, const Layout& L, const void* x, const moe_weights* w,
                    const int32_t* offsets, const int32_t* row_token, const int32_t* row_slot,
                    const float* topk_w, float* y_rows, void* ws, hipStream_t st,
-                   bool tiles_ready = false) {
+                   bool tiles_ready = false, int pass = kPassForward) {
   FfnArgs f{};
   f.T = c->T;
   f.d = c->d_model;
@@ -229,6 +260,8 @@ moe_status run_ffn(const moe_config* c, const Layout& L, const void* x, const mo
   f.row_gate = reinterpret_cast<float*>(at(ws, L.row_gate));
   f.tiles_ready = tiles_ready ? 1 : 0;
   f.row_gates = expert_choice(c) ? 1 : 0;
+  f.pass = pass;
+  f.Z = pass == kPassForwardTrain ? at(ws, L.Z) : nullptr;
   return hip_status(launch_ffn(L.gp, f, st));
 }
 
@@ -280,6 +313,86 @@ moe_status forward_expert_choice(const moe_config* c, const Layout& L, const moe
     return s;
   return hip_status(launch_combine_ec(c->T, c->d_model, c->n_experts, a.Ce, a.shared, c->dtype,
                                       y_rows, a.sel, a.pre, y, st));
+}
+
+// Token-choice layer (train: also keeps the softmax and the pre-activations
+// for moe_backward).
+moe_status forward_token(const moe_config* cfg, const Layout& L, const moe_weights* w,
+                         const void* x, void* y, const moe_stats& o, void* ws, hipStream_t st) {
+  moe_status s;
+  // training keeps the routing in the workspace (copied out when asked for)
+  int32_t* topk_idx = o.topk_idx && !L.train ? o.topk_idx
+                                             : reinterpret_cast<int32_t*>(at(ws, L.topk_idx));
+  float* topk_w = o.topk_w && !L.train ? o.topk_w : reinterpret_cast<float*>(at(ws, L.topk_w));
+  int32_t* counts = o.counts ? o.counts : reinterpret_cast<int32_t*>(at(ws, L.counts));
+  int32_t* kept = o.kept ? o.kept : reinterpret_cast<int32_t*>(at(ws, L.kept));
+  int32_t* offsets = reinterpret_cast<int32_t*>(at(ws, L.offsets));
+  int32_t* row_token = reinterpret_cast<int32_t*>(at(ws, L.row_token));
+  int32_t* row_slot = reinterpret_cast<int32_t*>(at(ws, L.row_slot));
+  int32_t* inv = reinterpret_cast<int32_t*>(at(ws, L.inv));
+  int32_t* hist = reinterpret_cast<int32_t*>(at(ws, L.hist));
+  float* y_rows = reinterpret_cast<float*>(at(ws, L.y_rows));
+
+  double* stat_part = reinterpret_cast<double*>(at(ws, L.stat));
+  // small batches: the whole dispatch (and the load statistics) in one block
+  const bool one = dispatch_one_block(L.rp.nb, cfg->n_experts);
+  if ((s = hip_status(launch_router(L.rp, x, cfg->dtype, w->Wg, w->bg,
+                                    reinterpret_cast<float*>(at(ws, L.part)), topk_idx, topk_w,
+                                    L.train ? reinterpret_cast<float*>(at(ws, L.probs)) : nullptr,
+                                    stat_part, hist, one ? nullptr : o.mean_prob,
+                                    one ? nullptr : o.balance, st))) != MOE_OK)
+    return s;
+  if (L.train && cfg->T > 0) {
+    const size_t n = static_cast<size_t>(cfg->T) * cfg->top_k * 4;
+    if (o.topk_idx &&
+        (s = hip_status(hipMemcpyAsync(o.topk_idx, topk_idx, n, hipMemcpyDeviceToDevice, st))) !=
+            MOE_OK)
+      return s;
+    if (o.topk_w &&
+        (s = hip_status(hipMemcpyAsync(o.topk_w, topk_w, n, hipMemcpyDeviceToDevice, st))) !=
+            MOE_OK)
+      return s;
+  }
+  // the gate kernel already wrote the per-block expert histogram
+  if (one) {
+    DispatchArgs d{};
+    d.topk_idx = topk_idx;
+    d.topk_w = topk_w;
+    d.hist = hist;
+    d.stat_part = stat_part;
+    d.T = cfg->T;
+    d.nb = L.rp.nb;
+    d.E = cfg->n_experts;
+    d.k = cfg->top_k;
+    d.capacity = cfg->capacity;
+    d.shared = cfg->shared_d_ff > 0;
+    d.BM = L.gp.BM;
+    d.counts = counts;
+    d.kept = kept;
+    d.offsets = offsets;
+    d.row_token = row_token;
+    d.row_slot = row_slot;
+    d.inv = inv;
+    d.row_gate = reinterpret_cast<float*>(at(ws, L.row_gate));
+    d.tiles = reinterpret_cast<RowTile*>(at(ws, L.tiles));
+    d.ntiles = reinterpret_cast<int32_t*>(at(ws, L.ntiles));
+    d.mean_prob = o.mean_prob;
+    d.balance = o.balance;
+    d.cv2 = o.cv2;
+    if ((s = hip_status(launch_dispatch_one_block(d, st))) != MOE_OK) return s;
+  } else if ((s = hip_status(launch_dispatch(cfg->T, cfg->n_experts, cfg->top_k, cfg->capacity,
+                                             cfg->shared_d_ff > 0, L.rp.nb, topk_idx, false,
+                                             hist, reinterpret_cast<int32_t*>(at(ws, L.base)),
+                                             counts, kept, offsets, row_token, row_slot, inv,
+                                             o.cv2, st))) != MOE_OK) {
+    return s;
+  }
+  if (cfg->T == 0) return MOE_OK;
+  if ((s = run_ffn(cfg, L, x, w, offsets, row_token, row_slot, topk_w, y_rows, ws, st, one,
+                   L.train ? kPassForwardTrain : kPassForward)) != MOE_OK)
+    return s;
+  return hip_status(launch_combine(cfg->T, cfg->d_model, cfg->n_experts, cfg->top_k,
+                                   cfg->shared_d_ff > 0, cfg->dtype, y_rows, inv, offsets, y, st));
 }
 
 }  // namespace
@@ -372,66 +485,152 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     return forward_expert_choice(cfg, L, w, x, y, o, ws, st);
   }
   if (o.ec_idx || o.ec_w) return MOE_ERR_INVALID_ARG;
+  return forward_token(cfg, L, w, x, y, o, ws, st);
+}
 
-  int32_t* topk_idx = o.topk_idx ? o.topk_idx : reinterpret_cast<int32_t*>(at(ws, L.topk_idx));
-  float* topk_w = o.topk_w ? o.topk_w : reinterpret_cast<float*>(at(ws, L.topk_w));
-  int32_t* counts = o.counts ? o.counts : reinterpret_cast<int32_t*>(at(ws, L.counts));
-  int32_t* kept = o.kept ? o.kept : reinterpret_cast<int32_t*>(at(ws, L.kept));
-  int32_t* offsets = reinterpret_cast<int32_t*>(at(ws, L.offsets));
-  int32_t* row_token = reinterpret_cast<int32_t*>(at(ws, L.row_token));
-  int32_t* row_slot = reinterpret_cast<int32_t*>(at(ws, L.row_slot));
-  int32_t* inv = reinterpret_cast<int32_t*>(at(ws, L.inv));
-  int32_t* hist = reinterpret_cast<int32_t*>(at(ws, L.hist));
-  float* y_rows = reinterpret_cast<float*>(at(ws, L.y_rows));
+size_t moe_train_workspace_bytes(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK || expert_choice(cfg)) return 0;
+  return layout(cfg, true).total;
+}
 
-  double* stat_part = reinterpret_cast<double*>(at(ws, L.stat));
-  // small batches: the whole dispatch (and the load statistics) in one block
-  const bool one = dispatch_one_block(L.rp.nb, cfg->n_experts);
-  if ((s = hip_status(launch_router(L.rp, x, cfg->dtype, w->Wg, w->bg,
-                                    reinterpret_cast<float*>(at(ws, L.part)), topk_idx, topk_w,
-                                    nullptr, stat_part, hist, one ? nullptr : o.mean_prob,
-                                    one ? nullptr : o.balance, st))) != MOE_OK)
-    return s;
-  // the gate kernel already wrote the per-block expert histogram
-  if (one) {
-    DispatchArgs d{};
-    d.topk_idx = topk_idx;
-    d.topk_w = topk_w;
-    d.hist = hist;
-    d.stat_part = stat_part;
-    d.T = cfg->T;
-    d.nb = L.rp.nb;
-    d.E = cfg->n_experts;
-    d.k = cfg->top_k;
-    d.capacity = cfg->capacity;
-    d.shared = cfg->shared_d_ff > 0;
-    d.BM = L.gp.BM;
-    d.counts = counts;
-    d.kept = kept;
-    d.offsets = offsets;
-    d.row_token = row_token;
-    d.row_slot = row_slot;
-    d.inv = inv;
-    d.row_gate = reinterpret_cast<float*>(at(ws, L.row_gate));
-    d.tiles = reinterpret_cast<RowTile*>(at(ws, L.tiles));
-    d.ntiles = reinterpret_cast<int32_t*>(at(ws, L.ntiles));
-    d.mean_prob = o.mean_prob;
-    d.balance = o.balance;
-    d.cv2 = o.cv2;
-    if ((s = hip_status(launch_dispatch_one_block(d, st))) != MOE_OK) return s;
-  } else if ((s = hip_status(launch_dispatch(cfg->T, cfg->n_experts, cfg->top_k, cfg->capacity,
-                                             cfg->shared_d_ff > 0, L.rp.nb, topk_idx, false,
-                                             hist, reinterpret_cast<int32_t*>(at(ws, L.base)),
-                                             counts, kept, offsets, row_token, row_slot, inv,
-                                             o.cv2, st))) != MOE_OK) {
-    return s;
+moe_status moe_forward_train(const moe_config* cfg, const moe_weights* w, const void* x, void* y,
+                             moe_stats* stats, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (expert_choice(cfg)) return MOE_ERR_UNSUPPORTED;
+  if ((s = check_weights(cfg, w)) != MOE_OK) return s;
+  if (cfg->T > 0 && (!x || !y || !aligned16(x) || !aligned16(y))) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(cfg, true);
+  if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
+  moe_stats none{};
+  const moe_stats& o = stats ? *stats : none;
+  if (o.ec_idx || o.ec_w) return MOE_ERR_INVALID_ARG;
+  return forward_token(cfg, L, w, x, y, o, ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x,
+                        const void* dy, float aux_coef, moe_grads* grads, void* ws,
+                        size_t ws_bytes, void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (expert_choice(cfg)) return MOE_ERR_UNSUPPORTED;
+  if ((s = check_weights(cfg, w)) != MOE_OK) return s;
+  if (!grads) return MOE_ERR_INVALID_ARG;
+  const moe_grads& g = *grads;
+  if (cfg->T > 0 && (!x || !dy || !aligned16(x) || !aligned16(dy))) return MOE_ERR_INVALID_ARG;
+  if (g.dx && !aligned16(g.dx)) return MOE_ERR_INVALID_ARG;
+  if (cfg->shared_d_ff == 0 && (g.dWs1 || g.dbs1 || g.dWs2 || g.dbs2)) return MOE_ERR_INVALID_ARG;
+  if (!(aux_coef == aux_coef)) return MOE_ERR_INVALID_ARG;  // NaN
+  const Layout L = layout(cfg, true);
+  if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t T = cfg->T, d = cfg->d_model, F = cfg->d_ff, E = cfg->n_experts;
+  const int64_t Fs = cfg->shared_d_ff;
+  const size_t elt = cfg->dtype == MOE_BF16 ? 2 : 4;
+  if (T == 0) {  // no tokens: every parameter gradient is zero
+    // (every size is a whole number of 4-byte words: d, F and Fs are multiples of 8)
+    const size_t e = static_cast<size_t>(E), dd = static_cast<size_t>(d);
+    const size_t ff = static_cast<size_t>(F), fs = static_cast<size_t>(Fs);
+    const struct {
+      void* p;
+      size_t n;
+    } z[] = {{g.dWg, 4 * e * dd},        {g.dbg, 4 * e},         {g.dW1, elt * e * ff * dd},
+             {g.db1, elt * e * ff},       {g.dW2, elt * e * dd * ff}, {g.db2, elt * e * dd},
+             {g.dWs1, elt * fs * dd},     {g.dbs1, elt * fs},     {g.dWs2, elt * dd * fs},
+             {g.dbs2, fs > 0 ? elt * dd : 0}};
+    for (const auto& q : z)
+      if (q.p && q.n && (s = hip_status(launch_zero(q.p, q.n, st))) != MOE_OK) return s;
+    return MOE_OK;
   }
-  if (cfg->T == 0) return MOE_OK;
-  if ((s = run_ffn(cfg, L, x, w, offsets, row_token, row_slot, topk_w, y_rows, ws, st, one)) !=
-      MOE_OK)
-    return s;
-  return hip_status(launch_combine(cfg->T, cfg->d_model, cfg->n_experts, cfg->top_k,
-                                   cfg->shared_d_ff > 0, cfg->dtype, y_rows, inv, offsets, y, st));
+  BwdArgs b{};
+  b.T = T;
+  b.d = cfg->d_model;
+  b.F = cfg->d_ff;
+  b.E = cfg->n_experts;
+  b.k = cfg->top_k;
+  b.Fs = cfg->shared_d_ff;
+  b.dtype = cfg->dtype;
+  b.renorm = cfg->renormalize;
+  b.nb = L.rp.nb;
+  b.alpha = aux_coef;
+  b.x = x;
+  b.dy = dy;
+  b.Wg = w->Wg;
+  b.W1 = w->W1;
+  b.W2 = w->W2;
+  b.Ws1 = w->Ws1;
+  b.Ws2 = w->Ws2;
+  b.W1T = at(ws, L.W1T);
+  b.W2T = at(ws, L.W2T);
+  b.Ws1T = at(ws, L.Ws1T);
+  b.Ws2T = at(ws, L.Ws2T);
+  b.probs = reinterpret_cast<const float*>(at(ws, L.probs));
+  b.topk_idx = reinterpret_cast<const int32_t*>(at(ws, L.topk_idx));
+  b.topk_w = reinterpret_cast<const float*>(at(ws, L.topk_w));
+  b.inv = reinterpret_cast<const int32_t*>(at(ws, L.inv));
+  b.offsets = reinterpret_cast<const int32_t*>(at(ws, L.offsets));
+  b.row_token = reinterpret_cast<const int32_t*>(at(ws, L.row_token));
+  b.row_gate = reinterpret_cast<const float*>(at(ws, L.row_gate));
+  b.stat_part = reinterpret_cast<const double*>(at(ws, L.stat));
+  b.y_rows = reinterpret_cast<const float*>(at(ws, L.y_rows));
+  b.dg = reinterpret_cast<float*>(at(ws, L.dg));
+  b.dl = reinterpret_cast<float*>(at(ws, L.dl));
+  b.aux_dp = reinterpret_cast<float*>(at(ws, L.aux_dp));
+  b.wg_part = reinterpret_cast<float*>(at(ws, L.wg_part));
+  b.wg_split = L.wg_split;
+  b.wg_chunk = L.wg_chunk;
+  b.dX = reinterpret_cast<const float*>(at(ws, L.y_rows));
+  b.Z = at(ws, L.Z);
+  b.H = at(ws, L.H);
+  b.poff = reinterpret_cast<int32_t*>(at(ws, L.poff));
+  b.Rp = L.Rp;
+  b.ZT = at(ws, L.ZT);
+  b.HT = at(ws, L.HT);
+  b.XT = at(ws, L.XT);
+  b.DT = at(ws, L.DT);
+  b.dx = g.dx;
+  b.dWg = g.dWg;
+  b.dbg = g.dbg;
+  b.dW1 = g.dW1;
+  b.db1 = g.db1;
+  b.dW2 = g.dW2;
+  b.db2 = g.db2;
+  b.dWs1 = g.dWs1;
+  b.dbs1 = g.dbs1;
+  b.dWs2 = g.dWs2;
+  b.dbs2 = g.dbs2;
+  if ((s = hip_status(launch_backward(b, kBwdWeights, st))) != MOE_OK) return s;
+  // gate gradients read the forward's expert rows before the dgrad pass reuses them
+  if ((s = hip_status(launch_backward(b, kBwdRouter, st))) != MOE_OK) return s;
+  // input-gradient pass: dz (in place of z) and dz W1 per row (in place of y_rows)
+  FfnArgs f{};
+  f.T = T;
+  f.d = cfg->d_model;
+  f.F = cfg->d_ff;
+  f.E = cfg->n_experts;
+  f.k = cfg->top_k;
+  f.Fs = cfg->shared_d_ff;
+  f.act = cfg->act;
+  f.dtype = cfg->dtype;
+  f.x = dy;
+  f.W1 = b.W2T;
+  f.W2 = b.W1T;
+  f.Ws1 = b.Ws2T;
+  f.Ws2 = b.Ws1T;
+  f.offsets = b.offsets;
+  f.row_token = b.row_token;
+  f.H = at(ws, L.Z);
+  f.y_rows = reinterpret_cast<float*>(at(ws, L.y_rows));
+  f.tiles = reinterpret_cast<RowTile*>(at(ws, L.tiles));
+  f.ntiles = reinterpret_cast<int32_t*>(at(ws, L.ntiles));
+  f.row_gate = reinterpret_cast<float*>(at(ws, L.row_gate));
+  f.tiles_ready = 1;
+  f.pass = kPassDgrad;
+  if ((s = hip_status(launch_ffn(L.gp, f, st))) != MOE_OK) return s;
+  if (g.dx && (s = hip_status(launch_backward(b, kBwdDx, st))) != MOE_OK) return s;
+  if (g.dW1 || g.db1 || g.dW2 || g.db2 || g.dWs1 || g.dbs1 || g.dWs2 || g.dbs2)
+    s = hip_status(launch_backward(b, kBwdExpertWeights, st));
+  return s;
 }
 
 const char* moe_status_string(moe_status s) {

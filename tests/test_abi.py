@@ -126,3 +126,34 @@ def test_expert_choice_config_checks(lib):
     st = moe.moe_stats(ec_idx=fake)
     assert lib.moe_forward(C.byref(ct), C.byref(w), fake, fake, C.byref(st), fake,
                            lib.moe_workspace_bytes(C.byref(ct)), None) == -1
+
+
+def test_training_entry_points_check_arguments(lib):
+    fake = C.c_void_p(0x10000)  # never dereferenced: checks fail first
+    w = moe.moe_weights(Wg=fake, W1=fake, W2=fake)
+    c = cfg()
+    n = lib.moe_train_workspace_bytes(C.byref(c))
+    assert n > lib.moe_workspace_bytes(C.byref(c)) > 0
+    ec = cfg(routing="expert")
+    assert lib.moe_train_workspace_bytes(C.byref(ec)) == 0
+    g = moe.moe_grads(dx=fake)
+    ne = lib.moe_workspace_bytes(C.byref(ec))
+    assert lib.moe_forward_train(C.byref(ec), C.byref(w), fake, fake, None, fake, ne, None) == -2
+    assert lib.moe_backward(C.byref(ec), C.byref(w), fake, fake, C.c_float(0.0), C.byref(g),
+                            fake, ne, None) == -2
+    # missing grads struct, NaN coefficient, shared-expert grads without a shared
+    # expert, misaligned dx, short workspace
+    assert lib.moe_backward(C.byref(c), C.byref(w), fake, fake, C.c_float(0.0), None, fake, n,
+                            None) == -1
+    assert lib.moe_backward(C.byref(c), C.byref(w), fake, fake, C.c_float(float("nan")),
+                            C.byref(g), fake, n, None) == -1
+    gs = moe.moe_grads(dWs1=fake)
+    assert lib.moe_backward(C.byref(c), C.byref(w), fake, fake, C.c_float(0.0), C.byref(gs),
+                            fake, n, None) == -1
+    gm = moe.moe_grads(dx=C.c_void_p(0x10008))
+    assert lib.moe_backward(C.byref(c), C.byref(w), fake, fake, C.c_float(0.0), C.byref(gm),
+                            fake, n, None) == -1
+    assert lib.moe_backward(C.byref(c), C.byref(w), fake, fake, C.c_float(0.0), C.byref(g),
+                            fake, n - 1, None) == -3
+    assert lib.moe_forward_train(C.byref(c), C.byref(w), fake, fake, None, fake,
+                                 lib.moe_workspace_bytes(C.byref(c)), None) == -3

@@ -1,0 +1,193 @@
+"""GPU parity of the backward pass: moe_forward_train + moe_backward through the
+C-ABI against the fp64 oracle's gradients of sum <dy, y> + alpha * balance.
+
+Small shapes compare every gradient tensor in full and span every GEMM tile
+tier (fp32, bf16 with K not a multiple of 64, the four LDS-DMA tiers), shared
+experts, capacity drops, no renormalisation, k = E, E = 1 and the empty batch.
+Tolerances: fp32 rel-L2 <= 1e-5 per gradient tensor; bf16 rel-L2 <= 1e-2
+(the layer's output tolerances; bf16 layers round dz, h and g dy to bf16 as
+their forward rounds h).  The workload tests check the page-1 and Mixtral
+shapes on sampled tokens and weight entries the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_45_amd as moe
+from moe_synth import LayerShape, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs, workload
+from gpu_common import cfg_of, device_inputs, rel_l2, say, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+F32_REL_L2, BF16_REL_L2 = 1e-5, 1e-2
+
+
+def S(name, **kw):
+    base = dict(name=name, T=300, d=200, F=328, E=7, k=3, dtype="bf16", router_bias="normal")
+    base.update(kw)
+    return LayerShape(**base)
+
+
+def make_dy(shape, seed=13):
+    dy = np.random.default_rng(seed).standard_normal((shape.T, shape.d)).astype(np.float32)
+    if shape.dtype == "bf16":
+        bits = f32_to_bf16_bits(dy)
+        return bits, bf16_bits_to_f32(bits).astype(np.float64)
+    return dy, dy.astype(np.float64)
+
+
+def grad_buffers(shape, names=None):
+    T, d, F, E, Fs = shape.T, shape.d, shape.F, shape.E, shape.Fs
+    dt = torch_dtype(shape)
+    sizes = dict(dx=((T, d), dt), dWg=((E, d), torch.float32), dbg=((E,), torch.float32),
+                 dW1=((E, F, d), dt), db1=((E, F), dt), dW2=((E, d, F), dt), db2=((E, d), dt))
+    if Fs:
+        sizes.update(dWs1=((Fs, d), dt), dbs1=((Fs,), dt), dWs2=((d, Fs), dt), dbs2=((d,), dt))
+    names = names or list(sizes)
+    return {n: torch.full(sizes[n][0], float("nan"), dtype=sizes[n][1], device="cuda")
+            for n in names}
+
+
+def gpu_backward(shape, dev, dy_dev, alpha, names=None):
+    c = cfg_of(shape)
+    ws = moe.train_workspace(c)
+    y = torch.empty((shape.T, shape.d), dtype=torch_dtype(shape), device="cuda")
+    moe.moe_forward_train(c, dev, dev["x"], y, None, ws)
+    g = grad_buffers(shape, names)
+    moe.moe_backward(c, dev, dev["x"], dy_dev, g, aux_coef=alpha, ws=ws)
+    torch.cuda.synchronize()
+    return {n: v.float().cpu().numpy().astype(np.float64) for n, v in g.items()}, y
+
+
+def check(shape, got, want, what):
+    tol = F32_REL_L2 if shape.dtype == "f32" else BF16_REL_L2
+    assert np.all(np.isfinite(got)), what
+    r = rel_l2(got, want)
+    assert r <= tol, (what, r)
+    return r
+
+
+def dy_device(shape, dy_raw):
+    if dy_raw.dtype == np.uint16:
+        return torch.from_numpy(dy_raw.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(dy_raw).cuda()
+
+
+SMALL = [
+    S("f32_shared_capacity", dtype="f32", Fs=136, E=5, k=2, T=130, capacity=40),
+    S("f32_relu_norenorm", dtype="f32", act="relu", renormalize=0),
+    S("bf16_generic_k8", T=257, d=96, F=200, E=9, k=2, Fs=72),
+    S("dma_large", T=800, d=192, F=320, E=2, k=2, Fs=192),
+    S("dma_mid_capacity", T=600, d=192, F=320, E=4, k=2, capacity=260, router_bias="zipf1.1"),
+    S("dma_small_relu", T=300, d=128, F=192, E=4, k=2, act="relu"),
+    S("dma_skinny_many", T=96, d=256, F=128, E=64, k=6, router_bias="none"),
+    S("bf16_k_equals_E", T=90, d=64, F=96, E=4, k=4),
+    S("bf16_one_expert", T=77, d=64, F=64, E=1, k=1),
+    S("bf16_no_expert_bias", T=150, d=128, F=128, E=8, k=2, expert_bias=False,
+      router_bias="none"),
+]
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.7])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: s.name)
+def test_backward_small(shape, alpha):
+    if shape.E == 1 and alpha:
+        pytest.skip("balance is undefined for one expert")
+    say("case", shape, "alpha", alpha)
+    inp = make_inputs(shape, 7)
+    dy_raw, dy64 = make_dy(shape)
+    want = oracle.backward(shape, inp, dy64, alpha)
+    got, _ = gpu_backward(shape, device_inputs(inp), dy_device(shape, dy_raw), alpha)
+    errs = {n: check(shape, got[n], want[n], n) for n in got}
+    # a bias left out (NULL) still has its gradient: the same sum
+    say("  rel-L2", " ".join("%s %.2g" % kv for kv in errs.items()))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_balance_term_only(dtype):
+    """dy = 0: only the balance term acts, so the expert-weight gradients are
+    zero and dx, dW_g, db_g are the balance term's alone."""
+    shape = S("balance_only", dtype=dtype, T=500, d=128, F=192, E=16, k=2, Fs=64)
+    inp = make_inputs(shape, 9)
+    dy = np.zeros((shape.T, shape.d), np.float32)
+    dy_raw = f32_to_bf16_bits(dy) if dtype == "bf16" else dy
+    want = oracle.backward(shape, inp, dy.astype(np.float64), 2.0)
+    got, _ = gpu_backward(shape, device_inputs(inp), dy_device(shape, dy_raw), 2.0)
+    for n in ("dx", "dWg", "dbg"):
+        assert np.any(want[n] != 0.0)
+        # fp32 softmax and statistics in the kernels: 1e-4 relative here
+        r = rel_l2(got[n], want[n])
+        assert r <= (1e-4 if dtype == "f32" else BF16_REL_L2), (n, r)
+    for n in ("dW1", "db1", "dW2", "db2", "dWs1", "dbs1", "dWs2", "dbs2"):
+        assert np.all(got[n] == 0.0), n
+
+
+def test_backward_empty_batch():
+    shape = S("empty", T=0, d=64, F=64, E=4, k=2, Fs=64)
+    inp = make_inputs(shape, 1)
+    got, _ = gpu_backward(shape, device_inputs(inp),
+                          torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), 0.5)
+    for n, v in got.items():
+        assert np.all(v == 0.0), n
+
+
+def test_backward_is_deterministic():
+    shape = S("det", T=400, d=128, F=192, E=8, k=2, Fs=64, capacity=90)
+    inp = make_inputs(shape, 3)
+    dev = device_inputs(inp)
+    dy_raw, _ = make_dy(shape)
+    dyd = dy_device(shape, dy_raw)
+    a, _ = gpu_backward(shape, dev, dyd, 0.3)
+    b, _ = gpu_backward(shape, dev, dyd, 0.3)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_forward_train_output_equals_forward():
+    """The training forward computes the same layer (bit for bit) as moe_forward."""
+    from gpu_common import gpu_forward
+    shape = S("ft", T=500, d=192, F=256, E=8, k=2, Fs=64, capacity=150)
+    inp = make_inputs(shape, 2)
+    dev = device_inputs(inp)
+    ref = gpu_forward(shape, dev)
+    _, y = gpu_backward(shape, dev, dy_device(shape, make_dy(shape)[0]), 0.0, names=["dx"])
+    assert torch.equal(y.view(torch.int16), ref["y_raw"].view(torch.int16))
+
+
+@pytest.mark.parametrize("name,n_tok", [("page1_b4s512", 48), ("mixtral_t4096", 12)])
+def test_backward_workload(name, n_tok):
+    """Full-size shapes: dx on sampled tokens, entries of two experts' weight
+    gradients (and the bias gradients at those entries), and, for page-1, the
+    router gradients from every token's dl."""
+    shape = workload(name)
+    say("workload", shape)
+    inp = make_inputs(shape, 0)
+    dy_raw, dy64 = make_dy(shape, 3)
+    alpha = 0.5
+    rt = oracle.route(shape, inp, with_probs=False)
+    full_router = name == "page1_b4s512"
+    names = ["dx", "dWg", "dbg", "dW1", "db1", "dW2", "db2"]
+    got, _ = gpu_backward(shape, device_inputs(inp), dy_device(shape, dy_raw), alpha, names)
+    toks = np.linspace(0, shape.T - 1, n_tok).astype(np.int64)
+    bt = oracle.backward_tokens(shape, inp, dy64, np.arange(shape.T) if full_router else toks,
+                                alpha, rt=rt)
+    dx_ref = bt["dx"] if not full_router else bt["dx"][toks]
+    r = check(shape, got["dx"][toks], dx_ref, "dx")
+    say("  dx rel-L2 on %d tokens: %.3g" % (len(toks), r))
+    if full_router:
+        x = inp["x"]
+        x64 = bf16_bits_to_f32(x).astype(np.float64) if shape.dtype == "bf16" else x
+        check(shape, got["dWg"], bt["dl"].T @ x64, "dWg")
+        check(shape, got["dbg"], bt["dl"].sum(axis=0), "dbg")
+    rng = np.random.default_rng(1)
+    for e in (0, shape.E - 1):
+        fl = np.sort(rng.choice(shape.F, 16, replace=False))
+        jl = np.sort(rng.choice(shape.d, 16, replace=False))
+        ent = oracle.backward_expert_entries(shape, inp, dy64, e, fl, jl, rt=rt)
+        check(shape, got["dW1"][e][np.ix_(fl, jl)], ent["dW1"], "dW1[%d]" % e)
+        check(shape, got["dW2"][e][np.ix_(jl, fl)], ent["dW2"], "dW2[%d]" % e)
+        check(shape, got["db1"][e][fl], ent["db1"], "db1[%d]" % e)
+        check(shape, got["db2"][e][jl], ent["db2"], "db2[%d]" % e)
+    del got
+    torch.cuda.empty_cache()
