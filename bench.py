@@ -53,6 +53,9 @@ def parse():
                         "copy of known size, then moe_expert_ffn calls")
     p.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="turn the two probe databases into the stored traffic summary")
+    p.add_argument("--backward", action="store_true",
+                   help="time a training step (moe_forward_train + moe_backward with every "
+                        "gradient and the balance term) instead of the forward")
     return p.parse_args()
 
 
@@ -296,6 +299,93 @@ def cpu_baseline(shape, inp, seconds):
                       "MLPs and combine of %s, %.1f s" % (what, dt)}
 
 
+def bench_backward(args):
+    """Training step of the layer: moe_forward_train then moe_backward (all
+    gradients, balance coefficient 0.01), replayed from one HIP graph; the
+    backward alone is timed with events on its stream."""
+    import torch
+    import sparse_mixture_experts_45_amd as moe
+    from moe_synth import make_inputs, to_device, workload
+
+    shape = workload(args.workload)
+    if shape.routing != "token":
+        raise SystemExit("the backward covers token-choice routing only")
+    dev = to_device(make_inputs(shape, args.seed), "cuda")
+    cfg = layer_config(moe, torch, shape)
+    ws = moe.train_workspace(cfg)
+    T, d, F, E, Fs = shape.T, shape.d, shape.F, shape.E, shape.Fs
+    tdt = dev["x"].dtype
+    gen = torch.Generator(device="cuda").manual_seed(args.seed + 1)
+    dy = torch.randn((T, d), generator=gen, device="cuda").to(tdt)
+    y = torch.empty((T, d), dtype=tdt, device="cuda")
+    z = lambda *sh, dt=tdt: torch.empty(sh, dtype=dt, device="cuda")  # noqa: E731
+    grads = dict(dx=z(T, d), dWg=z(E, d, dt=torch.float32), dbg=z(E, dt=torch.float32),
+                 dW1=z(E, F, d), db1=z(E, F), dW2=z(E, d, F), db2=z(E, d))
+    if Fs:
+        grads.update(dWs1=z(Fs, d), dbs1=z(Fs), dWs2=z(d, Fs), dbs2=z(d))
+    kept = torch.empty(E, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def fwd():
+        moe.moe_forward_train(cfg, dev, dev["x"], y, dict(kept=kept), ws, stream=stream)
+
+    def bwd():
+        moe.moe_backward(cfg, dev, dev["x"], dy, grads, aux_coef=0.01, ws=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            fwd()
+            bwd()
+    torch.cuda.synchronize()
+    g_step = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step, stream=stream):
+        fwd()
+        bwd()
+    g_bwd = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_bwd, stream=stream):
+        bwd()
+    torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            g_step.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            fwd()  # the backward reads what this forward leaves in the workspace
+            a.record(stream)
+            g_bwd.replay()
+            b.record(stream)
+    torch.cuda.synchronize()
+    bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kept_rows = int(kept.sum())
+    # backward GEMM work: input-gradient pass and weight-gradient pass, each 4 d F
+    # per kept row (+ 4 d Fs per token for the shared expert)
+    flop = 8.0 * kept_rows * d * F + (8.0 * T * d * Fs if Fs else 0.0)
+    peak = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
+    ach = flop / (bwd_ms * 1e-3) / 1e12
+    out = {
+        "metric": "MoE layer training step (forward + backward) tokens/s",
+        "value": round(T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if shape.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; random-init weights; dy ~ N(0, 1))",
+        "config": {"workload": shape.name, "tokens": T, "d_model": d, "d_ff": F,
+                   "n_experts": E, "top_k": shape.k, "capacity": shape.capacity,
+                   "shared_d_ff": Fs, "aux_coef": 0.01, "hip_graph": True,
+                   "kept_rows": kept_rows},
+        "backward": {"ms": round(bwd_ms, 4), "gemm_flop": flop, "achieved_tflops": round(ach, 1),
+                     "peak_tflops": peak, "frac": round(ach / peak, 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_summarize:
@@ -309,6 +399,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe(args)
+        return
+    if args.backward:
+        bench_backward(args)
         return
 
     import torch
