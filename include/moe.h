@@ -214,8 +214,9 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
 /* Gradients written by moe_backward; each member may be NULL (not computed).
  * Each has the layout and dtype of its tensor: dx [T, d] and the expert weight
  * and bias gradients in cfg->dtype, dWg [E, d] and dbg [E] fp32.  The shared
- * expert's members must be NULL when shared_d_ff = 0.  dx must be 16-byte
- * aligned.  Gradients overwrite (they are not accumulated into). */
+ * expert's members must be NULL when shared_d_ff = 0.  dx and the weight
+ * gradients dW1, dW2, dWs1, dWs2 must be 16-byte aligned.  Gradients overwrite
+ * (they are not accumulated into). */
 typedef struct {
   void *dx;
   float *dWg, *dbg;

@@ -38,22 +38,40 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// out[b][c][r] = in[b][r][c]; 64 x 64 tiles through LDS.
+// out[b][c][r] = in[b][r][c].  A block moves a 64 x 64 tile: 16-byte row
+// chunks are loaded (8 threads cover a 128-byte bf16 row segment), stored to
+// LDS, read back down the columns and written as 16-byte chunks of the output
+// rows.  The padded LDS row (PAD elements) keeps the column reads on distinct
+// banks.  R and C are multiples of the chunk width (8 bf16 or 4 fp32).
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in,
                                                         T* __restrict__ out, int R, int C) {
-  __shared__ T tile[64][65];
+  constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = 64 / V;        // chunks per 64-element row
+  constexpr int PAD = V;             // keeps LDS rows 16-byte aligned
+  constexpr int LDT = 64 + PAD;
+  __shared__ __align__(16) T tile[64 * LDT];
   const int64_t off = static_cast<int64_t>(blockIdx.z) * R * C;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    if (r < R && c < C) tile[i][tx] = in[off + static_cast<int64_t>(r) * C + c];
+  for (int q = threadIdx.x; q < 64 * CPR; q += 256) {
+    const int i = q / CPR, ch = q % CPR;
+    const int r = r0 + i, c = c0 + ch * V;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < R && c < C) v = *reinterpret_cast<const uint4*>(in + off + static_cast<int64_t>(r) * C + c);
+    *reinterpret_cast<uint4*>(&tile[i * LDT + ch * V]) = v;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < C && r < R) out[off + static_cast<int64_t>(c) * R + r] = tile[tx][i];
+  for (int q = threadIdx.x; q < 64 * CPR; q += 256) {
+    const int j = q / CPR, ch = q % CPR;  // output row c0 + j, rows r0 + ch V ..
+    const int c = c0 + j, r = r0 + ch * V;
+    if (c >= C || r >= R) continue;
+    union {
+      uint4 u;
+      T e[V];
+    } w;
+#pragma unroll
+    for (int i = 0; i < V; ++i) w.e[i] = tile[(ch * V + i) * LDT + j];
+    *reinterpret_cast<uint4*>(out + off + static_cast<int64_t>(c) * R + r) = w.u;
   }
 }
 
@@ -74,13 +92,16 @@ __global__ __launch_bounds__(kMaxExperts) void poff_kernel(const int32_t* __rest
 // row_token[offsets[g] + j] when gathering, else offsets[g] + j; scale =
 // row_gate of that grouped row when given, else 1); zero in the padding
 // columns.  A block covers 64 padded columns (inside one group, as every group
-// spans a multiple of 64) and 64 values of c.
+// spans a multiple of 64) and 64 values of c, moved as 16-byte chunks through
+// a padded LDS tile as in transpose_kernel.  C and lds are multiples of the
+// chunk width.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_transpose_kernel(
     const T* __restrict__ src, int64_t lds, int C, const int32_t* __restrict__ row_token,
     const float* __restrict__ row_gate, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ poff, int G, T* __restrict__ out, int64_t ldo) {
-  __shared__ T tile[64][65];
+  constexpr int V = 16 / sizeof(T), CPR = 64 / V, LDT = 64 + V;
+  __shared__ __align__(16) T tile[64 * LDT];
   const int col0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   if (col0 >= poff[G]) return;
   int lo = 0, hi = G;  // poff[lo] <= col0 < poff[hi]
@@ -90,22 +111,36 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(
     else hi = mid;
   }
   const int j0 = col0 - poff[lo], base = offsets[lo], rows = offsets[lo + 1] - base;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int j = j0 + i, c = c0 + tx;
-    float v = 0.f;
+  union Chunk {
+    uint4 u;
+    T e[V];
+  };
+  for (int q = threadIdx.x; q < 64 * CPR; q += 256) {
+    const int i = q / CPR, ch = q % CPR;  // tile row i = padded column col0 + i
+    const int j = j0 + i, c = c0 + ch * V;
+    Chunk v;
+    v.u = make_uint4(0, 0, 0, 0);
     if (j < rows && c < C) {
       const int r = base + j;
       const int64_t srow = row_token ? row_token[r] : r;
-      v = to_f32<T>(src[srow * lds + c]);
-      if (row_gate) v *= row_gate[r];
+      v.u = *reinterpret_cast<const uint4*>(src + srow * lds + c);
+      if (row_gate) {
+        const float g = row_gate[r];
+#pragma unroll
+        for (int e = 0; e < V; ++e) v.e[e] = from_f32<T>(g * to_f32<T>(v.e[e]));
+      }
     }
-    tile[i][tx] = from_f32<T>(v);
+    *reinterpret_cast<uint4*>(&tile[i * LDT + ch * V]) = v.u;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i;
-    if (c < C) out[static_cast<int64_t>(c) * ldo + col0 + tx] = tile[tx][i];
+  for (int q = threadIdx.x; q < 64 * CPR; q += 256) {
+    const int cc = q / CPR, ch = q % CPR;  // output row c0 + cc, columns col0 + ch V ..
+    const int c = c0 + cc;
+    if (c >= C) continue;
+    Chunk w;
+#pragma unroll
+    for (int e = 0; e < V; ++e) w.e[e] = tile[(ch * V + e) * LDT + cc];
+    *reinterpret_cast<uint4*>(out + static_cast<int64_t>(c) * ldo + col0 + ch * V) = w.u;
   }
 }
 
@@ -154,8 +189,9 @@ __global__ __launch_bounds__(WM* WN * 64) void wgrad_kernel(WgradArgs a) {
   constexpr int CPR = BK / CH;
   constexpr int ACH = BM * CPR / NT, BCH = BN * CPR / NT;
   static_assert(ACH >= 1 && BCH >= 1 && BM * CPR % NT == 0 && BN * CPR % NT == 0, "loader");
-  __shared__ __align__(16) T As[BM * LDK];
-  __shared__ __align__(16) T Bs[BN * LDK];
+  __shared__ __align__(16) T smem[(BM + BN) * LDK];
+  T* As = smem;
+  T* Bs = smem + BM * LDK;
 
   const int per = a.tiles_m * a.tiles_n;
   const int gi = blockIdx.x / per, rem = blockIdx.x % per;
@@ -230,18 +266,31 @@ __global__ __launch_bounds__(WM* WN * 64) void wgrad_kernel(WgradArgs a) {
         for (int j = 0; j < NI; ++j) acc[i][j] = M::op(fa[i], fb[j], acc[i][j]);
     }
   }
-  T* Cg = static_cast<T*>(a.C) + static_cast<int64_t>(gi) * a.M * a.N;
+  // Epilogue through LDS: each wave writes its WTM x WTN block (in T) to its own
+  // region of the (now free) tile buffers, then stores whole 16-byte chunks of
+  // output rows, so a wave's stores cover full 128-byte lines.
+  constexpr int V = 16 / sizeof(T), LDW = WTN + V;
+  static_assert(WM * WN * WTM * LDW <= (BM + BN) * LDK, "epilogue staging fits the tile buffers");
+  __syncthreads();  // every wave is done with As / Bs
+  T* stage = smem + wave * WTM * LDW;
 #pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int n = n0 + wn * WTN + j * 32 + (lane & 31);
-    if (n >= a.N) continue;
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int m = m0 + wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-        if (m < a.M) Cg[static_cast<int64_t>(m) * a.N + n] = from_f32<T>(acc[i][j][q]);
+        const int r = i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+        stage[r * LDW + j * 32 + (lane & 31)] = from_f32<T>(acc[i][j][q]);
       }
+  __syncthreads();
+  T* Cg = static_cast<T*>(a.C) + static_cast<int64_t>(gi) * a.M * a.N;
+  constexpr int CPRW = WTN / V;  // chunks per wave row
+  for (int q = lane; q < WTM * CPRW; q += 64) {
+    const int r = q / CPRW, ch = q % CPRW;
+    const int m = m0 + wm * WTM + r, n = n0 + wn * WTN + ch * V;
+    if (m < a.M && n < a.N)
+      *reinterpret_cast<uint4*>(Cg + static_cast<int64_t>(m) * a.N + n) =
+          *reinterpret_cast<const uint4*>(stage + r * LDW + ch * V);
   }
 }
 

@@ -518,7 +518,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   if (!grads) return MOE_ERR_INVALID_ARG;
   const moe_grads& g = *grads;
   if (cfg->T > 0 && (!x || !dy || !aligned16(x) || !aligned16(dy))) return MOE_ERR_INVALID_ARG;
-  if (g.dx && !aligned16(g.dx)) return MOE_ERR_INVALID_ARG;
+  if ((g.dx && !aligned16(g.dx)) || (g.dW1 && !aligned16(g.dW1)) ||
+      (g.dW2 && !aligned16(g.dW2)) || (g.dWs1 && !aligned16(g.dWs1)) ||
+      (g.dWs2 && !aligned16(g.dWs2)))
+    return MOE_ERR_INVALID_ARG;
   if (cfg->shared_d_ff == 0 && (g.dWs1 || g.dbs1 || g.dWs2 || g.dbs2)) return MOE_ERR_INVALID_ARG;
   if (!(aux_coef == aux_coef)) return MOE_ERR_INVALID_ARG;  // NaN
   const Layout L = layout(cfg, true);
