@@ -170,6 +170,15 @@ def traffic_probe(args):
     print("traffic probe done:", shape.name, flush=True)
 
 
+# epilogue mode of a grouped-GEMM kernel: its last template argument
+GEMM_MODE_UP, GEMM_MODE_DOWN = 0, 1
+
+
+def gemm_mode(kernel_name):
+    args = kernel_name.split("<", 1)[1].split(">", 1)[0].split(",")
+    return int(args[-1])
+
+
 def _counter_rows(db, counter):
     con = sqlite3.connect(db)
     rows = con.execute("select dispatch_id, kernel_name, value from counters_collection "
@@ -190,8 +199,8 @@ def traffic_summarize(args):
         factor = (COPY_BYTES / 1024.0) / float(np.mean(copies))
         rec[counter.lower() + "_copy_kib"] = float(np.mean(copies))
         rec[counter.lower() + "_factor"] = round(factor, 4)
-        for tag, flag in (("up", "true>"), ("down", "false>")):
-            vals = [v for _, n, v in rows if "grouped_gemm" in n and flag in n]
+        for tag, mode in (("up", GEMM_MODE_UP), ("down", GEMM_MODE_DOWN)):
+            vals = [v for _, n, v in rows if "grouped_gemm" in n and gemm_mode(n) == mode]
             if not vals:
                 sys.exit("no %s GEMM dispatches in %s" % (tag, db))
             kib[(tag, counter)] = (float(np.mean(vals)), len(vals), factor)
