@@ -226,8 +226,8 @@ typedef struct {
 
 /* Workspace bytes of moe_forward_train + moe_backward (0 on an invalid or
  * expert-choice config).  Besides the forward's buffers it holds the
- * pre-activations, the softmax, transposed copies of the expert weights and of
- * the grouped activations (each expert's rows padded to a multiple of 64). */
+ * pre-activations, the softmax and transposed copies of the grouped
+ * activations (each expert's rows padded to a multiple of 64). */
 size_t moe_train_workspace_bytes(const moe_config *cfg);
 
 /*

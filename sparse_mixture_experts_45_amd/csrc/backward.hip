@@ -18,11 +18,11 @@
 //   dl     = p (dp - <p, dp>)                                       router_bwd_kernel
 //   dW_g   = dl^T x, db_g = sum_t dl                                 router_wgrad_*
 //
-// The GEMMs need K-contiguous operands: the input-gradient pass multiplies by
-// the transposed expert weights (transpose_kernel), and the weight-gradient
-// GEMMs contract over an expert's rows, so their operands are transposed with
-// each expert's rows padded to a multiple of 64 columns (gather_transpose_kernel;
-// padding columns are zero, so every group's K is a whole number of K steps).
+// The input-gradient pass reads the expert weights in their stored layout
+// (the grouped GEMM's transposed-B path).  The weight-gradient GEMMs contract
+// over an expert's rows, so their operands are transposed with each expert's
+// rows padded to a multiple of 64 columns (gather_transpose_kernel; padding
+// columns are zero, so every group's K is a whole number of K steps).
 #include "kernels.h"
 #include "block_ops.h"
 #include "mfma.h"
@@ -36,43 +36,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
-}
-
-// out[b][c][r] = in[b][r][c].  A block moves a 64 x 64 tile: 16-byte row
-// chunks are loaded (8 threads cover a 128-byte bf16 row segment), stored to
-// LDS, read back down the columns and written as 16-byte chunks of the output
-// rows.  The padded LDS row (PAD elements) keeps the column reads on distinct
-// banks.  R and C are multiples of the chunk width (8 bf16 or 4 fp32).
-template <typename T>
-__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in,
-                                                        T* __restrict__ out, int R, int C) {
-  constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
-  constexpr int CPR = 64 / V;        // chunks per 64-element row
-  constexpr int PAD = V;             // keeps LDS rows 16-byte aligned
-  constexpr int LDT = 64 + PAD;
-  __shared__ __align__(16) T tile[64 * LDT];
-  const int64_t off = static_cast<int64_t>(blockIdx.z) * R * C;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  for (int q = threadIdx.x; q < 64 * CPR; q += 256) {
-    const int i = q / CPR, ch = q % CPR;
-    const int r = r0 + i, c = c0 + ch * V;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < R && c < C) v = *reinterpret_cast<const uint4*>(in + off + static_cast<int64_t>(r) * C + c);
-    *reinterpret_cast<uint4*>(&tile[i * LDT + ch * V]) = v;
-  }
-  __syncthreads();
-  for (int q = threadIdx.x; q < 64 * CPR; q += 256) {
-    const int j = q / CPR, ch = q % CPR;  // output row c0 + j, rows r0 + ch V ..
-    const int c = c0 + j, r = r0 + ch * V;
-    if (c >= C || r >= R) continue;
-    union {
-      uint4 u;
-      T e[V];
-    } w;
-#pragma unroll
-    for (int i = 0; i < V; ++i) w.e[i] = tile[(ch * V + i) * LDT + j];
-    *reinterpret_cast<uint4*>(out + off + static_cast<int64_t>(c) * R + r) = w.u;
-  }
 }
 
 // Padded column offsets of the G row groups: poff[g + 1] = poff[g] + the
@@ -93,8 +56,8 @@ __global__ __launch_bounds__(kMaxExperts) void poff_kernel(const int32_t* __rest
 // row_gate of that grouped row when given, else 1); zero in the padding
 // columns.  A block covers 64 padded columns (inside one group, as every group
 // spans a multiple of 64) and 64 values of c, moved as 16-byte chunks through
-// a padded LDS tile as in transpose_kernel.  C and lds are multiples of the
-// chunk width.
+// a padded LDS tile (the padding keeps the column reads on distinct banks).
+// C and lds are multiples of the chunk width.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_transpose_kernel(
     const T* __restrict__ src, int64_t lds, int C, const int32_t* __restrict__ row_token,
@@ -494,13 +457,6 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int
 }
 
 template <typename T>
-void run_transpose(const void* in, void* out, int B, int R, int C, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(ceil_div(C, 64)), static_cast<unsigned>(ceil_div(R, 64)),
-                  static_cast<unsigned>(B));
-  transpose_kernel<T><<<grid, 256, 0, st>>>(static_cast<const T*>(in), static_cast<T*>(out), R, C);
-}
-
-template <typename T>
 void run_wgrad(const WgradArgs& w, int groups, hipStream_t st) {
   if (groups <= 0 || w.M <= 0 || w.N <= 0) return;
   constexpr bool B16 = sizeof(T) == 2;
@@ -516,15 +472,6 @@ template <typename T>
 void run_bwd(const BwdArgs& b, int part, hipStream_t st) {
   const int ldh = b.F > b.Fs ? b.F : b.Fs;
   const int G = b.E + (b.Fs > 0 ? 1 : 0);
-  if (part == kBwdWeights) {
-    run_transpose<T>(b.W1, b.W1T, b.E, b.F, b.d, st);
-    run_transpose<T>(b.W2, b.W2T, b.E, b.d, b.F, st);
-    if (b.Fs > 0) {
-      run_transpose<T>(b.Ws1, b.Ws1T, 1, b.Fs, b.d, st);
-      run_transpose<T>(b.Ws2, b.Ws2T, 1, b.d, b.Fs, st);
-    }
-    return;
-  }
   if (part == kBwdRouter) {
     const int64_t pairs = b.T * b.k;
     gate_grad_kernel<T><<<static_cast<unsigned>(ceil_div(pairs, 4)), 256, 0, st>>>(

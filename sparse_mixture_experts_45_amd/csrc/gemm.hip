@@ -113,7 +113,7 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int pid, int tota
 // Generic kernel: any K that is a multiple of 8 (bf16) or 4 (fp32); tiles are
 // staged through registers with zero fill beyond K and beyond the tile rows.
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int BK, int WM, int WN, int MODE>
+template <typename T, int BM, int BN, int BK, int WM, int WN, int MODE, bool BT>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
   using M = Mfma<T>;
   using MD = ModeOf<MODE>;
@@ -176,10 +176,19 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < BCH; ++i) {
     const int c = tid + i * NT;
-    const int r = c / CPR;
-    bkc[i] = (c % CPR) * CH;
-    boff[i] = r * LDK + bkc[i];
-    bsrc[i] = (n0 + r < N) ? Bw + static_cast<int64_t>(n0 + r) * K : nullptr;
+    if constexpr (BT) {
+      // B stored [K, N]: chunk c is row k = c / (BN / CH), columns n0 + (c % (BN / CH)) CH ..;
+      // its values go to LDS transposed, Bs[n][k]
+      const int kr = c / (BN / CH), nc = (c % (BN / CH)) * CH;
+      bkc[i] = kr;
+      boff[i] = nc * LDK + kr;
+      bsrc[i] = (n0 + nc < N) ? Bw + static_cast<int64_t>(kr) * N + n0 + nc : nullptr;
+    } else {
+      const int r = c / CPR;
+      bkc[i] = (c % CPR) * CH;
+      boff[i] = r * LDK + bkc[i];
+      bsrc[i] = (n0 + r < N) ? Bw + static_cast<int64_t>(n0 + r) * K : nullptr;
+    }
   }
 
   uint4 ra[ACH], rb[BCH];
@@ -193,8 +202,13 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
       const int kk = k0 + bkc[i];
-      rb[i] = (bsrc[i] && kk < K) ? *reinterpret_cast<const uint4*>(bsrc[i] + kk)
-                                  : make_uint4(0, 0, 0, 0);
+      if constexpr (BT)
+        rb[i] = (bsrc[i] && kk < K)
+                    ? *reinterpret_cast<const uint4*>(bsrc[i] + static_cast<int64_t>(k0) * N)
+                    : make_uint4(0, 0, 0, 0);
+      else
+        rb[i] = (bsrc[i] && kk < K) ? *reinterpret_cast<const uint4*>(bsrc[i] + kk)
+                                    : make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -212,7 +226,19 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < ACH; ++i) *reinterpret_cast<uint4*>(&As[aoff[i]]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) *reinterpret_cast<uint4*>(&Bs[boff[i]]) = rb[i];
+    for (int i = 0; i < BCH; ++i) {
+      if constexpr (BT) {
+        union {
+          uint4 u;
+          T e[CH];
+        } v;
+        v.u = rb[i];
+#pragma unroll
+        for (int e = 0; e < CH; ++e) Bs[boff[i] + e * LDK] = v.e[e];
+      } else {
+        *reinterpret_cast<uint4*>(&Bs[boff[i]]) = rb[i];
+      }
+    }
     __syncthreads();
     if (k0 + BK < K) gload(k0 + BK);
 #pragma unroll
@@ -291,6 +317,22 @@ __device__ __forceinline__ int swz(int r) {
   return CPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
+// Chunk swizzle of a [BK, BN] (K-major) B tile row k: the transposing reads of
+// one 16-lane group touch 4 consecutive rows at the same chunk pair, so row k
+// moves its chunks by 4 (k % 4) positions (4 rows x 2 chunks x 2 column halves
+// = 16 distinct chunk positions, one pass of the 64 banks).
+__device__ __forceinline__ int swzt(int k) { return (k & 3) << 2; }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16: within each group of 16 lanes, the four 16-bit values
+// the lanes address (lane i: 4 values at its address) are redistributed so
+// that lane j gets value j of the group's rows: lane i = 4 r + q addressing
+// row r, columns 4 q .. 4 q + 3 hands lane j the column-j value of rows 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<char*>(p)));
+}
+
 // s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding)
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -318,9 +360,14 @@ __device__ __forceinline__ void sched_steps() {
 // next tile (its token rows, its gates) is already loaded; after the K loop
 // the next tile's first stages are issued before tile t's epilogue runs, so
 // load latency hides under the epilogue instead of idling the CU.
-template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int MODE>
+template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int MODE,
+          bool BT>
 __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(GemmArgs a) {
   using MD = ModeOf<MODE>;
+  // BT: the group's B is stored [K, N] (row k holds N contiguous values), as
+  // the input-gradient pass reads the expert weights; its tile sits in LDS as
+  // BK rows of BN values and MFMA fragments come from transposing LDS reads.
+  static_assert(!BT || BN >= 128, "transposed B tile: at least 16 chunks per row");
   constexpr int NW = WM * WN;
   constexpr int NT = NW * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -354,6 +401,18 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
 #pragma unroll
   for (int j = 0; j < NI; ++j) boffs[j] = (BM + wn * WTN + j * 32 + lrow) * RB;
   const int rsw = swz<CPR>(lrow);  // the same for every fragment row of this lane
+  // BT fragment reads: lane l takes rows 8 (l / 32) + (l % 16) / 4 (+ 4 for the
+  // second read) and 4 columns from 16 ((l / 16) % 2) + 4 (l % 4) of its
+  // 32-column block; btoffs[j] is the byte offset (k16 step 0, first read)
+  int btoffs[NI];
+  if constexpr (BT) {
+    const int trow = 8 * (lane >> 5) + ((lane & 15) >> 2);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int col = wn * WTN + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      btoffs[j] = BM * RB + trow * (BN * 2) + (((col >> 3) ^ swzt(trow)) << 4) + (col & 7) * 2;
+    }
+  }
 
   struct Tile {
     int row0, rows, n0, N, K;
@@ -398,10 +457,19 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     return static_cast<uint32_t>(arow) * static_cast<uint32_t>(a.lda * 2) + chunk * 16;
   };
   auto b_off = [&](const Tile& c, int j) -> uint32_t {
-    const int r = (wave + j * NW) * RPI + lr;
-    const int chunk = (lane % CPR) ^ swz<CPR>(r);
-    const int nn = min(c.n0 + r - BM, c.N - 1);
-    return static_cast<uint32_t>(nn) * static_cast<uint32_t>(c.K * 2) + chunk * 16;
+    if constexpr (BT) {
+      // this lane's 16 bytes of the B region: row kr, chunk position pos, which
+      // holds global chunk pos ^ swzt(kr) (clamped to a valid column chunk)
+      const int o = ((wave + j * NW) * RPI - BM) * RB + lane * 16;
+      const int kr = o / (BN * 2), pos = (o % (BN * 2)) >> 4;
+      const int nn = min(c.n0 + ((pos ^ swzt(kr)) << 3), c.N - 8);
+      return static_cast<uint32_t>(kr) * static_cast<uint32_t>(c.N * 2) + nn * 2;
+    } else {
+      const int r = (wave + j * NW) * RPI + lr;
+      const int chunk = (lane % CPR) ^ swz<CPR>(r);
+      const int nn = min(c.n0 + r - BM, c.N - 1);
+      return static_cast<uint32_t>(nn) * static_cast<uint32_t>(c.K * 2) + chunk * 16;
+    }
   };
   auto gate_of = [&](const Tile& c, int m) -> float {
     return m < c.rows ? (a.row_gate ? a.row_gate[c.row0 + m] : 1.f) : 0.f;
@@ -419,10 +487,13 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
   }
   const char* abase = static_cast<const char*>(a.A);
   const char* bbase = reinterpret_cast<const char*>(cur.bw);
+  // bytes per k of B: 2 (K-contiguous rows) or one [K, N] row
+  uint32_t bstep = BT ? static_cast<uint32_t>(cur.N) * 2 : 2;
   auto issue = [&](int stage, int k0) {
 #pragma unroll
     for (int j = 0; j < JPW; ++j)
-      lds_dma16((j < JA ? abase : bbase) + src[j] + static_cast<uint32_t>(k0) * 2,
+      lds_dma16((j < JA ? abase : bbase) + src[j] +
+                    static_cast<uint32_t>(k0) * (j < JA ? 2u : bstep),
                 smem + stage * STAGE + (wave + j * NW) * RPI * RB);
   };
   {
@@ -496,9 +567,19 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
 #pragma unroll
         for (int i = 0; i < MI; ++i)
           fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + aoffs[i] + cb);
+        if constexpr (BT) {
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-          fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boffs[j] + cb);
+          for (int j = 0; j < NI; ++j) {
+            const char* p = st + btoffs[j] + s * 16 * (BN * 2);
+            const i16x4 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * (BN * 2));
+            fb[buf][j] = __builtin_bit_cast(
+                bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boffs[j] + cb);
+        }
       };
       frags(0, 0);
 #pragma unroll
@@ -513,8 +594,9 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
       }
       // Instruction order for the scheduler: the first step's fragment reads,
       // then each step's MFMAs with the next step's reads spread between them.
-      __builtin_amdgcn_sched_group_barrier(0x100, MI + NI, 0);
-      sched_steps<0, KS - 1, MI + NI, MI * NI>();
+      constexpr int NRD = MI + (BT ? 2 : 1) * NI;  // fragment reads per k16 step
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+      sched_steps<0, KS - 1, NRD, MI * NI>();
       __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
     }
     // Every wave is done reading this tile's stages (and every load of it has
@@ -525,6 +607,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
 #pragma unroll
       for (int j = 0; j < JPW; ++j) src[j] = j < JA ? a_off(j, ntok[j]) : b_off(nxt, j);
       bbase = reinterpret_cast<const char*>(nxt.bw);
+      bstep = BT ? static_cast<uint32_t>(nxt.N) * 2 : 2;
       const int KTn = nxt.K / BK;
 #pragma unroll
       for (int p = 0; p < NS - 1; ++p)
@@ -672,17 +755,17 @@ static GemmArgs down_args(const FfnArgs& f, int BN) {
   return dn;
 }
 
-template <typename T, int BM, int BNU, int BND, int BK, int WM, int WN, int M1>
+template <typename T, int BM, int BNU, int BND, int BK, int WM, int WN, int M1, bool BT>
 static void run_generic(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const GemmArgs u = up_args(f, BNU);
   const int64_t gu = gp.tiles_max * u.n_tiles_n;
   if (gu > 0)
-    grouped_gemm_kernel<T, BM, BNU, BK, WM, WN, M1>
+    grouped_gemm_kernel<T, BM, BNU, BK, WM, WN, M1, BT>
         <<<static_cast<unsigned>(gu), WM * WN * 64, 0, st>>>(u);
   const GemmArgs dn = down_args(f, BND);
   const int64_t gd = gp.tiles_max * dn.n_tiles_n;
   if (gd > 0)
-    grouped_gemm_kernel<T, BM, BND, BK, WM, WN, kDown>
+    grouped_gemm_kernel<T, BM, BND, BK, WM, WN, kDown, BT>
         <<<static_cast<unsigned>(gd), WM * WN * 64, 0, st>>>(dn);
 }
 
@@ -697,10 +780,11 @@ static int cu_count() {
 
 // Persistent launch: as many blocks as can be resident, capped by the tile
 // count; otherwise one block per tile.
-template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int MODE>
+template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int MODE,
+          bool BT>
 static void launch_dma(const GemmArgs& g, int64_t tiles, hipStream_t st) {
   if (tiles <= 0) return;
-  auto kern = grouped_gemm_dma_kernel<BM, BN, BK, NS, WM, WN, OCC, PERSIST, MODE>;
+  auto kern = grouped_gemm_dma_kernel<BM, BN, BK, NS, WM, WN, OCC, PERSIST, MODE, BT>;
   const size_t lds = static_cast<size_t>(NS) * (BM + BN) * BK * 2;
   static int per_cu = [&] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -716,24 +800,28 @@ static void launch_dma(const GemmArgs& g, int64_t tiles, hipStream_t st) {
   kern<<<static_cast<unsigned>(grid), WM * WN * 64, lds, st>>>(g);
 }
 
-template <int BM, int BNU, int BND, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int M1>
+template <int BM, int BNU, int BND, int BK, int NS, int WM, int WN, int OCC, int PERSIST,
+          int WMD, int WND, int M1, bool BT>
 static void run_dma(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const GemmArgs u = up_args(f, BNU);
-  launch_dma<BM, BNU, BK, NS, WM, WN, OCC, PERSIST, M1>(u, gp.tiles_max * u.n_tiles_n, st);
+  launch_dma<BM, BNU, BK, NS, WM, WN, OCC, PERSIST, M1, BT>(u, gp.tiles_max * u.n_tiles_n, st);
   const GemmArgs dn = down_args(f, BND);
-  launch_dma<BM, BND, BK, NS, WM, WN, OCC, PERSIST, kDown>(dn, gp.tiles_max * dn.n_tiles_n, st);
+  launch_dma<BM, BND, BK, NS, WMD, WND, OCC, PERSIST, kDown, BT>(
+      dn, gp.tiles_max * dn.n_tiles_n, st);
 }
 
-// The two GEMMs of one pass over the grouped rows; M1 is the first GEMM's mode.
-template <int M1>
+// The two GEMMs of one pass over the grouped rows; M1 is the first GEMM's mode,
+// BT whether B is stored [K, N].
+template <int M1, bool BT>
 static void run_pass(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   switch (gp.shape) {
-    case kGemmF32: run_generic<float, 64, 64, 64, 32, 2, 2, M1>(gp, f, st); break;
-    case kGemmBf16Large: run_generic<bf16, 128, 128, 128, 64, 2, 2, M1>(gp, f, st); break;
-    case kGemmBf16Mid: run_generic<bf16, 64, 128, 128, 64, 1, 4, M1>(gp, f, st); break;
-    case kGemmBf16Small: run_generic<bf16, 32, 128, 128, 64, 1, 4, M1>(gp, f, st); break;
-#define MOE_RUN_DMA(C) \
-  run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN, C.OCC, C.PERSIST, M1>(gp, f, st)
+    case kGemmF32: run_generic<float, 64, 64, 64, 32, 2, 2, M1, BT>(gp, f, st); break;
+    case kGemmBf16Large: run_generic<bf16, 128, 128, 128, 64, 2, 2, M1, BT>(gp, f, st); break;
+    case kGemmBf16Mid: run_generic<bf16, 64, 128, 128, 64, 1, 4, M1, BT>(gp, f, st); break;
+    case kGemmBf16Small: run_generic<bf16, 32, 128, 128, 64, 1, 4, M1, BT>(gp, f, st); break;
+#define MOE_RUN_DMA(C)                                                                     \
+  run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN, C.OCC, C.PERSIST, C.WMD, C.WND, M1, BT>( \
+      gp, f, st)
     case kGemmDmaLarge: MOE_RUN_DMA(kDmaLarge); break;
     case kGemmDmaMid: MOE_RUN_DMA(kDmaMid); break;
     case kGemmDmaSmall: MOE_RUN_DMA(kDmaSmall); break;
@@ -750,9 +838,9 @@ hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
                                                   f.row_slot, f.topk_w, f.tiles, f.ntiles,
                                                   f.row_gate);
   switch (f.pass) {
-    case kPassForward: run_pass<kUp>(gp, f, st); break;
-    case kPassForwardTrain: run_pass<kUpTrain>(gp, f, st); break;
-    default: run_pass<kDz>(gp, f, st); break;
+    case kPassForward: run_pass<kUp, false>(gp, f, st); break;
+    case kPassForwardTrain: run_pass<kUpTrain, false>(gp, f, st); break;
+    default: run_pass<kDz, true>(gp, f, st); break;
   }
   return hipGetLastError();
 }

@@ -32,15 +32,16 @@ enum GemmShape {
 // Tile configurations of the LDS-DMA grouped GEMM.  The host plan (row-tile
 // height for the tile list) and the launcher read the same table.
 struct DmaCfg {
-  // rows, up/down columns, K step, stages, wave grid, the waves per SIMD the
-  // register budget is sized for, and whether blocks stay resident and walk
-  // several tiles (1) or each block takes one tile (0)
-  int BM, BNU, BND, BK, NS, WM, WN, OCC, PERSIST;
+  // rows, up/down columns, K step, stages, the up GEMM's wave grid, the waves
+  // per SIMD the register budget is sized for, whether blocks stay resident and
+  // walk several tiles (1) or each block takes one tile (0), and the down
+  // GEMM's wave grid
+  int BM, BNU, BND, BK, NS, WM, WN, OCC, PERSIST, WMD, WND;
 };
-constexpr DmaCfg kDmaLarge{256, 256, 256, 64, 2, 2, 4, 2, 0};   // >= 768 rows per expert
-constexpr DmaCfg kDmaMid{128, 128, 128, 64, 2, 2, 4, 2, 0};     // >= 256
-constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 4, 1, 4, 2, 1};    // >= 48
-constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 4, 1, 4, 2, 0};   // fewer: weight streaming
+constexpr DmaCfg kDmaLarge{256, 256, 256, 64, 2, 2, 4, 2, 0, 2, 4};   // >= 768 rows per expert
+constexpr DmaCfg kDmaMid{128, 128, 128, 64, 2, 2, 4, 2, 0, 2, 4};     // >= 256
+constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 4, 1, 4, 2, 1, 1, 4};    // >= 48
+constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 4, 1, 4, 2, 0, 1, 4};   // fewer: weight streaming
 
 struct GemmPlan {
   int shape;        // GemmShape
@@ -50,10 +51,11 @@ struct GemmPlan {
 
 // Passes of the grouped-GEMM pair.  kPassDgrad is the input-gradient pass of
 // the backward, run with the forward's argument roles re-bound: x = dy
-// (gathered), W1 = W2 transposed [E, F, d], W2 = W1 transposed [E, d, F]
-// (likewise the shared expert's), no biases, Z = the forward's pre-activations
-// (overwritten with dz = gate * (dy W2) * act'(z)), y_rows = dz W1 per row
-// (fp32, no gate).
+// (gathered), W1 = the forward's W2 and W2 = the forward's W1 (likewise the
+// shared expert's), both read in their stored layout as [K, N] matrices
+// (W2[e] is [d, F]: K = d, N = F), no biases, H = the forward's
+// pre-activations (overwritten with dz = gate * (dy W2) * act'(z)), y_rows =
+// dz W1 per row (fp32, no gate).
 enum { kPassForward = 0, kPassForwardTrain = 1, kPassDgrad = 2 };
 
 struct FfnArgs {
@@ -129,20 +131,18 @@ hipError_t launch_combine_ec(int64_t T, int d, int E, int Ce, int shared, int dt
 
 hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& a, hipStream_t st);
 
-// Backward (token choice).  moe_backward enqueues, in order: kBwdWeights (the
-// transposed expert weights), kBwdRouter (gate gradients, the balance term,
+// Backward (token choice).  moe_backward enqueues, in order: kBwdRouter (gate
+// gradients, the balance term,
 // router-score gradients dl, dW_g and db_g), the input-gradient GEMM pass
 // (launch_ffn with kPassDgrad), kBwdDx (dx), kBwdExpertWeights (transposed
 // activations, expert weight and bias gradients).
-enum { kBwdWeights = 0, kBwdRouter = 1, kBwdDx = 2, kBwdExpertWeights = 3 };
+enum { kBwdRouter = 1, kBwdDx = 2, kBwdExpertWeights = 3 };
 struct BwdArgs {
   int64_t T;
   int d, F, E, k, Fs, dtype, renorm, nb;
   float alpha;                  // coefficient of the balance term
   const void *x, *dy;           // [T, d] layer dtype
   const float* Wg;              // [E, d]
-  const void *W1, *W2, *Ws1, *Ws2;
-  void *W1T, *W2T, *Ws1T, *Ws2T;  // transposed weights [E, d, F], [E, F, d], [d, Fs], [Fs, d]
   const float* probs;           // [T, E] the forward's softmax
   const int32_t* topk_idx;      // [T, k]
   const float* topk_w;          // [T, k]

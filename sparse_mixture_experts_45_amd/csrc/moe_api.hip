@@ -20,7 +20,7 @@ struct Layout {
   bool train;
   int wg_split;
   int64_t wg_chunk, Rp;
-  size_t Z, probs, dg, dl, aux_dp, wg_part, W1T, W2T, Ws1T, Ws2T, poff, ZT, HT, XT, DT;
+  size_t Z, probs, dg, dl, aux_dp, wg_part, poff, ZT, HT, XT, DT;
 };
 
 bool expert_choice(const moe_config* c) { return c->routing == MOE_ROUTE_EXPERT; }
@@ -193,10 +193,6 @@ Layout layout(const moe_config* c, bool train = false) {
         1, std::min<int64_t>(ceil_div(512, col_blocks), ceil_div(std::max<int64_t>(T, 1), 64))));
     L.wg_chunk = ceil_div(std::max<int64_t>(T, 1), L.wg_split);
     L.wg_part = take(sizeof(float) * L.wg_split * E * (d + 1));
-    L.W1T = take(elt * E * F * d);
-    L.W2T = take(elt * E * d * F);
-    L.Ws1T = take(elt * Fs * d);
-    L.Ws2T = take(elt * d * Fs);
     L.poff = take(sizeof(int32_t) * (G + 1));
     L.Rp = static_cast<int64_t>(align_up(L.rows_max + 64 * G, 64));
     L.ZT = take(elt * ldh * L.Rp);
@@ -559,14 +555,6 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   b.x = x;
   b.dy = dy;
   b.Wg = w->Wg;
-  b.W1 = w->W1;
-  b.W2 = w->W2;
-  b.Ws1 = w->Ws1;
-  b.Ws2 = w->Ws2;
-  b.W1T = at(ws, L.W1T);
-  b.W2T = at(ws, L.W2T);
-  b.Ws1T = at(ws, L.Ws1T);
-  b.Ws2T = at(ws, L.Ws2T);
   b.probs = reinterpret_cast<const float*>(at(ws, L.probs));
   b.topk_idx = reinterpret_cast<const int32_t*>(at(ws, L.topk_idx));
   b.topk_w = reinterpret_cast<const float*>(at(ws, L.topk_w));
@@ -602,7 +590,6 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   b.dbs1 = g.dbs1;
   b.dWs2 = g.dWs2;
   b.dbs2 = g.dbs2;
-  if ((s = hip_status(launch_backward(b, kBwdWeights, st))) != MOE_OK) return s;
   // gate gradients read the forward's expert rows before the dgrad pass reuses them
   if ((s = hip_status(launch_backward(b, kBwdRouter, st))) != MOE_OK) return s;
   // input-gradient pass: dz (in place of z) and dz W1 per row (in place of y_rows)
@@ -616,10 +603,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   f.act = cfg->act;
   f.dtype = cfg->dtype;
   f.x = dy;
-  f.W1 = b.W2T;
-  f.W2 = b.W1T;
-  f.Ws1 = b.Ws2T;
-  f.Ws2 = b.Ws1T;
+  f.W1 = w->W2;  // read as [K = d, N = F]
+  f.W2 = w->W1;  // read as [K = F, N = d]
+  f.Ws1 = w->Ws2;
+  f.Ws2 = w->Ws1;
   f.offsets = b.offsets;
   f.row_token = b.row_token;
   f.H = at(ws, L.Z);
