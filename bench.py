@@ -170,13 +170,14 @@ def traffic_probe(args):
     print("traffic probe done:", shape.name, flush=True)
 
 
-# epilogue mode of a grouped-GEMM kernel: its last template argument
+# epilogue mode of a grouped-GEMM kernel: its last integer template argument
+# (a trailing bool says whether B is read [K, N])
 GEMM_MODE_UP, GEMM_MODE_DOWN = 0, 1
 
 
 def gemm_mode(kernel_name):
-    args = kernel_name.split("<", 1)[1].split(">", 1)[0].split(",")
-    return int(args[-1])
+    args = [x.strip() for x in kernel_name.split("<", 1)[1].split(">", 1)[0].split(",")]
+    return int([x for x in args if x.lstrip("-").isdigit()][-1])
 
 
 def _counter_rows(db, counter):
@@ -200,7 +201,8 @@ def traffic_summarize(args):
         rec[counter.lower() + "_copy_kib"] = float(np.mean(copies))
         rec[counter.lower() + "_factor"] = round(factor, 4)
         for tag, mode in (("up", GEMM_MODE_UP), ("down", GEMM_MODE_DOWN)):
-            vals = [v for _, n, v in rows if "grouped_gemm" in n and gemm_mode(n) == mode]
+            vals = [v for _, n, v in rows
+                    if "grouped_gemm" in n and gemm_mode(n) == mode and "true>" not in n]
             if not vals:
                 sys.exit("no %s GEMM dispatches in %s" % (tag, db))
             kib[(tag, counter)] = (float(np.mean(vals)), len(vals), factor)
