@@ -42,6 +42,21 @@ def test_drawn_shapes(shape):
     check_y(shape, g["y"], ref["y"])
 
 
+@pytest.mark.parametrize("shape", draw_shapes(12, 77), ids=lambda s: s.name)
+def test_drawn_shapes_backward(shape):
+    """Every gradient of sum <dy, y> + 0.3 balance against the oracle's (balance
+    term off for one expert, where it is undefined)."""
+    from test_gpu_backward import check, dy_device, gpu_backward, make_dy
+    say("case", shape)
+    alpha = 0.3 if shape.E > 1 else 0.0
+    inp = make_inputs(shape, 6)
+    dy_raw, dy64 = make_dy(shape, 9)
+    want = oracle.backward(shape, inp, dy64, alpha)
+    got, _ = gpu_backward(shape, device_inputs(inp), dy_device(shape, dy_raw), alpha)
+    for n in got:
+        check(shape, got[n], want[n], n)
+
+
 GUARD = 4096  # bytes of canary before and after each output
 
 
