@@ -328,3 +328,22 @@ def backward_expert_entries(shape, inp, dy, e: int, f_list, j_list, rt: Optional
     if rc != 0:
         raise ValueError("orc_backward_expert_entries failed")
     return out
+
+
+def ec_slots(shape, r: dict) -> tuple:
+    """Expert choice as k = E slots: (shape with k = E and no renormalisation,
+    routing dict with every expert a slot, gates p, the selection as keep)."""
+    E = shape.E
+    s = shape.with_(k=E, renormalize=0)
+    rt = dict(topk_idx=np.tile(np.arange(E, dtype=np.int32), (shape.T, 1)),
+              topk_w=np.ascontiguousarray(r["p"], np.float64),
+              keep=np.ascontiguousarray(r["sel"], np.int32),
+              mean_prob=np.ascontiguousarray(r["mean_prob"], np.float64))
+    return s, rt
+
+
+def ec_backward(shape, inp, dy, alpha: float = 0.0, r: Optional[dict] = None) -> dict:
+    """Every gradient of the expert-choice layer (selection fixed), fp64."""
+    r = ec_route(shape, inp) if r is None else r
+    s, rt = ec_slots(shape, r)
+    return backward(s, inp, dy, alpha, rt=rt)

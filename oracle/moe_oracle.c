@@ -44,7 +44,9 @@
  *                 (matteuscruz "Load balancing", expert choice routing)
  *   backward      gradients of sum_t <dy_t, y_t> + alpha * balance with the
  *                 selection and the drops held fixed (the chain rule written
- *                 out above orc_backward)
+ *                 out above orc_backward); expert choice is the same chain
+ *                 rule with every expert a slot, the selection as the keep
+ *                 mask, gates p[t, e] and no renormalisation
  *
  * Precision: everything is fp64 except one decision: the top-k selection is
  * taken on the scores rounded to fp32, the precision the GPU router decides in.
@@ -533,7 +535,7 @@ static void mlp_bwd(const orc_config *c, int32_t Fm, const void *W1, const void 
 
 /* scratch of one token's backward */
 typedef struct {
-  double *xt, *l, *p, *dp, *go, *o, *z, *h, *dz;
+  double *xt, *l, *p, *dp, *go, *o, *z, *h, *dz, *dg;
 } bwd_scratch;
 
 static int scratch_alloc(bwd_scratch *s, const orc_config *c) {
@@ -547,7 +549,8 @@ static int scratch_alloc(bwd_scratch *s, const orc_config *c) {
   s->z = (double *)malloc(sizeof(double) * (Fm > 0 ? Fm : 1));
   s->h = (double *)malloc(sizeof(double) * (Fm > 0 ? Fm : 1));
   s->dz = (double *)malloc(sizeof(double) * (Fm > 0 ? Fm : 1));
-  return s->xt && s->l && s->p && s->dp && s->go && s->o && s->z && s->h && s->dz;
+  s->dg = (double *)malloc(sizeof(double) * c->k);
+  return s->xt && s->l && s->p && s->dp && s->go && s->o && s->z && s->h && s->dz && s->dg;
 }
 
 static void scratch_free(bwd_scratch *s) {
@@ -560,6 +563,7 @@ static void scratch_free(bwd_scratch *s) {
   free(s->z);
   free(s->h);
   free(s->dz);
+  free(s->dg);
 }
 
 /*
@@ -587,8 +591,7 @@ static void bwd_token(const orc_config *c, const void *x, const orc_weights *w, 
   for (int32_t e = 0; e < E; ++e) s->p[e] /= zsum;
 
   /* routed experts */
-  double dg_local[64];
-  double *dg = dgt ? dgt : dg_local;
+  double *dg = dgt ? dgt : s->dg;
   for (int32_t i = 0; i < k; ++i) {
     dg[i] = 0.0;
     if (!keep[i]) continue;
@@ -649,7 +652,7 @@ static void bwd_token(const orc_config *c, const void *x, const orc_weights *w, 
 int orc_backward(const orc_config *c, const void *x, const orc_weights *w, const double *dy,
                  double alpha, const int32_t *topk_idx, const double *topk_w,
                  const int32_t *keep, const double *mean_prob, const orc_grads *g) {
-  if (!c || c->k > 64 || c->T < 0) return -1;
+  if (!c || c->k < 1 || c->T < 0) return -1;
   const int64_t T = c->T;
   const int32_t d = c->d, E = c->E, F = c->F, Fs = c->Fs;
   /* zero every requested output */
@@ -692,7 +695,7 @@ int orc_backward_tokens(const orc_config *c, const void *x, const orc_weights *w
                         const double *topk_w, const int32_t *keep, const double *mean_prob,
                         const int64_t *tokens, int64_t n_tok, double *dx, double *dl,
                         double *dg) {
-  if (!c || c->k > 64) return -1;
+  if (!c || c->k < 1) return -1;
   const int32_t d = c->d, E = c->E, k = c->k;
   int bad = 0;
 #pragma omp parallel

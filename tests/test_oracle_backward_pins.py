@@ -219,3 +219,47 @@ def test_sampled_entry_points_agree_with_the_full_backward():
         assert np.allclose(s["dW2"], G2[np.ix_(jl, fl_)], rtol=0, atol=1e-12)
         assert np.allclose(s["db1"], B1[fl_], rtol=0, atol=1e-12)
         assert np.allclose(s["db2"], B2[jl], rtol=0, atol=1e-12)
+
+
+def torch_ec_grads(shape, inp, sel, dy, alpha):
+    """Autograd of the expert-choice layer as torch library calls with the
+    oracle's selection held fixed: y = sum_e sel[:, e] p[:, e] E_e(x) (+ shared)."""
+    P = {n: as64(inp.get(n), shape, n) for n in PARAMS}
+    for v in P.values():
+        if v is not None:
+            v.requires_grad_(True)
+    x = P["x"]
+    probs = torch.softmax(Fn.linear(x, P["Wg"], P["bg"]), dim=-1)
+    act = Fn.gelu if shape.act == "gelu" else torch.relu
+    y = torch.zeros_like(x)
+    selt = torch.from_numpy(sel.astype(bool))
+    for e in range(shape.E):
+        rows = selt[:, e].nonzero().flatten()
+        if rows.numel() == 0:
+            continue
+        b1 = None if P["b1"] is None else P["b1"][e]
+        b2 = None if P["b2"] is None else P["b2"][e]
+        out = Fn.linear(act(Fn.linear(x[rows], P["W1"][e], b1)), P["W2"][e], b2)
+        y = y.index_add(0, rows, probs[rows, e:e + 1] * out)
+    if shape.Fs:
+        y = y + Fn.linear(act(Fn.linear(x, P["Ws1"], P["bs1"])), P["Ws2"], P["bs2"])
+    L = (torch.from_numpy(dy) * y).sum()
+    if alpha:
+        L = L + alpha * torch.var(probs.mean(dim=0))
+    L.backward()
+    return {GRAD[n]: v.grad.numpy() for n, v in P.items() if v is not None}
+
+
+@pytest.mark.parametrize("shape", [
+    small(routing="expert", Fs=16),
+    small(routing="expert", dtype="bf16", act="relu", E=5, k=2, capacity=9),
+    small(routing="expert", E=70, k=3, T=50, router_bias="none"),
+], ids=["f32_shared", "bf16_capacity", "e70"])
+def test_ec_backward_matches_torch_autograd(shape):
+    inp = make_inputs(shape, 23)
+    r = oracle.ec_route(shape, inp)
+    dy = dy_of(shape)
+    got = oracle.ec_backward(shape, inp, dy, 0.6, r=r)
+    want = torch_ec_grads(shape, inp, r["sel"], dy, 0.6)
+    for key, w in want.items():
+        assert_close(got[key], w, what=key)
