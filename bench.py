@@ -319,8 +319,6 @@ def bench_backward(args):
     from moe_synth import make_inputs, to_device, workload
 
     shape = workload(args.workload)
-    if shape.routing != "token":
-        raise SystemExit("the backward covers token-choice routing only")
     dev = to_device(make_inputs(shape, args.seed), "cuda")
     cfg = layer_config(moe, torch, shape)
     ws = moe.train_workspace(cfg)
@@ -389,8 +387,8 @@ def bench_backward(args):
         "data": "synthetic (seeded; random-init weights; dy ~ N(0, 1))",
         "config": {"workload": shape.name, "tokens": T, "d_model": d, "d_ff": F,
                    "n_experts": E, "top_k": shape.k, "capacity": shape.capacity,
-                   "shared_d_ff": Fs, "aux_coef": 0.01, "hip_graph": True,
-                   "kept_rows": kept_rows},
+                   "shared_d_ff": Fs, "routing": shape.routing, "aux_coef": 0.01,
+                   "hip_graph": True, "kept_rows": kept_rows},
         "backward": {"ms": round(bwd_ms, 4), "gemm_flop": flop, "achieved_tflops": round(ach, 1),
                      "peak_tflops": peak, "frac": round(ach / peak, 4)},
     }

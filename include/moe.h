@@ -207,8 +207,8 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
  * "Load balancing").  The top-k selection and the capacity drops are held
  * fixed, as autograd treats them: a dropped slot gets no gate gradient but
  * still counts in the renormalisation sum.  With E = 1 the balance term has
- * no gradient.  Token choice only (MOE_ERR_UNSUPPORTED under
- * MOE_ROUTE_EXPERT).
+ * no gradient.  Under MOE_ROUTE_EXPERT the selection is held fixed and each
+ * taken pair's gate is p[t, e] (no renormalisation).
  */
 
 /* Gradients written by moe_backward; each member may be NULL (not computed).
@@ -224,15 +224,16 @@ typedef struct {
   void *dWs1, *dbs1, *dWs2, *dbs2;
 } moe_grads;
 
-/* Workspace bytes of moe_forward_train + moe_backward (0 on an invalid or
- * expert-choice config).  Besides the forward's buffers it holds the
+/* Workspace bytes of moe_forward_train + moe_backward (0 on an invalid
+ * config).  Besides the forward's buffers it holds the
  * pre-activations, the softmax and transposed copies of the grouped
  * activations (each expert's rows padded to a multiple of 64). */
 size_t moe_train_workspace_bytes(const moe_config *cfg);
 
 /*
- * moe_forward that also leaves in ws what moe_backward reads: the routing,
- * the grouping, the softmax [T, E], the pre-activations z and hidden
+ * moe_forward that also leaves in ws what moe_backward reads: the routing
+ * (or the expert-choice selection), the grouping, the softmax, the
+ * pre-activations z and hidden
  * activations h of every row, and the gated expert outputs.  Same arguments
  * and outputs as moe_forward; ws must have moe_train_workspace_bytes(cfg)
  * bytes and stay untouched until the moe_backward call that consumes it.

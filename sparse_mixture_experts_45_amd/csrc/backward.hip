@@ -16,6 +16,9 @@
 //   dg     = <dy_t, o_r> = <dy_t, y_rows[r]> / g                     gate_grad_kernel
 //   dp     = renormalisation backward of dg, plus the balance term,
 //   dl     = p (dp - <p, dp>)                                       router_bwd_kernel
+// Expert choice is the same with gates p[t, e], no renormalisation, and each
+// token's rows found in the selection bitmaps (ec_router_bwd_kernel,
+// ec_dx_kernel).
 //   dW_g   = dl^T x, db_g = sum_t dl                                 router_wgrad_*
 //
 // The input-gradient pass reads the expert weights in their stored layout
@@ -258,20 +261,22 @@ __global__ __launch_bounds__(WM* WN * 64) void wgrad_kernel(WgradArgs a) {
 }
 
 // dg[t * k + i] = <dy_t, y_rows[r]> / gate_r for the pair's row r = inv[t * k + i]
-// (the expert output before gating); 0 for a dropped pair or a zero gate.  One
-// wave per pair.
+// (the expert output before gating); 0 for a dropped pair or a zero gate.
+// Without inv (expert choice) the pairs are the rows themselves: dg[r] for
+// token row_token[r].  One wave per pair.
 template <typename T>
 __global__ __launch_bounds__(256) void gate_grad_kernel(const T* __restrict__ dy,
                                                         const float* __restrict__ y_rows,
                                                         const int32_t* __restrict__ inv,
+                                                        const int32_t* __restrict__ row_token,
                                                         const float* __restrict__ row_gate,
                                                         int64_t pairs, int k, int d,
                                                         float* __restrict__ dg) {
   const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (pair >= pairs) return;
-  const int r = inv[pair];
-  const int64_t t = pair / k;
+  const int r = inv ? inv[pair] : static_cast<int>(pair);
+  const int64_t t = inv ? pair / k : row_token[r];
   float s = 0.f;
   if (r >= 0) {
     const float* yr = y_rows + static_cast<int64_t>(r) * d;
@@ -340,6 +345,39 @@ __global__ __launch_bounds__(64) void router_bwd_kernel(const float* __restrict_
   for (int e = lane; e < E; e += 64) s += p[e] * dp[e];
   s = wave_sum<float>(s);
   for (int e = lane; e < E; e += 64) dl[t * E + e] = p[e] * (dp[e] - s);
+}
+
+// Expert choice, one 64-lane block per token: dp[e] = the gate gradient of the
+// row where expert e took the token (from the selection bitmap; 0 if it did
+// not take it) + aux_dp[e], then dl = p (dp - <p, dp>) with p read from the
+// expert-major softmax.
+__global__ __launch_bounds__(64) void ec_router_bwd_kernel(const float* __restrict__ probsT,
+                                                           const uint32_t* __restrict__ sel,
+                                                           const int32_t* __restrict__ pre,
+                                                           const float* __restrict__ dgr,
+                                                           const float* __restrict__ aux_dp,
+                                                           int64_t Tn, int E, int W, int Ce,
+                                                           float* __restrict__ dl) {
+  __shared__ float dp[kMaxExperts];
+  __shared__ float pp[kMaxExperts];
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int64_t w = t >> 5;
+  const uint32_t bit = 1u << (t & 31);
+  float s = 0.f;
+  for (int e = lane; e < E; e += 64) {
+    const float p = probsT[static_cast<int64_t>(e) * Tn + t];
+    float g = aux_dp[e];
+    const uint32_t m = sel[static_cast<int64_t>(e) * W + w];
+    if (m & bit)
+      g += dgr[static_cast<int64_t>(e) * Ce + pre[static_cast<int64_t>(e) * W + w] +
+               __popc(m & (bit - 1u))];
+    dp[e] = g;
+    pp[e] = p;
+    s += p * g;
+  }
+  s = wave_sum<float>(s);
+  for (int e = lane; e < E; e += 64) dl[t * E + e] = pp[e] * (dp[e] - s);
 }
 
 // part[s][e][j] = sum over the tokens of chunk s of dl[t][e] x[t][j]; column
@@ -449,6 +487,101 @@ __global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dX,
   }
 }
 
+// Expert choice: dx[t] = sum over the experts that took t, in expert order, of
+// dX rows (+ the shared row) + sum_e dl[t][e] W_g[e].  Eight tokens per block:
+// each token's rows are found in the selection bitmaps and compacted into LDS
+// in expert order (ballots), then summed as in dx_kernel.
+template <typename T>
+__global__ __launch_bounds__(256) void ec_dx_kernel(const float* __restrict__ dX,
+                                                    const uint32_t* __restrict__ sel,
+                                                    const int32_t* __restrict__ pre, int W,
+                                                    int Ce, const float* __restrict__ dl,
+                                                    const float* __restrict__ Wg, int64_t Tn,
+                                                    int d, int E, int shared,
+                                                    T* __restrict__ dx) {
+  __shared__ float sdl[kDxTokens][kMaxExperts];
+  __shared__ int32_t rows[kDxTokens][kMaxExperts];
+  __shared__ int32_t nrow[kDxTokens];
+  __shared__ int32_t wcnt[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kDxTokens;
+  for (int i = tid; i < kDxTokens * E; i += 256) {
+    const int tt = i / E, e = i % E;
+    sdl[tt][e] = t0 + tt < Tn ? dl[(t0 + tt) * E + e] : 0.f;
+  }
+  for (int tt = 0; tt < kDxTokens; ++tt) {
+    const int64_t t = t0 + tt;
+    const int64_t w = t >> 5;
+    const uint32_t bit = 1u << (t & 31);
+    int n = 0;
+    for (int e0 = 0; e0 < E; e0 += 256) {
+      const int e = e0 + tid;
+      int row = -1;
+      if (t < Tn && e < E) {
+        const uint32_t m = sel[static_cast<int64_t>(e) * W + w];
+        const int32_t p = pre[static_cast<int64_t>(e) * W + w];
+        if (m & bit) row = e * Ce + p + __popc(m & (bit - 1u));
+      }
+      const uint64_t b = __ballot(row >= 0);
+      if (lane == 0) wcnt[wave] = __popcll(b);
+      __syncthreads();
+      int off = n, tot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        off += i < wave ? wcnt[i] : 0;
+        tot += wcnt[i];
+      }
+      if (row >= 0) rows[tt][off + __popcll(b & ((uint64_t(1) << lane) - 1))] = row;
+      n += tot;
+      __syncthreads();
+    }
+    if (tid == 0) nrow[tt] = n;
+  }
+  __syncthreads();
+  const int c = (blockIdx.y * 256 + tid) * 4;
+  if (c >= d) return;
+  float4 acc[kDxTokens];
+#pragma unroll
+  for (int tt = 0; tt < kDxTokens; ++tt) acc[tt] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int e = 0; e < E; ++e) {
+    const float4 wv = *reinterpret_cast<const float4*>(Wg + static_cast<int64_t>(e) * d + c);
+#pragma unroll
+    for (int tt = 0; tt < kDxTokens; ++tt) {
+      const float l = sdl[tt][e];
+      acc[tt].x += l * wv.x;
+      acc[tt].y += l * wv.y;
+      acc[tt].z += l * wv.z;
+      acc[tt].w += l * wv.w;
+    }
+  }
+  const int64_t rs0 = static_cast<int64_t>(E) * Ce;
+  for (int tt = 0; tt < kDxTokens; ++tt) {
+    const int64_t t = t0 + tt;
+    if (t >= Tn) break;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < nrow[tt]; ++i) {
+      const float4 u =
+          *reinterpret_cast<const float4*>(dX + static_cast<int64_t>(rows[tt][i]) * d + c);
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
+    if (shared) {
+      const float4 u = *reinterpret_cast<const float4*>(dX + (rs0 + t) * d + c);
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
+    v.x += acc[tt].x;
+    v.y += acc[tt].y;
+    v.z += acc[tt].z;
+    v.w += acc[tt].w;
+    store4<T>(dx + t * d + c, v);
+  }
+}
+
 // Zero fill (used where a gradient is zero by definition, e.g. T = 0).
 __global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int64_t words) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < words;
@@ -473,12 +606,18 @@ void run_bwd(const BwdArgs& b, int part, hipStream_t st) {
   const int ldh = b.F > b.Fs ? b.F : b.Fs;
   const int G = b.E + (b.Fs > 0 ? 1 : 0);
   if (part == kBwdRouter) {
-    const int64_t pairs = b.T * b.k;
-    gate_grad_kernel<T><<<static_cast<unsigned>(ceil_div(pairs, 4)), 256, 0, st>>>(
-        static_cast<const T*>(b.dy), b.y_rows, b.inv, b.row_gate, pairs, b.k, b.d, b.dg);
+    const int64_t pairs = b.ec ? static_cast<int64_t>(b.E) * b.Ce : b.T * b.k;
+    if (pairs > 0)
+      gate_grad_kernel<T><<<static_cast<unsigned>(ceil_div(pairs, 4)), 256, 0, st>>>(
+          static_cast<const T*>(b.dy), b.y_rows, b.ec ? nullptr : b.inv, b.row_token, b.row_gate,
+          pairs, b.k, b.d, b.dg);
     aux_prep_kernel<<<1, kMaxExperts, 0, st>>>(b.stat_part, b.nb, b.E, b.T, b.alpha, b.aux_dp);
-    router_bwd_kernel<<<static_cast<unsigned>(b.T), 64, 0, st>>>(
-        b.probs, b.topk_idx, b.topk_w, b.dg, b.aux_dp, b.E, b.k, b.renorm, b.dl);
+    if (b.ec)
+      ec_router_bwd_kernel<<<static_cast<unsigned>(b.T), 64, 0, st>>>(
+          b.probsT, b.sel, b.pre, b.dg, b.aux_dp, b.T, b.E, b.W, b.Ce, b.dl);
+    else
+      router_bwd_kernel<<<static_cast<unsigned>(b.T), 64, 0, st>>>(
+          b.probs, b.topk_idx, b.topk_w, b.dg, b.aux_dp, b.E, b.k, b.renorm, b.dl);
     if (b.dWg || b.dbg) {
       const dim3 grid(static_cast<unsigned>(ceil_div(b.d + 1, 256)),
                       static_cast<unsigned>(ceil_div(b.E, 8)), static_cast<unsigned>(b.wg_split));
@@ -493,8 +632,12 @@ void run_bwd(const BwdArgs& b, int part, hipStream_t st) {
   if (part == kBwdDx) {
     const dim3 grid(static_cast<unsigned>(ceil_div(b.T, kDxTokens)),
                     static_cast<unsigned>(ceil_div(b.d, 1024)));
-    dx_kernel<T><<<grid, 256, 0, st>>>(b.dX, b.inv, b.offsets, b.dl, b.Wg, b.T, b.d, b.E, b.k,
-                                       b.Fs > 0, static_cast<T*>(b.dx));
+    if (b.ec)
+      ec_dx_kernel<T><<<grid, 256, 0, st>>>(b.dX, b.sel, b.pre, b.W, b.Ce, b.dl, b.Wg, b.T, b.d,
+                                            b.E, b.Fs > 0, static_cast<T*>(b.dx));
+    else
+      dx_kernel<T><<<grid, 256, 0, st>>>(b.dX, b.inv, b.offsets, b.dl, b.Wg, b.T, b.d, b.E, b.k,
+                                         b.Fs > 0, static_cast<T*>(b.dx));
     return;
   }
   // kBwdExpertWeights: transposed operands, weight GEMMs, bias sums

@@ -143,15 +143,20 @@ struct BwdArgs {
   float alpha;                  // coefficient of the balance term
   const void *x, *dy;           // [T, d] layer dtype
   const float* Wg;              // [E, d]
-  const float* probs;           // [T, E] the forward's softmax
+  const float* probs;           // [T, E] the forward's softmax (token choice)
   const int32_t* topk_idx;      // [T, k]
   const float* topk_w;          // [T, k]
   const int32_t* inv;           // [T, k] row of each pair, -1 when dropped
+  // expert choice: rows e * Ce + j, gates p[t, e], the selection as bitmaps
+  int ec, Ce, W;                // W = ceil(T / 32)
+  const uint32_t* sel;          // [E, W] bit t of expert e: e took token t
+  const int32_t* pre;           // [E, W] tokens expert e took before word w
+  const float* probsT;          // [E, T] the forward's softmax
   const int32_t *offsets, *row_token;  // the forward's grouping
   const float* row_gate;        // [rows] gate of each row (1 for shared rows)
   const double* stat_part;      // [nb, E] the gate's per-block probability sums
   const float* y_rows;          // [rows, d] the forward's gated expert outputs
-  float *dg, *dl, *aux_dp;      // scratch [T, k], [T, E], [E]
+  float *dg, *dl, *aux_dp;      // scratch [T, k] (expert choice: [E * Ce]), [T, E], [E]
   float* wg_part;               // scratch [wg_split, E, d + 1]
   int wg_split;
   int64_t wg_chunk;             // tokens per split

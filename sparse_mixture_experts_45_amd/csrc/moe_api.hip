@@ -183,8 +183,9 @@ Layout layout(const moe_config* c, bool train = false) {
     const int64_t d = c->d_model, F = c->d_ff, Fs = c->shared_d_ff;
     const int64_t G = E + (Fs > 0 ? 1 : 0);
     L.Z = take(elt * L.rows_max * ldh);
-    L.probs = take(sizeof(float) * T * E);
-    L.dg = take(sizeof(float) * T * k);
+    L.probs = take(sizeof(float) * (ec ? 0 : T * E));  // expert choice keeps probsT
+    // gate gradients: one per (token, slot), or per routed row under expert choice
+    L.dg = take(sizeof(float) * (ec ? L.rows_max : T * k));
     L.dl = take(sizeof(float) * T * E);
     L.aux_dp = take(sizeof(float) * E);
     // router weight gradient: enough token chunks for ~512 blocks
@@ -304,8 +305,8 @@ moe_status forward_expert_choice(const moe_config* c, const Layout& L, const moe
   if ((s = hip_status(launch_expert_choice(a, probsT, st))) != MOE_OK) return s;
   if (c->T == 0) return MOE_OK;
   float* y_rows = reinterpret_cast<float*>(at(ws, L.y_rows));
-  if ((s = run_ffn(c, L, x, w, a.offsets, a.row_token, nullptr, nullptr, y_rows, ws, st, true)) !=
-      MOE_OK)
+  if ((s = run_ffn(c, L, x, w, a.offsets, a.row_token, nullptr, nullptr, y_rows, ws, st, true,
+                   L.train ? kPassForwardTrain : kPassForward)) != MOE_OK)
     return s;
   return hip_status(launch_combine_ec(c->T, c->d_model, c->n_experts, a.Ce, a.shared, c->dtype,
                                       y_rows, a.sel, a.pre, y, st));
@@ -485,7 +486,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
 }
 
 size_t moe_train_workspace_bytes(const moe_config* cfg) {
-  if (check_config(cfg) != MOE_OK || expert_choice(cfg)) return 0;
+  if (check_config(cfg) != MOE_OK) return 0;
   return layout(cfg, true).total;
 }
 
@@ -493,15 +494,19 @@ moe_status moe_forward_train(const moe_config* cfg, const moe_weights* w, const 
                              moe_stats* stats, void* ws, size_t ws_bytes, void* stream) {
   moe_status s = check_config(cfg);
   if (s != MOE_OK) return s;
-  if (expert_choice(cfg)) return MOE_ERR_UNSUPPORTED;
   if ((s = check_weights(cfg, w)) != MOE_OK) return s;
   if (cfg->T > 0 && (!x || !y || !aligned16(x) || !aligned16(y))) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(cfg, true);
   if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
   moe_stats none{};
   const moe_stats& o = stats ? *stats : none;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (expert_choice(cfg)) {
+    if (o.topk_idx || o.topk_w) return MOE_ERR_INVALID_ARG;
+    return forward_expert_choice(cfg, L, w, x, y, o, ws, st);
+  }
   if (o.ec_idx || o.ec_w) return MOE_ERR_INVALID_ARG;
-  return forward_token(cfg, L, w, x, y, o, ws, static_cast<hipStream_t>(stream));
+  return forward_token(cfg, L, w, x, y, o, ws, st);
 }
 
 moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x,
@@ -509,7 +514,6 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
                         size_t ws_bytes, void* stream) {
   moe_status s = check_config(cfg);
   if (s != MOE_OK) return s;
-  if (expert_choice(cfg)) return MOE_ERR_UNSUPPORTED;
   if ((s = check_weights(cfg, w)) != MOE_OK) return s;
   if (!grads) return MOE_ERR_INVALID_ARG;
   const moe_grads& g = *grads;
@@ -556,6 +560,12 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   b.dy = dy;
   b.Wg = w->Wg;
   b.probs = reinterpret_cast<const float*>(at(ws, L.probs));
+  b.ec = expert_choice(cfg) ? 1 : 0;
+  b.Ce = static_cast<int>(L.ec_C);
+  b.W = L.ec_W;
+  b.sel = reinterpret_cast<const uint32_t*>(at(ws, L.sel));
+  b.pre = reinterpret_cast<const int32_t*>(at(ws, L.pre));
+  b.probsT = reinterpret_cast<const float*>(at(ws, L.probsT));
   b.topk_idx = reinterpret_cast<const int32_t*>(at(ws, L.topk_idx));
   b.topk_w = reinterpret_cast<const float*>(at(ws, L.topk_w));
   b.inv = reinterpret_cast<const int32_t*>(at(ws, L.inv));

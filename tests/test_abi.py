@@ -135,12 +135,18 @@ def test_training_entry_points_check_arguments(lib):
     n = lib.moe_train_workspace_bytes(C.byref(c))
     assert n > lib.moe_workspace_bytes(C.byref(c)) > 0
     ec = cfg(routing="expert")
-    assert lib.moe_train_workspace_bytes(C.byref(ec)) == 0
+    ne = lib.moe_train_workspace_bytes(C.byref(ec))
+    assert ne > lib.moe_workspace_bytes(C.byref(ec)) > 0
     g = moe.moe_grads(dx=fake)
-    ne = lib.moe_workspace_bytes(C.byref(ec))
-    assert lib.moe_forward_train(C.byref(ec), C.byref(w), fake, fake, None, fake, ne, None) == -2
+    # expert choice trains too: its checks are the same (short workspace here),
+    # and the top-k outputs do not exist under it
+    assert lib.moe_forward_train(C.byref(ec), C.byref(w), fake, fake, None, fake, ne - 1,
+                                 None) == -3
+    st = moe.moe_stats(topk_w=fake)
+    assert lib.moe_forward_train(C.byref(ec), C.byref(w), fake, fake, C.byref(st), fake, ne,
+                                 None) == -1
     assert lib.moe_backward(C.byref(ec), C.byref(w), fake, fake, C.c_float(0.0), C.byref(g),
-                            fake, ne, None) == -2
+                            fake, ne - 1, None) == -3
     # missing grads struct, NaN coefficient, shared-expert grads without a shared
     # expert, misaligned dx, short workspace
     assert lib.moe_backward(C.byref(c), C.byref(w), fake, fake, C.c_float(0.0), None, fake, n,

@@ -191,3 +191,59 @@ def test_backward_workload(name, n_tok):
         check(shape, got["db2"][e][jl], ent["db2"], "db2[%d]" % e)
     del got
     torch.cuda.empty_cache()
+
+
+EC_SMALL = [
+    S("ec_f32_shared", dtype="f32", Fs=136, E=5, k=2, T=130, routing="expert"),
+    S("ec_bf16_k64", T=600, d=128, F=192, E=8, k=2, routing="expert"),
+    S("ec_bf16_capacity_relu", T=500, d=96, F=200, E=9, k=2, capacity=37, act="relu",
+      routing="expert"),
+    S("ec_capacity0_shared", T=60, d=64, F=64, E=4, k=2, capacity=0, Fs=64, routing="expert"),
+    S("ec_k_equals_E", T=77, d=64, F=64, E=3, k=3, routing="expert"),
+    S("ec_one_expert", T=65, d=64, F=64, E=1, k=1, routing="expert"),
+    S("ec_many_experts", T=200, d=64, F=32, E=300, k=3, router_bias="none", routing="expert"),
+    S("ec_uncached_keys", T=20000, d=64, F=64, E=8, k=1, routing="expert"),
+]
+
+
+@pytest.mark.parametrize("shape", EC_SMALL, ids=lambda s: s.name)
+def test_ec_backward_small(shape):
+    """Expert choice: every gradient against the oracle's (the token-choice
+    chain rule with gates p[t, e], no renormalisation, the selection fixed)."""
+    alpha = 0.7 if shape.E > 1 else 0.0
+    say("case", shape, "alpha", alpha)
+    inp = make_inputs(shape, 7)
+    dy_raw, dy64 = make_dy(shape)
+    want = oracle.ec_backward(shape, inp, dy64, alpha)
+    got, _ = gpu_backward(shape, device_inputs(inp), dy_device(shape, dy_raw), alpha)
+    errs = {n: check(shape, got[n], want[n], n) for n in got}
+    say("  rel-L2", " ".join("%s %.2g" % kv for kv in errs.items()))
+
+
+def test_ec_backward_workload():
+    """T=8192, d=1024, d_ff=4096, E=64, C=256: dx on sampled tokens, entries
+    of two experts' weight gradients."""
+    shape = workload("expert_choice_t8192_e64")
+    say("workload", shape)
+    inp = make_inputs(shape, 0)
+    dy_raw, dy64 = make_dy(shape, 3)
+    alpha = 0.5
+    r = oracle.ec_route(shape, inp)
+    s, rt = oracle.ec_slots(shape, r)
+    got, _ = gpu_backward(shape, device_inputs(inp), dy_device(shape, dy_raw), alpha,
+                          ["dx", "dW1", "db1", "dW2", "db2"])
+    toks = np.linspace(0, shape.T - 1, 16).astype(np.int64)
+    bt = oracle.backward_tokens(s, inp, dy64, toks, alpha, rt=rt)
+    rl = check(shape, got["dx"][toks], bt["dx"], "dx")
+    say("  dx rel-L2 on %d tokens: %.3g" % (len(toks), rl))
+    rng = np.random.default_rng(2)
+    for e in (0, shape.E - 1):
+        fl = np.sort(rng.choice(shape.F, 16, replace=False))
+        jl = np.sort(rng.choice(shape.d, 16, replace=False))
+        ent = oracle.backward_expert_entries(s, inp, dy64, e, fl, jl, rt=rt)
+        check(shape, got["dW1"][e][np.ix_(fl, jl)], ent["dW1"], "dW1[%d]" % e)
+        check(shape, got["dW2"][e][np.ix_(jl, fl)], ent["dW2"], "dW2[%d]" % e)
+        check(shape, got["db1"][e][fl], ent["db1"], "db1[%d]" % e)
+        check(shape, got["db2"][e][jl], ent["db2"], "db2[%d]" % e)
+    del got
+    torch.cuda.empty_cache()
