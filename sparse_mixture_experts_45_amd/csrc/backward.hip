@@ -1,4 +1,4 @@
-// Backward pass of the token-choice layer: gradients of
+// Backward pass of the layer: gradients of
 //   L = sum_t <dy_t, y_t> + alpha * balance
 // with the top-k selection and the capacity drops fixed (the training side of
 // the layer: botmartz "Load Balancing: The Hidden Challenge", total loss = task
@@ -16,10 +16,10 @@
 //   dg     = <dy_t, o_r> = <dy_t, y_rows[r]> / g                     gate_grad_kernel
 //   dp     = renormalisation backward of dg, plus the balance term,
 //   dl     = p (dp - <p, dp>)                                       router_bwd_kernel
+//   dW_g   = dl^T x, db_g = sum_t dl                                 router_wgrad_*
 // Expert choice is the same with gates p[t, e], no renormalisation, and each
 // token's rows found in the selection bitmaps (ec_router_bwd_kernel,
 // ec_dx_kernel).
-//   dW_g   = dl^T x, db_g = sum_t dl                                 router_wgrad_*
 //
 // The input-gradient pass reads the expert weights in their stored layout
 // (the grouped GEMM's transposed-B path).  The weight-gradient GEMMs contract
@@ -34,7 +34,7 @@ namespace moe {
 
 namespace {
 
-template <typename T>
+// Sum over the 64 lanes of a wave (xor tree, every lane gets the total).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void seg_sum_kernel(const T* __restrict__ in, 
   const T* row = in + static_cast<int64_t>(c) * ldi;
   float s = 0.f;
   for (int col = poff[g] + lane; col < poff[g + 1]; col += 64) s += to_f32<T>(row[col]);
-  s = wave_sum<T>(s);
+  s = wave_sum(s);
   if (lane == 0) o[c] = from_f32<T>(s);
 }
 
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(const T* __restrict__ dy
            v.w * to_f32<T>(dyt[c + 3]);
     }
   }
-  s = wave_sum<T>(s);
+  s = wave_sum(s);
   if (lane == 0) {
     const float g = r >= 0 ? row_gate[r] : 0.f;
     dg[pair] = g != 0.f ? s / g : 0.f;
@@ -337,13 +337,13 @@ __global__ __launch_bounds__(64) void router_bwd_kernel(const float* __restrict_
     gi = topk_w[t * k + lane];
     dgi = dg[t * k + lane];
   }
-  const float S = wave_sum<float>(pi), dot = wave_sum<float>(dgi * gi);
+  const float S = wave_sum(pi), dot = wave_sum(dgi * gi);
   __syncthreads();
   if (lane < k) dp[ei] += renorm ? (dgi - dot) / S : dgi;  // the k experts are distinct
   __syncthreads();
   float s = 0.f;
   for (int e = lane; e < E; e += 64) s += p[e] * dp[e];
-  s = wave_sum<float>(s);
+  s = wave_sum(s);
   for (int e = lane; e < E; e += 64) dl[t * E + e] = p[e] * (dp[e] - s);
 }
 
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(64) void ec_router_bwd_kernel(const float* __restri
     pp[e] = p;
     s += p * g;
   }
-  s = wave_sum<float>(s);
+  s = wave_sum(s);
   for (int e = lane; e < E; e += 64) dl[t * E + e] = pp[e] * (dp[e] - s);
 }
 
