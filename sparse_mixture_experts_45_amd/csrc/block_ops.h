@@ -33,7 +33,8 @@ __device__ inline int block_excl_scan(int v, int32_t* wsum, int& total) {
 // Group g (expert g, or the shared expert as group E) owns rows
 // off[g] .. off[g+1] and is cut into ceil(rows / BM) tiles of at most BM rows;
 // tiles are listed group by group, row-ascending.  `off` may sit in global
-// memory or LDS.
+// memory or LDS.  ntiles[0] gets the tile count, ntiles[1 .. kSplitSlots]
+// (the grouped GEMM's split counters) zero.
 __device__ inline void build_tile_list(const int32_t* off, int G, int BM,
                                        RowTile* __restrict__ tiles, int32_t* __restrict__ ntiles,
                                        int32_t* wsum) {
@@ -59,6 +60,8 @@ __device__ inline void build_tile_list(const int32_t* off, int G, int BM,
     }
   }
   if (g == 0) ntiles[0] = total;
+  // arrival counters of the grouped GEMM's K split start from zero
+  for (int i = threadIdx.x; i < kSplitSlots; i += blockDim.x) ntiles[1 + i] = 0;
 }
 
 // Sum of v over the block: xor-shuffle tree in each wave (every lane ends with

@@ -90,7 +90,33 @@ struct GemmArgs {
   void* aux;             // up (train): the pre-activations (T), same layout as out
   int64_t ldo;
   int act;
+  // K split of the tiles of a last, partly filled round (LDS-DMA kernel, one
+  // tile per block): kpart null or smax < 2 turns it off
+  float* kpart;   // partial tiles, BM * BN fp32 each
+  int32_t* ksem;  // one arrival counter per split tile, zero between launches
+  int slots;      // resident blocks of the launch (at most the partial tiles reserved)
+  int smax;       // parts per tile, at most
 };
+
+// Whole tiles and split tiles of a launch over `total` tiles: the tiles of a
+// last round that fills at most half of the `slots` resident blocks are cut
+// into S = min(smax, slots / R) parts (R = those tiles); D tiles run whole.
+// Blocks 0 .. D-1 take whole tiles; block D + i S + s takes part s of tile
+// D + i.  Every block computes the same plan from the same tile count.
+__device__ __forceinline__ void split_plan(int total, int slots, int smax, int* D, int* R,
+                                           int* S) {
+  *D = total;
+  *R = 0;
+  *S = 1;
+  if (smax < 2 || slots <= 0 || total <= 0) return;
+  const int rem = total % slots;
+  if (rem == 0) return;
+  const int s = min(smax, slots / rem);
+  if (s < 2) return;
+  *D = total - rem;
+  *R = rem;
+  *S = s;
+}
 
 // Tile id -> (row tile, n tile).  XCD i % 8 runs the blocks with id i, and
 // the ids are remapped so each XCD walks a contiguous range of the tile list.
@@ -386,10 +412,18 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
 
   extern __shared__ __align__(16) char smem[];
   __shared__ float gate_s[2][BM];
+  __shared__ int split_last;
 
   const int total = *a.ntiles * a.n_tiles_n;
+  int D = total, R = 0, S = 1;
+  if constexpr (!PERSIST) split_plan(total, a.slots, a.smax, &D, &R, &S);
   int t = blockIdx.x;
-  if (t >= total) return;
+  if (t >= D + R * S) return;
+  int part = -1;  // K part of a split tile, or -1 for a whole tile
+  if (t >= D) {
+    part = (t - D) % S;
+    t = D + (t - D) / S;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -487,6 +521,12 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
   }
   const char* abase = static_cast<const char*>(a.A);
   const char* bbase = reinterpret_cast<const char*>(cur.bw);
+  // K steps of this block: [kb, kb + ksteps) of the tile's K / BK
+  int kb = 0, ksteps = cur.K / BK;
+  if (part >= 0) {
+    kb = part * ksteps / S;
+    ksteps = (part + 1) * ksteps / S - kb;
+  }
   // bytes per k of B: 2 (K-contiguous rows) or one [K, N] row
   uint32_t bstep = BT ? static_cast<uint32_t>(cur.N) * 2 : 2;
   auto issue = [&](int stage, int k0) {
@@ -496,12 +536,9 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
                     static_cast<uint32_t>(k0) * (j < JA ? 2u : bstep),
                 smem + stage * STAGE + (wave + j * NW) * RPI * RB);
   };
-  {
-    const int KT = cur.K / BK;
 #pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-      if (p < KT) issue(p, p * BK);
-  }
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < ksteps) issue(p, (kb + p) * BK);
 
   int gb = 0;
   for (;;) {
@@ -524,7 +561,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    const int KT = cur.K / BK;
+    const int KT = ksteps;
     for (int kt = 0; kt < KT; ++kt) {
       // this lane's loads of stage kt have landed once at most the loads of the
       // later stages already issued (min(NS - 2, KT - 1 - kt) of them) are
@@ -558,7 +595,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
             if (tid + g * NT < BM) ngate[g] = gate_of(nxt, tid + g * NT);
         }
       }
-      if (kt + NS - 1 < KT) issue((kt + NS - 1) % NS, (kt + NS - 1) * BK);
+      if (kt + NS - 1 < KT) issue((kt + NS - 1) % NS, (kb + kt + NS - 1) * BK);
       const char* st = smem + (kt % NS) * STAGE;
       // fragments of k16 step s + 1 are read while the MFMAs of step s run
       bf16x8_t fa[2][MI], fb[2][NI];
@@ -603,6 +640,75 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     // landed: the last iteration waited for all of them).
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (!PERSIST && part >= 0) {
+      // Park this part's accumulators in its slot, lane-major (one 16-byte
+      // store per lane: 1 KiB per wave instruction).  The last part to arrive
+      // adds the S slots in part order (its own from registers) and goes on to
+      // the epilogue; the others are done.
+      constexpr int F4 = MI * NI * 4;  // float4 per lane
+      const int u = static_cast<int>(blockIdx.x) - D, ti = u / S;
+      float4* mine = reinterpret_cast<float4*>(a.kpart) + static_cast<int64_t>(u) * F4 * NT;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            mine[((i * NI + j) * 4 + c) * NT + tid] =
+                make_float4(acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
+                            acc[i][j][4 * c + 3]);
+      // Each wave waits until its stores have reached the L2; after the
+      // barrier one thread writes this XCD's L2 back (agent-scope release) and
+      // counts the arrival; the last part invalidates its stale L2 lines
+      // (agent-scope acquire) before any wave reads the other parts' slots.
+      // One release per part and one acquire per tile: each is a whole-L2
+      // operation, so no wave beyond the first does either.
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // the write-back has completed before the arrival is counted (an
+        // explicit wait: the compiler drops its own here, as its counter model
+        // already saw vmcnt at zero)
+        wait_vmcnt<0>();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const int before =
+            __hip_atomic_fetch_add(a.ksem + ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        split_last = before == S - 1;
+        if (before == S - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+      __syncthreads();
+      if (!split_last) return;
+      const float4* slots0 =
+          reinterpret_cast<const float4*>(a.kpart) + static_cast<int64_t>(ti) * S * F4 * NT;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          f32x16 sum;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) sum[q] = 0.f;
+          for (int p = 0; p < S; ++p) {
+            if (p == part) {
+#pragma unroll
+              for (int q = 0; q < 16; ++q) sum[q] += acc[i][j][q];
+            } else {
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const float4 v = slots0[(static_cast<int64_t>(p) * F4 + (i * NI + j) * 4 + c) * NT + tid];
+                sum[4 * c] += v.x;
+                sum[4 * c + 1] += v.y;
+                sum[4 * c + 2] += v.z;
+                sum[4 * c + 3] += v.w;
+              }
+            }
+          }
+          acc[i][j] = sum;
+        }
+      if (tid == 0) a.ksem[ti] = 0;  // ready for the next launch (kernel end orders it)
+    }
     if (has_next) {
 #pragma unroll
       for (int j = 0; j < JPW; ++j) src[j] = j < JA ? a_off(j, ntok[j]) : b_off(nxt, j);
@@ -683,6 +789,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     if (!has_next) break;
     cur = nxt;
     t = tn;
+    ksteps = cur.K / BK;
     gb ^= 1;
   }
 }
@@ -731,6 +838,8 @@ static GemmArgs up_args(const FfnArgs& f, int BN) {
   u.aux = f.Z;
   u.ldo = ldh;
   u.act = f.act;
+  u.kpart = f.kpart;
+  u.ksem = f.ksem;
   return u;
 }
 
@@ -779,10 +888,11 @@ static int cu_count() {
 }
 
 // Persistent launch: as many blocks as can be resident, capped by the tile
-// count; otherwise one block per tile.
+// count; otherwise one block per tile, plus up to `slots` more for the K split
+// of a last round (split: partial tiles reserved, 0 for none).
 template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int MODE,
           bool BT>
-static void launch_dma(const GemmArgs& g, int64_t tiles, hipStream_t st) {
+static void launch_dma(GemmArgs g, int64_t tiles, int split, hipStream_t st) {
   if (tiles <= 0) return;
   auto kern = grouped_gemm_dma_kernel<BM, BN, BK, NS, WM, WN, OCC, PERSIST, MODE, BT>;
   const size_t lds = static_cast<size_t>(NS) * (BM + BN) * BK * 2;
@@ -795,19 +905,29 @@ static void launch_dma(const GemmArgs& g, int64_t tiles, hipStream_t st) {
       b = 1;
     return b;
   }();
-  const int64_t grid =
-      PERSIST ? std::min<int64_t>(tiles, static_cast<int64_t>(cu_count()) * per_cu) : tiles;
+  g.slots = 0;
+  g.smax = 1;
+  if (!PERSIST && split > 0 && g.kpart && g.ksem) {
+    // the shared expert's K counts too when there is one
+    const bool sh = g.Ns > 0 && g.Ks > 0;
+    const int kt_min = (sh ? std::min(g.K, g.Ks) : g.K) / BK;
+    g.smax = std::min(kSplitMax, kt_min / kSplitMinSteps);
+    g.slots = std::min(cu_count() * per_cu, split);
+  }
+  const int64_t grid = PERSIST ? std::min<int64_t>(tiles, static_cast<int64_t>(cu_count()) * per_cu)
+                               : tiles + (g.smax > 1 ? g.slots : 0);
   kern<<<static_cast<unsigned>(grid), WM * WN * 64, lds, st>>>(g);
 }
 
 template <int BM, int BNU, int BND, int BK, int NS, int WM, int WN, int OCC, int PERSIST,
-          int WMD, int WND, int M1, bool BT>
+          int WMD, int WND, int SPLIT, int M1, bool BT>
 static void run_dma(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const GemmArgs u = up_args(f, BNU);
-  launch_dma<BM, BNU, BK, NS, WM, WN, OCC, PERSIST, M1, BT>(u, gp.tiles_max * u.n_tiles_n, st);
+  launch_dma<BM, BNU, BK, NS, WM, WN, OCC, PERSIST, M1, BT>(u, gp.tiles_max * u.n_tiles_n, SPLIT,
+                                                            st);
   const GemmArgs dn = down_args(f, BND);
   launch_dma<BM, BND, BK, NS, WMD, WND, OCC, PERSIST, kDown, BT>(
-      dn, gp.tiles_max * dn.n_tiles_n, st);
+      dn, gp.tiles_max * dn.n_tiles_n, SPLIT, st);
 }
 
 // The two GEMMs of one pass over the grouped rows; M1 is the first GEMM's mode,
@@ -820,8 +940,8 @@ static void run_pass(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
     case kGemmBf16Mid: run_generic<bf16, 64, 128, 128, 64, 1, 4, M1, BT>(gp, f, st); break;
     case kGemmBf16Small: run_generic<bf16, 32, 128, 128, 64, 1, 4, M1, BT>(gp, f, st); break;
 #define MOE_RUN_DMA(C)                                                                     \
-  run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN, C.OCC, C.PERSIST, C.WMD, C.WND, M1, BT>( \
-      gp, f, st)
+  run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN, C.OCC, C.PERSIST, C.WMD, C.WND, C.SPLIT, \
+          M1, BT>(gp, f, st)
     case kGemmDmaLarge: MOE_RUN_DMA(kDmaLarge); break;
     case kGemmDmaMid: MOE_RUN_DMA(kDmaMid); break;
     case kGemmDmaSmall: MOE_RUN_DMA(kDmaSmall); break;

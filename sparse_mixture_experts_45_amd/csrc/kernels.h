@@ -35,18 +35,33 @@ struct DmaCfg {
   // rows, up/down columns, K step, stages, the up GEMM's wave grid, the waves
   // per SIMD the register budget is sized for, whether blocks stay resident and
   // walk several tiles (1) or each block takes one tile (0), and the down
-  // GEMM's wave grid
-  int BM, BNU, BND, BK, NS, WM, WN, OCC, PERSIST, WMD, WND;
+  // GEMM's wave grid; SPLIT: partial tiles reserved for the K split below (0:
+  // the tier never splits)
+  int BM, BNU, BND, BK, NS, WM, WN, OCC, PERSIST, WMD, WND, SPLIT;
 };
-constexpr DmaCfg kDmaLarge{256, 256, 256, 64, 2, 2, 4, 2, 0, 2, 4};   // >= 768 rows per expert
-constexpr DmaCfg kDmaMid{128, 128, 128, 64, 2, 2, 4, 2, 0, 2, 4};     // >= 256
-constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 4, 1, 4, 2, 1, 1, 4};    // >= 48
-constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 4, 1, 4, 2, 0, 1, 4};   // fewer: weight streaming
+constexpr DmaCfg kDmaLarge{256, 256, 256, 64, 2, 2, 4, 2, 0, 2, 4, 256};  // >= 768 rows per expert
+constexpr DmaCfg kDmaMid{128, 128, 128, 64, 2, 2, 4, 2, 0, 2, 4, 512};    // >= 256
+constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 4, 1, 4, 2, 1, 1, 4, 0};     // >= 48
+constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 4, 1, 4, 2, 0, 1, 4, 0};    // fewer: weight streaming
+
+// K split of a last, partly filled round.  When a launch's tiles leave the
+// final round of resident blocks (`slots` of them) at most half full, each of
+// those R tiles is cut into S <= slots / R parts along K, run by S blocks; a
+// part parks its fp32 accumulators in a partial-tile slot, and the part that
+// arrives last (an arrival counter per tile) adds the S slots in part order and
+// runs the tile's epilogue.  The sum order is fixed, so results do not depend
+// on which part finishes first.  Counters are zeroed with every tile list and
+// reset by the last part.
+constexpr int kSplitMax = 4;       // parts per tile
+constexpr int kSplitMinSteps = 32;  // K steps per part, at least (the fences cost)
+constexpr int kSplitSlots = 512;   // counters kept after the tile count (>= every SPLIT)
+static_assert(kDmaLarge.SPLIT <= kSplitSlots && kDmaMid.SPLIT <= kSplitSlots, "split slots");
 
 struct GemmPlan {
   int shape;        // GemmShape
   int BM, BN_up, BN_down;
   int64_t tiles_max;  // upper bound on row tiles over all groups
+  int64_t kpart_floats;  // fp32 partial tiles of the K split (0: no split)
 };
 
 // Passes of the grouped-GEMM pair.  kPassDgrad is the input-gradient pass of
@@ -68,13 +83,15 @@ struct FfnArgs {
   void* H;           // [rows_max, max(F, Fs)] in dtype
   float* y_rows;     // [rows_max, d]
   RowTile* tiles;    // [tiles_max]
-  int32_t* ntiles;   // [1]
+  int32_t* ntiles;   // [1 + kSplitSlots]: the tile count, then the split counters
   float* row_gate;   // [rows_max]
   int tiles_ready;   // tiles, ntiles and row_gate already written by the dispatch
   int row_gates;     // topk_w holds one gate per routed row (expert choice)
   int pass;          // kPassForward, kPassForwardTrain (also keeps z in Z) or
                      // kPassDgrad (the roles above)
   void* Z;           // [rows_max, max(F, Fs)] pre-activations (train / dgrad)
+  float* kpart;      // [GemmPlan::kpart_floats] partial tiles of the K split, or null
+  int32_t* ksem;     // [kSplitSlots] arrival counters of split tiles (ntiles + 1)
 };
 
 // Everything the single-block dispatch reads and writes.

@@ -15,7 +15,7 @@ struct Layout {
   int64_t ec_C;      // tokens per expert under expert choice
   int ec_W;          // 32-token words of the expert-choice bitmaps
   size_t part, stat, hist, base, topk_idx, topk_w, counts, kept, offsets, row_token, row_slot,
-      inv, tiles, ntiles, row_gate, probsT, sel, pre, H, y_rows, total;
+      inv, tiles, ntiles, row_gate, probsT, sel, pre, H, y_rows, kpart, total;
   // training: what the forward keeps for the backward, and the backward's scratch
   bool train;
   int wg_split;
@@ -78,9 +78,12 @@ GemmPlan gemm_plan(const moe_config* c) {
   } else if (k64 && (avg >= 768 || ec_whole)) {
     g.shape = kGemmDmaLarge;
     g.BM = kDmaLarge.BM;
+    g.kpart_floats = int64_t(kDmaLarge.SPLIT) * kDmaLarge.BM *
+                     std::max(kDmaLarge.BNU, kDmaLarge.BND);
   } else if (k64 && avg >= 256) {
     g.shape = kGemmDmaMid;
     g.BM = kDmaMid.BM;
+    g.kpart_floats = int64_t(kDmaMid.SPLIT) * kDmaMid.BM * std::max(kDmaMid.BNU, kDmaMid.BND);
   } else if (k64 && avg >= 48) {
     g.shape = kGemmDmaSmall;
     g.BM = kDmaSmall.BM;
@@ -172,13 +175,14 @@ Layout layout(const moe_config* c, bool train = false) {
   L.row_slot = take(sizeof(int32_t) * (ec ? 0 : L.rows_max));
   L.inv = take(sizeof(int32_t) * (ec ? 0 : T * k));
   L.tiles = take(sizeof(RowTile) * L.gp.tiles_max);
-  L.ntiles = take(sizeof(int32_t));
+  L.ntiles = take(sizeof(int32_t) * (1 + kSplitSlots));  // count, split counters
   L.row_gate = take(sizeof(float) * L.rows_max);
   L.probsT = take(sizeof(float) * (ec ? E * T : 0));
   L.sel = take(sizeof(uint32_t) * E * L.ec_W);
   L.pre = take(sizeof(int32_t) * E * L.ec_W);
   L.H = take(elt * L.rows_max * ldh);
   L.y_rows = take(sizeof(float) * L.rows_max * c->d_model);
+  L.kpart = take(sizeof(float) * L.gp.kpart_floats);
   if (train) {
     const int64_t d = c->d_model, F = c->d_ff, Fs = c->shared_d_ff;
     const int64_t G = E + (Fs > 0 ? 1 : 0);
@@ -259,6 +263,8 @@ moe_status run_ffn(const moe_config* c, const Layout& L, const void* x, const mo
   f.row_gates = expert_choice(c) ? 1 : 0;
   f.pass = pass;
   f.Z = pass == kPassForwardTrain ? at(ws, L.Z) : nullptr;
+  f.kpart = L.gp.kpart_floats ? reinterpret_cast<float*>(at(ws, L.kpart)) : nullptr;
+  f.ksem = f.ntiles + 1;
   return hip_status(launch_ffn(L.gp, f, st));
 }
 
@@ -626,6 +632,8 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   f.row_gate = reinterpret_cast<float*>(at(ws, L.row_gate));
   f.tiles_ready = 1;
   f.pass = kPassDgrad;
+  f.kpart = L.gp.kpart_floats ? reinterpret_cast<float*>(at(ws, L.kpart)) : nullptr;
+  f.ksem = f.ntiles + 1;
   if ((s = hip_status(launch_ffn(L.gp, f, st))) != MOE_OK) return s;
   if (g.dx && (s = hip_status(launch_backward(b, kBwdDx, st))) != MOE_OK) return s;
   if (g.dW1 || g.db1 || g.dW2 || g.db2 || g.dWs1 || g.dbs1 || g.dWs2 || g.dbs2)

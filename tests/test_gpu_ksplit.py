@@ -1,0 +1,133 @@
+"""K split of a last, partly filled round of GEMM tiles (the LDS-DMA tiers that
+take one tile per block).  When a launch's tiles leave the final round of
+resident blocks at most half full, each tile of that round is cut into S parts
+along K; each part parks its fp32 partial tile and the last to arrive adds the
+S partials in part order before the epilogue.
+
+The shapes below are chosen so that the up- or the down-projection (or both)
+split, with S = 2, 3 and 4, with and without a shared expert, under token and
+expert choice; `planned_splits` restates the launch plan so each case asserts
+that it covers what it is meant to.  Each case is checked against the oracle
+(the forward output in full; the backward's dx on sampled tokens and entries
+of the weight and bias gradients), and twice in a row for bit equality: the
+partial sums are added in a fixed order.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_45_amd as moe
+from moe_synth import LayerShape, make_inputs
+from gpu_common import (check_ec_selection, check_routing, check_y, cfg_of, device_inputs,
+                        gpu_forward, gpu_forward_ec, say)
+from test_gpu_backward import check, dy_device, gpu_backward, make_dy
+
+pytestmark = pytest.mark.gpu
+
+# tiers of the LDS-DMA GEMM that split: rows and columns per tile, blocks per CU
+TIERS = {"large": (256, 256, 1), "mid": (128, 128, 2)}
+SPLIT_MAX, SPLIT_MIN_STEPS, BK = 4, 32, 64
+
+
+def tier_of(shape):
+    """The tile tier the library picks for this shape (bf16, K multiple of 64)."""
+    if shape.routing == "expert":
+        C = oracle.ec_capacity(shape)
+        rows = shape.E * C
+        whole = C >= 256 and (-(-C // 256) * 256 - C) * 8 <= C
+    else:
+        rows = shape.T * shape.k if shape.capacity < 0 else min(shape.T * shape.k,
+                                                                 shape.E * shape.capacity)
+        whole = False
+    avg = rows // shape.E
+    if avg >= 768 or whole:
+        return "large"
+    return "mid" if avg >= 256 else None
+
+
+def split_plan(total, slots, smax):
+    if smax < 2 or total <= 0 or total % slots == 0:
+        return 1
+    s = min(smax, slots // (total % slots))
+    return s if s >= 2 else 1
+
+
+def planned_splits(shape, kept):
+    """S of the up- and the down-projection launch, from the kept rows per expert."""
+    BM, BN, per_cu = TIERS[tier_of(shape)]
+    slots = torch.cuda.get_device_properties(0).multi_processor_count * per_cu
+    rt = sum(-(-int(r) // BM) for r in kept) + (-(-shape.T // BM) if shape.Fs else 0)
+    out = []
+    for N, K, Ks in ((max(shape.F, shape.Fs), shape.d, shape.d), (shape.d, shape.F, shape.Fs)):
+        kt = (min(K, Ks) if shape.Fs else K) // BK
+        out.append(split_plan(rt * -(-N // BN), slots, min(SPLIT_MAX, kt // SPLIT_MIN_STEPS)))
+    return tuple(out)
+
+
+def L(name, **kw):
+    base = dict(name=name, dtype="bf16", router_bias="normal")
+    base.update(kw)
+    return LayerShape(**base)
+
+
+# (shape, the (up, down) splits it is built for)
+CASES = [
+    (L("mid_up4", T=256, d=8192, F=256, E=2, k=2), (4, 1)),
+    (L("mid_down3", T=256, d=256, F=6144, E=2, k=2, act="relu"), (1, 3)),
+    (L("large_up2", T=768, d=4096, F=512, E=2, k=2), (2, 1)),
+    (L("large_down4_shared", T=768, d=256, F=8192, E=2, k=2, Fs=8192), (1, 4)),
+    (L("large_ec_up2", T=1024, d=4096, F=512, E=4, k=1, routing="expert"), (2, 1)),
+]
+
+
+@pytest.mark.parametrize("shape,splits", CASES, ids=[c[0].name for c in CASES])
+def test_split_forward(shape, splits):
+    say("case", shape, "splits", splits)
+    inp = make_inputs(shape, 21)
+    dev = device_inputs(inp)
+    if shape.routing == "expert":
+        C = oracle.ec_capacity(shape)
+        ref = oracle.ec_forward(shape, inp)
+        g = gpu_forward_ec(shape, dev, C)
+        check_ec_selection(shape, g, ref)
+    else:
+        ref = oracle.forward(shape, inp)
+        g = gpu_forward(shape, dev)
+        check_routing(shape, g, ref)
+    assert planned_splits(shape, g["kept"]) == splits
+    check_y(shape, g["y"], ref["y"])
+    # the same call again: bit-identical output
+    g2 = gpu_forward_ec(shape, dev, C) if shape.routing == "expert" else gpu_forward(shape, dev)
+    assert torch.equal(g["y_raw"].view(torch.int16), g2["y_raw"].view(torch.int16))
+
+
+@pytest.mark.parametrize("shape,splits", CASES[:4], ids=[c[0].name for c in CASES[:4]])
+def test_split_backward(shape, splits):
+    """The input-gradient pass runs the same GEMMs with K = d for dz and K =
+    d_ff for dz W1, so it splits where the forward does.  dx on sampled tokens
+    and entries of both experts' weight and bias gradients against the oracle
+    (computed one by one), then a second run bit for bit."""
+    say("case", shape)
+    inp = make_inputs(shape, 22)
+    dy_raw, dy64 = make_dy(shape, 5)
+    alpha = 0.2
+    dev = device_inputs(inp)
+    names = ["dx", "dW1", "db1", "dW2", "db2"]
+    got, _ = gpu_backward(shape, dev, dy_device(shape, dy_raw), alpha, names)
+    rt = oracle.route(shape, inp, with_probs=False)
+    toks = np.linspace(0, shape.T - 1, 24).astype(np.int64)
+    bt = oracle.backward_tokens(shape, inp, dy64, toks, alpha, rt=rt)
+    check(shape, got["dx"][toks], bt["dx"], "dx")
+    rng = np.random.default_rng(2)
+    for e in range(shape.E):
+        fl = np.sort(rng.choice(shape.F, 16, replace=False))
+        jl = np.sort(rng.choice(shape.d, 16, replace=False))
+        ent = oracle.backward_expert_entries(shape, inp, dy64, e, fl, jl, rt=rt)
+        check(shape, got["dW1"][e][np.ix_(fl, jl)], ent["dW1"], "dW1[%d]" % e)
+        check(shape, got["dW2"][e][np.ix_(jl, fl)], ent["dW2"], "dW2[%d]" % e)
+        check(shape, got["db1"][e][fl], ent["db1"], "db1[%d]" % e)
+        check(shape, got["db2"][e][jl], ent["db2"], "db2[%d]" % e)
+    again, _ = gpu_backward(shape, dev, dy_device(shape, dy_raw), alpha, names)
+    for n in got:
+        assert np.array_equal(got[n], again[n]), n
