@@ -341,83 +341,115 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(
   }
 }
 
-// The whole dispatch of a batch whose per-block bases fit in LDS, in one block
-// of kMaxExperts threads: load statistics (mean router probability per expert
-// and its unbiased variance, fp64), the scan of the gate's
-// per-block histogram, the GEMM row-tile list, and the scatter (16 waves walk
-// the 64-token blocks), which also writes every row's gate.  Same arithmetic
-// and the same outputs as the multi-kernel path.
+// The whole dispatch of a batch whose per-block histogram has at most
+// kDispatchLdsBases entries: one workgroup of kMaxExperts threads per 64-token
+// block (one for an empty batch).  Each workgroup reduces the gate's per-block
+// histogram to the expert totals and to its block's count of earlier pairs per
+// expert (thread (c, e) sums expert e over a range c of blocks), takes kept =
+// min(count, C) and the offsets, and its first wave ranks and scatters the
+// block's pairs and writes every kept row's gate.  Workgroup 0 also writes
+// counts, kept and offsets, the load statistics (mean router probability per
+// expert and its unbiased variance, fp64; cv^2 of the counts) and the GEMM
+// row-tile list.  Every workgroup derives the same integers from the same
+// histogram, so none waits for another, and the scattered stores spread over
+// as many compute units as there are blocks.  Same outputs as the multi-kernel
+// path.
 template <int KM>
-__global__ __launch_bounds__(1024) void dispatch_one_block_kernel(DispatchArgs a) {
-  __shared__ int32_t sbase[kDispatchLdsBases];
-  __shared__ int32_t sh[2 * kMaxExperts];
-  __shared__ int32_t wsum[kMaxExperts / 64];
-  __shared__ double wsd[kMaxExperts / 64];
+__global__ __launch_bounds__(1024) void dispatch_blocks_kernel(DispatchArgs a) {
+  __shared__ int32_t part[2][kMaxExperts];  // (expert, range) sums: earlier blocks, all blocks
+  __shared__ int32_t sbase[kMaxExperts];
   __shared__ int32_t skept[kMaxExperts];
   __shared__ int32_t soff[kMaxExperts + 2];
-  __shared__ int32_t sids[KM <= 4 ? 1 : kMaxExperts / 64][KM <= 4 ? 1 : kGateTokens * (kIdsK + 1)];
-  __shared__ float sgts[KM <= 4 ? 1 : kMaxExperts / 64][KM <= 4 ? 1 : kGateTokens * (kIdsK + 1)];
+  __shared__ int32_t wsum[kMaxExperts / 64];
+  __shared__ double wsd[kMaxExperts / 64];
+  __shared__ int32_t sids[KM <= 4 ? 1 : kGateTokens * (kIdsK + 1)];
+  __shared__ float sgts[KM <= 4 ? 1 : kGateTokens * (kIdsK + 1)];
   const int tid = threadIdx.x, wave = tid >> 6;
-  const int E = a.E, nb = a.nb;
-  constexpr int kWaves = kMaxExperts / 64;
-  // few slots: the ids and gates of the wave's first 64-token blocks (up to 8
-  // ids per lane) do not depend on the scan, so their loads go out first and
-  // overlap it
-  constexpr int PF = KM == 1 ? 8 : KM == 2 ? 4 : KM == 4 ? 2 : 0;
+  const int E = a.E, nb = a.nb, b = blockIdx.x;
+  const bool scatter = wave == 0 && b < nb;
+  // the block's ids and gates do not depend on the reduction: loaded first
   constexpr int KP = KM <= 4 ? KM : 1;
-  int mine[PF > 0 ? PF : 1][KP];
-  float wsel[PF > 0 ? PF : 1][KP];
-#pragma unroll
-  for (int p = 0; p < PF; ++p)
-    load_block<KP>(wave + p * kWaves, a.topk_idx, a.topk_w, a.T, a.k, mine[p], wsel[p]);
-
-  if (a.mean_prob || a.balance)
+  int mine[KP];
+  float wsel[KP];
+  if constexpr (KM <= 4) {
+    if (scatter) load_block<KP>(b, a.topk_idx, a.topk_w, a.T, a.k, mine, wsel);
+  }
+  if (b == 0 && (a.mean_prob || a.balance))
     load_stats(a.stat_part, nb, E, a.T, a.mean_prob, a.balance, wsd);
 
-  const int cnt = scan_hist<true>(a.hist, nb, E, a.T, a.capacity, a.shared, sbase, a.counts,
-                                  a.kept, a.offsets, skept, soff, sh, wsum);
-  if (a.cv2) counts_cv2(cnt, E, a.cv2, wsd);
-  build_tile_list(soff, E + (a.shared ? 1 : 0), a.BM, a.tiles, a.ntiles, wsum);
-
+  const int chunks = max(1, min(kMaxExperts / E, nb));
+  const int len = (nb + chunks - 1) / chunks;
+  const int c1 = tid / E, e1 = tid - c1 * E;
+  if (c1 < chunks) {
+    int before = 0, all = 0;
+    const int b0 = c1 * len, b1 = min(nb, b0 + len);
+#pragma unroll 8
+    for (int bb = b0; bb < b1; ++bb) {
+      const int h = a.hist[static_cast<int64_t>(bb) * E + e1];
+      all += h;
+      before += bb < b ? h : 0;
+    }
+    part[0][e1 * chunks + c1] = before;
+    part[1][e1 * chunks + c1] = all;
+  }
+  __syncthreads();
+  int cnt = 0, kp = 0;
+  if (tid < E) {
+    int before = 0;
+    for (int c = 0; c < chunks; ++c) {
+      before += part[0][tid * chunks + c];
+      cnt += part[1][tid * chunks + c];
+    }
+    kp = a.capacity < 0 ? cnt : min(cnt, a.capacity);
+    sbase[tid] = before;
+    skept[tid] = kp;
+  }
+  int ktot;
+  const int kx = block_excl_scan(kp, wsum, ktot);
+  if (tid < E) soff[tid] = kx;
+  if (tid == 0) {
+    soff[E] = ktot;
+    soff[E + 1] = ktot + (a.shared ? static_cast<int32_t>(a.T) : 0);
+  }
+  __syncthreads();
+  if (b == 0) {
+    if (tid < E) {
+      a.counts[tid] = cnt;
+      a.kept[tid] = kp;
+      a.offsets[tid] = kx;
+    }
+    if (tid == 0) {
+      a.offsets[E] = soff[E];
+      a.offsets[E + 1] = soff[E + 1];
+    }
+    if (a.cv2) counts_cv2(cnt, E, a.cv2, wsd);
+    build_tile_list(soff, E + (a.shared ? 1 : 0), a.BM, a.tiles, a.ntiles, wsum);
+  }
+  if (!scatter) return;
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
   if constexpr (KM <= 4) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int b = wave + p * kWaves;
-      if (b < nb)
-        scatter_block_few<KP>(b, mine[p], wsel[p], a.T, a.k, E, nbits, sbase + b * E, skept,
-                              soff, a.shared, a.row_token, a.row_slot, a.inv, a.row_gate);
-    }
-    for (int b = wave + PF * kWaves; b < nb; b += kWaves) {
-      load_block<KP>(b, a.topk_idx, a.topk_w, a.T, a.k, mine[0], wsel[0]);
-      scatter_block_few<KP>(b, mine[0], wsel[0], a.T, a.k, E, nbits, sbase + b * E, skept, soff,
-                            a.shared, a.row_token, a.row_slot, a.inv, a.row_gate);
-    }
+    scatter_block_few<KP>(b, mine, wsel, a.T, a.k, E, nbits, sbase, skept, soff, a.shared,
+                          a.row_token, a.row_slot, a.inv, a.row_gate);
+  } else if (a.k <= kIdsK) {
+    stage_ids(b, a.topk_idx, a.topk_w, a.T, a.k, sids, sgts);
+    scatter_block_any(b, sids, kIdsK + 1, sgts, a.T, a.k, E, nbits, sbase, skept, soff, a.shared,
+                      a.row_token, a.row_slot, a.inv, a.row_gate);
   } else {
-    for (int b = wave; b < nb; b += kWaves) {
-      if (a.k <= kIdsK) {
-        stage_ids(b, a.topk_idx, a.topk_w, a.T, a.k, sids[wave], sgts[wave]);
-        scatter_block_any(b, sids[wave], kIdsK + 1, sgts[wave], a.T, a.k, E, nbits,
-                          sbase + b * E, skept, soff, a.shared, a.row_token, a.row_slot, a.inv,
-                          a.row_gate);
-      } else {
-        const int64_t f0 = static_cast<int64_t>(b) * kGateTokens * a.k;
-        scatter_block_any(b, a.topk_idx + f0, a.k, a.topk_w + f0, a.T, a.k, E, nbits,
-                          sbase + b * E, skept, soff, a.shared, a.row_token, a.row_slot, a.inv,
-                          a.row_gate);
-      }
-    }
+    const int64_t f0 = static_cast<int64_t>(b) * kGateTokens * a.k;
+    scatter_block_any(b, a.topk_idx + f0, a.k, a.topk_w + f0, a.T, a.k, E, nbits, sbase, skept,
+                      soff, a.shared, a.row_token, a.row_slot, a.inv, a.row_gate);
   }
 }
 
-hipError_t launch_dispatch_one_block(const DispatchArgs& a, hipStream_t st) {
-#define MOE_ONE(KM) dispatch_one_block_kernel<KM><<<1, kMaxExperts, 0, st>>>(a)
-  if (a.k <= 1) MOE_ONE(1);
-  else if (a.k <= 2) MOE_ONE(2);
-  else if (a.k <= 4) MOE_ONE(4);
-  else MOE_ONE(kMaxTopK);  // slots rolled
-#undef MOE_ONE
+hipError_t launch_dispatch_blocks(const DispatchArgs& a, hipStream_t st) {
+  const unsigned grid = static_cast<unsigned>(a.nb > 0 ? a.nb : 1);
+#define MOE_BLOCKS(KM) dispatch_blocks_kernel<KM><<<grid, kMaxExperts, 0, st>>>(a)
+  if (a.k <= 1) MOE_BLOCKS(1);
+  else if (a.k <= 2) MOE_BLOCKS(2);
+  else if (a.k <= 4) MOE_BLOCKS(4);
+  else MOE_BLOCKS(kMaxTopK);  // slots rolled
+#undef MOE_BLOCKS
   return hipGetLastError();
 }
 

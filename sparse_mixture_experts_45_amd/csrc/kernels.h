@@ -109,9 +109,12 @@ struct DispatchArgs {
   float *mean_prob, *balance, *cv2;  // optional
 };
 
-// per-block bases of the single-block dispatch live in LDS: nb * E must fit
+// Every workgroup of the fused dispatch reads the whole per-block histogram
+// (nb * E ints); up to this size that costs less than separate scan and
+// scatter launches.  kDispatchLdsBases also bounds the LDS copy of the
+// multi-kernel path's scan.
 constexpr int kDispatchLdsBases = 8192;
-inline bool dispatch_one_block(int64_t nb, int E) { return nb * E <= kDispatchLdsBases; }
+inline bool dispatch_fused(int64_t nb, int E) { return nb * E <= kDispatchLdsBases; }
 
 hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const float* Wg,
                          const float* bg, float* part, int32_t* topk_idx, float* topk_w,
@@ -123,7 +126,7 @@ hipError_t launch_dispatch(int64_t T, int E, int k, int capacity, int shared, in
                            int32_t* counts, int32_t* kept, int32_t* offsets, int32_t* row_token,
                            int32_t* row_slot, int32_t* inv, float* cv2, hipStream_t st);
 
-hipError_t launch_dispatch_one_block(const DispatchArgs& a, hipStream_t st);
+hipError_t launch_dispatch_blocks(const DispatchArgs& a, hipStream_t st);
 
 // Everything the expert-choice selection and its finishing block read and write.
 struct EcArgs {

@@ -337,8 +337,9 @@ moe_status forward_token(const moe_config* cfg, const Layout& L, const moe_weigh
   float* y_rows = reinterpret_cast<float*>(at(ws, L.y_rows));
 
   double* stat_part = reinterpret_cast<double*>(at(ws, L.stat));
-  // small batches: the whole dispatch (and the load statistics) in one block
-  const bool one = dispatch_one_block(L.rp.nb, cfg->n_experts);
+  // up to kDispatchLdsBases histogram entries: the whole dispatch (and the load
+  // statistics) in one launch
+  const bool one = dispatch_fused(L.rp.nb, cfg->n_experts);
   if ((s = hip_status(launch_router(L.rp, x, cfg->dtype, w->Wg, w->bg,
                                     reinterpret_cast<float*>(at(ws, L.part)), topk_idx, topk_w,
                                     L.train ? reinterpret_cast<float*>(at(ws, L.probs)) : nullptr,
@@ -382,7 +383,7 @@ moe_status forward_token(const moe_config* cfg, const Layout& L, const moe_weigh
     d.mean_prob = o.mean_prob;
     d.balance = o.balance;
     d.cv2 = o.cv2;
-    if ((s = hip_status(launch_dispatch_one_block(d, st))) != MOE_OK) return s;
+    if ((s = hip_status(launch_dispatch_blocks(d, st))) != MOE_OK) return s;
   } else if ((s = hip_status(launch_dispatch(cfg->T, cfg->n_experts, cfg->top_k, cfg->capacity,
                                              cfg->shared_d_ff > 0, L.rp.nb, topk_idx, false,
                                              hist, reinterpret_cast<int32_t*>(at(ws, L.base)),
