@@ -290,6 +290,18 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
     const float bv = bias ? to_f32(bias[n]) : 0.f;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
+      // kDz: the 16 pre-activations are loaded before any result is stored
+      // (a load after a possibly aliasing store waits out a memory latency)
+      float zr[MODE == kDz ? 16 : 1];
+      if constexpr (MODE == kDz) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m = wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+          // rows past the tile read its last row (no branch); unused
+          zr[q] = to_f32<T>(
+              static_cast<const T*>(a.out)[static_cast<int64_t>(row0 + min(m, rows - 1)) * a.ldo + n]);
+        }
+      }
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int m = wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
@@ -301,10 +313,9 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
           static_cast<T*>(a.out)[o] = from_f32<T>(h);
           if constexpr (MODE == kUpTrain) static_cast<T*>(a.aux)[o] = from_f32<T>(z);
         } else if constexpr (MODE == kDz) {
-          T* zp = static_cast<T*>(a.out) + o;
-          const float pre = to_f32<T>(*zp);
+          const float pre = zr[q];
           const float da = (a.act == MOE_ACT_RELU) ? (pre > 0.f ? 1.f : 0.f) : gelu_erf_grad(pre);
-          *zp = from_f32<T>(gate_s[m] * z * da);
+          static_cast<T*>(a.out)[o] = from_f32<T>(gate_s[m] * z * da);
         } else {
           static_cast<float*>(a.out)[o] = gate_s[m] * z;
         }
@@ -749,7 +760,29 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+       for (int qh = 0; qh < 16; qh += 8) {
+        // kDz: eight rows' pre-activations are loaded before any of their
+        // results is stored (a load after a possibly aliasing store would wait
+        // out a full memory latency)
+        uint16_t zr[MODE == kDz ? 8 : 1][MODE == kDz ? NI : 1];
+        if constexpr (MODE == kDz) {
+#pragma unroll
+          for (int qq = 0; qq < 8; ++qq) {
+            const int q = qh + qq;
+            // partial tiles read a clamped valid element (no branch); the
+            // value is used only where the result is stored
+            const int m = wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+            const uint32_t orow = static_cast<uint32_t>(CHK ? min(m, cur.rows - 1) : m) * ldo;
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+              const int nc = CHK ? min(ncol[j], cur.N - 1 - cur.n0) : ncol[j];
+              zr[qq][j] = *reinterpret_cast<const uint16_t*>(
+                  obase + (orow + static_cast<uint32_t>(nc)) * OE);
+            }
+          }
+        }
+#pragma unroll
+        for (int q = qh; q < qh + 8; ++q) {
           const int m = wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
           if (CHK && m >= cur.rows) continue;
           const uint32_t orow = static_cast<uint32_t>(m) * ldo;
@@ -765,21 +798,25 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
               if constexpr (MODE == kUpTrain)
                 *reinterpret_cast<uint16_t*>(xbase + off) = f32_to_bf16(z);
             } else if constexpr (MODE == kDz) {
-              uint16_t* zp = reinterpret_cast<uint16_t*>(obase + off);
-              const float pre = bf16_to_f32(*zp);
+              const float pre = bf16_to_f32(zr[q - qh][j]);
               const float da = RELU ? (pre > 0.f ? 1.f : 0.f) : gelu_erf_grad(pre);
-              *zp = f32_to_bf16(g * z * da);
+              *reinterpret_cast<uint16_t*>(obase + off) = f32_to_bf16(g * z * da);
             } else {
               *reinterpret_cast<float*>(obase + off) = g * z;
             }
           }
         }
+       }
         // one 32-row block at a time: keeps the epilogue's temporaries few
         __builtin_amdgcn_sched_barrier(0);
       }
     };
+    // A tile whose columns all lie past its group's N (the shared expert's
+    // narrower projection) stores nothing; the clamps of the partial-tile
+    // path assume at least one valid column.
     const bool full = cur.rows == BM && cur.n0 + BN <= cur.N;
-    if ((MD::fwd_act || MODE == kDz) && a.act == MOE_ACT_RELU) {
+    if (cur.n0 >= cur.N) {
+    } else if ((MD::fwd_act || MODE == kDz) && a.act == MOE_ACT_RELU) {
       if (full) epilogue(std::false_type{}, std::true_type{});
       else epilogue(std::true_type{}, std::true_type{});
     } else {
