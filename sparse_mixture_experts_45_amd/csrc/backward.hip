@@ -590,8 +590,17 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int
 }
 
 template <typename T>
-void run_wgrad(const WgradArgs& w, int groups, hipStream_t st) {
+void run_wgrad(const WgradArgs& w, int groups, int gshape, hipStream_t st) {
   if (groups <= 0 || w.M <= 0 || w.N <= 0) return;
+  if constexpr (sizeof(T) == 2) {
+    // bf16 with the forward on the 256- or 128-row LDS-DMA tiers: the same
+    // tiles, with each group's K range
+    const WgradGemm g{w.A, w.lda, w.B, w.ldb, w.poff, w.g0, groups, w.M, w.N, w.C};
+    if (wgrad_dma_fits(gshape, g)) {
+      (void)launch_wgrad_dma(gshape, g, st);
+      return;
+    }
+  }
   constexpr bool B16 = sizeof(T) == 2;
   constexpr int BM = B16 ? 128 : 64, BN = B16 ? 128 : 64, BK = B16 ? 64 : 32;
   WgradArgs a = w;
@@ -665,22 +674,22 @@ void run_bwd(const BwdArgs& b, int part, hipStream_t st) {
   if (b.dW1) {  // dW1[e] [F, d] = dz^T x
     w.A = b.ZT, w.lda = b.Rp, w.B = b.XT, w.ldb = b.Rp, w.g0 = 0, w.M = b.F, w.N = b.d;
     w.C = b.dW1;
-    run_wgrad<T>(w, b.E, st);
+    run_wgrad<T>(w, b.E, b.gshape, st);
   }
   if (b.dWs1 && b.Fs > 0) {
     w.A = b.ZT, w.lda = b.Rp, w.B = b.XT, w.ldb = b.Rp, w.g0 = b.E, w.M = b.Fs, w.N = b.d;
     w.C = b.dWs1;
-    run_wgrad<T>(w, 1, st);
+    run_wgrad<T>(w, 1, b.gshape, st);
   }
   if (b.dW2) {  // dW2[e] [d, F] = (gate dy)^T h
     w.A = b.DT, w.lda = b.Rp, w.B = b.HT, w.ldb = b.Rp, w.g0 = 0, w.M = b.d, w.N = b.F;
     w.C = b.dW2;
-    run_wgrad<T>(w, b.E, st);
+    run_wgrad<T>(w, b.E, b.gshape, st);
   }
   if (b.dWs2 && b.Fs > 0) {
     w.A = b.DT, w.lda = b.Rp, w.B = b.HT, w.ldb = b.Rp, w.g0 = b.E, w.M = b.d, w.N = b.Fs;
     w.C = b.dWs2;
-    run_wgrad<T>(w, 1, st);
+    run_wgrad<T>(w, 1, b.gshape, st);
   }
   if (b.db1 || b.dbs1)
     seg_sum_kernel<T><<<dim3(static_cast<unsigned>(ceil_div(ldh, 4)), G), 256, 0, st>>>(

@@ -63,10 +63,13 @@ __device__ __forceinline__ float gelu_erf_grad(float z) {
 //             of the row (1 when row_gate is null)
 //   kDz       A = upstream-gradient rows gathered by row_token; out holds the
 //             pre-activation z on entry and gets gate * C * act'(z) (in place)
-enum GemmMode { kUp = 0, kDown = 1, kDz = 2, kUpTrain = 3 };
+//   kWgrad    weight gradients: A [M, lda] and B [N, ldb] (transposed grouped
+//             activations), group g's K columns poff[g0 + g] .. poff[g0 + g + 1];
+//             out [groups, M, N] (layer dtype) = C, no bias, no gate, no tile list
+enum GemmMode { kUp = 0, kDown = 1, kDz = 2, kUpTrain = 3, kWgrad = 4 };
 template <int MODE>
 struct ModeOf {
-  static constexpr bool gather = MODE != kDown;
+  static constexpr bool gather = MODE != kDown && MODE != kWgrad;
   static constexpr bool gated = MODE == kDown || MODE == kDz;
   static constexpr bool out_f32 = MODE == kDown;
   static constexpr bool fwd_act = MODE == kUp || MODE == kUpTrain;
@@ -96,6 +99,10 @@ struct GemmArgs {
   int32_t* ksem;  // one arrival counter per split tile, zero between launches
   int slots;      // resident blocks of the launch (at most the partial tiles reserved)
   int smax;       // parts per tile, at most
+  // kWgrad only (E = groups, W = B, out = C [groups, M, N], ldo = N)
+  const int32_t* poff;
+  int g0, M, tiles_m;
+  int64_t ldb;
 };
 
 // Whole tiles and split tiles of a launch over `total` tiles: the tiles of a
@@ -118,14 +125,19 @@ __device__ __forceinline__ void split_plan(int total, int slots, int smax, int* 
   *S = s;
 }
 
-// Tile id -> (row tile, n tile).  XCD i % 8 runs the blocks with id i, and
-// the ids are remapped so each XCD walks a contiguous range of the tile list.
+// XCD i % 8 runs the blocks with id i: block ids are remapped so each XCD walks
+// a contiguous range of [0, total).
+__device__ __forceinline__ int xcd_order(int pid, int total) {
+  const int q = total / kXcd, r = total % kXcd;
+  const int x = pid % kXcd, local = pid / kXcd;
+  return x * q + min(x, r) + local;  // bijection onto [0, total)
+}
+
+// Tile id -> (row tile, n tile), each XCD on a contiguous range of the tile list.
 __device__ __forceinline__ void decode_tile(const GemmArgs& a, int pid, int total, int* rt,
                                             int* nt) {
   const int NT = a.n_tiles_n;
-  const int q = total / kXcd, r = total % kXcd;
-  const int x = pid % kXcd, local = pid / kXcd;
-  const int v = x * q + min(x, r) + local;  // bijection onto [0, total)
+  const int v = xcd_order(pid, total);
   const RowTile& t = a.tiles[v / NT];
   const int m = t.count;
   const int ve = v - t.first * NT;           // index inside the group
@@ -405,6 +417,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
   // the input-gradient pass reads the expert weights; its tile sits in LDS as
   // BK rows of BN values and MFMA fragments come from transposing LDS reads.
   static_assert(!BT || BN >= 128, "transposed B tile: at least 16 chunks per row");
+  static_assert(MODE != kWgrad || (!PERSIST && !BT), "weight gradients: one tile per block");
   constexpr int NW = WM * WN;
   constexpr int NT = NW * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -425,7 +438,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
   __shared__ float gate_s[2][BM];
   __shared__ int split_last;
 
-  const int total = *a.ntiles * a.n_tiles_n;
+  const int total = MODE == kWgrad ? a.E * a.tiles_m * a.n_tiles_n : *a.ntiles * a.n_tiles_n;
   int D = total, R = 0, S = 1;
   if constexpr (!PERSIST) split_plan(total, a.slots, a.smax, &D, &R, &S);
   int t = blockIdx.x;
@@ -463,10 +476,34 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     int row0, rows, n0, N, K;
     const bf16* bw;    // weight rows of this group
     const bf16* bias;  // bias of this group, or null
+    int ldb;           // elements between B rows (K, or ldb for kWgrad)
+    uint32_t aoff;     // bytes from A to the tile's first K column (kWgrad)
+    int64_t ooff;      // output elements before the group's matrix (kWgrad)
   };
   // Tile fields are the same for the whole block: readfirstlane keeps them in
   // scalar registers (the vector register budget is tight).
   auto decode = [&](int tt) {
+    Tile c;
+    if constexpr (MODE == kWgrad) {
+      // group-major, row tiles fastest: neighbouring blocks share B's column tile
+      const int per = a.tiles_m * a.n_tiles_n;
+      const int v = xcd_order(tt, total);
+      const int g = v / per, rr = v - g * per;
+      const int nt = rr / a.tiles_m, mt = rr - nt * a.tiles_m;
+      const int k0 = __builtin_amdgcn_readfirstlane(a.poff[a.g0 + g]);
+      const int k1 = __builtin_amdgcn_readfirstlane(a.poff[a.g0 + g + 1]);
+      c.row0 = mt * BM;
+      c.rows = min(BM, a.M - c.row0);
+      c.n0 = nt * BN;
+      c.N = a.N;
+      c.K = k1 - k0;
+      c.bw = static_cast<const bf16*>(a.W) + k0;
+      c.bias = nullptr;
+      c.ldb = static_cast<int>(a.ldb);
+      c.aoff = static_cast<uint32_t>(k0) * 2u;
+      c.ooff = static_cast<int64_t>(g) * a.M * a.N;
+      return c;
+    }
     int rt, nt;
     decode_tile(a, tt, total, &rt, &nt);
     rt = __builtin_amdgcn_readfirstlane(rt);
@@ -474,7 +511,6 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     const RowTile& rtile = a.tiles[rt];
     const int group = __builtin_amdgcn_readfirstlane(rtile.group);
     const bool sh = (group == a.E);
-    Tile c;
     c.row0 = __builtin_amdgcn_readfirstlane(rtile.row0);
     c.rows = __builtin_amdgcn_readfirstlane(rtile.rows);
     c.n0 = nt * BN;
@@ -484,6 +520,9 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
            (sh ? 0 : static_cast<int64_t>(group) * c.N * c.K);
     c.bias = static_cast<const bf16*>(sh ? a.bias_sh : a.bias);
     if (c.bias && !sh) c.bias += static_cast<int64_t>(group) * c.N;
+    c.ldb = c.K;
+    c.aoff = 0;
+    c.ooff = 0;
     return c;
   };
   // token row (up-projection) or H row (down-projection) behind A row r
@@ -513,7 +552,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
       const int r = (wave + j * NW) * RPI + lr;
       const int chunk = (lane % CPR) ^ swz<CPR>(r);
       const int nn = min(c.n0 + r - BM, c.N - 1);
-      return static_cast<uint32_t>(nn) * static_cast<uint32_t>(c.K * 2) + chunk * 16;
+      return static_cast<uint32_t>(nn) * static_cast<uint32_t>(c.ldb * 2) + chunk * 16;
     }
   };
   auto gate_of = [&](const Tile& c, int m) -> float {
@@ -530,7 +569,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     for (int g = 0; g < GPT; ++g)
       if (tid + g * NT < BM) gate_s[0][tid + g * NT] = gate_of(cur, tid + g * NT);
   }
-  const char* abase = static_cast<const char*>(a.A);
+  const char* abase = static_cast<const char*>(a.A) + cur.aoff;
   const char* bbase = reinterpret_cast<const char*>(cur.bw);
   // K steps of this block: [kb, kb + ksteps) of the tile's K / BK
   int kb = 0, ksteps = cur.K / BK;
@@ -749,7 +788,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     }
     constexpr int OE = MD::out_f32 ? 4 : 2;  // output element bytes
     char* obase = static_cast<char*>(a.out) +
-                  (static_cast<int64_t>(cur.row0) * a.ldo + cur.n0) * OE;
+                  (cur.ooff + static_cast<int64_t>(cur.row0) * a.ldo + cur.n0) * OE;
     char* xbase = MODE == kUpTrain ? static_cast<char*>(a.aux) +
                                          (static_cast<int64_t>(cur.row0) * a.ldo + cur.n0) * OE
                                    : nullptr;
@@ -801,6 +840,8 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
               const float pre = bf16_to_f32(zr[q - qh][j]);
               const float da = RELU ? (pre > 0.f ? 1.f : 0.f) : gelu_erf_grad(pre);
               *reinterpret_cast<uint16_t*>(obase + off) = f32_to_bf16(g * z * da);
+            } else if constexpr (MODE == kWgrad) {
+              *reinterpret_cast<uint16_t*>(obase + off) = f32_to_bf16(z);
             } else {
               *reinterpret_cast<float*>(obase + off) = g * z;
             }
@@ -985,6 +1026,48 @@ static void run_pass(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
     default: MOE_RUN_DMA(kDmaSkinny); break;
 #undef MOE_RUN_DMA
   }
+}
+
+template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC>
+static void run_wgrad_dma(const WgradGemm& w, hipStream_t st) {
+  GemmArgs g{};
+  g.A = w.A;
+  g.lda = w.lda;
+  g.W = w.B;
+  g.ldb = w.ldb;
+  g.poff = w.poff;
+  g.g0 = w.g0;
+  g.E = w.groups;
+  g.M = w.M;
+  g.N = w.N;
+  g.out = w.C;
+  g.ldo = w.N;
+  g.tiles_m = static_cast<int>(ceil_div(w.M, BM));
+  g.n_tiles_n = static_cast<int>(ceil_div(w.N, BN));
+  launch_dma<BM, BN, BK, NS, WM, WN, OCC, 0, kWgrad, false>(
+      g, static_cast<int64_t>(w.groups) * g.tiles_m * g.n_tiles_n, 0, st);
+}
+
+bool wgrad_dma_fits(int shape, const WgradGemm& w) {
+  if (shape != kGemmDmaLarge && shape != kGemmDmaMid) return false;
+  // 16-byte LDS-DMA chunks along K, 32-bit byte offsets inside A and B
+  const bool k16 = w.lda % 8 == 0 && w.ldb % 8 == 0 &&
+                   reinterpret_cast<uintptr_t>(w.A) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(w.B) % 16 == 0;
+  return k16 && int64_t(w.M) * w.lda * 2 < (int64_t(1) << 31) &&
+         int64_t(w.N) * w.ldb * 2 < (int64_t(1) << 31) && int64_t(w.M) * w.N < (int64_t(1) << 31);
+}
+
+hipError_t launch_wgrad_dma(int shape, const WgradGemm& w, hipStream_t st) {
+  if (w.groups <= 0 || w.M <= 0 || w.N <= 0) return hipSuccess;
+  if (shape == kGemmDmaLarge) {
+    constexpr DmaCfg C = kDmaLarge;
+    run_wgrad_dma<C.BM, C.BNU, C.BK, C.NS, C.WM, C.WN, C.OCC>(w, st);
+  } else {
+    constexpr DmaCfg C = kDmaMid;
+    run_wgrad_dma<C.BM, C.BNU, C.BK, C.NS, C.WM, C.WN, C.OCC>(w, st);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {

@@ -151,6 +151,22 @@ hipError_t launch_combine_ec(int64_t T, int d, int E, int Ce, int shared, int dt
 
 hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& a, hipStream_t st);
 
+// Weight gradients on the LDS-DMA GEMM (bf16): C[g] [M, N] = A[:, Kg] B[:, Kg]^T
+// for groups g = 0 .. groups-1, Kg = columns poff[g0 + g] .. poff[g0 + g + 1]
+// (multiples of 64) of A [M, lda] and B [N, ldb].  `shape` is the forward's
+// tile tier (large or mid); wgrad_dma_fits says whether this path applies.
+struct WgradGemm {
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  const int32_t* poff;
+  int g0, groups, M, N;
+  void* C;
+};
+bool wgrad_dma_fits(int shape, const WgradGemm& w);
+hipError_t launch_wgrad_dma(int shape, const WgradGemm& w, hipStream_t st);
+
 // Backward (token choice).  moe_backward enqueues, in order: kBwdRouter (gate
 // gradients, the balance term,
 // router-score gradients dl, dW_g and db_g), the input-gradient GEMM pass
@@ -160,6 +176,7 @@ enum { kBwdRouter = 1, kBwdDx = 2, kBwdExpertWeights = 3 };
 struct BwdArgs {
   int64_t T;
   int d, F, E, k, Fs, dtype, renorm, nb;
+  int gshape;                   // the forward's GEMM tile tier (GemmShape)
   float alpha;                  // coefficient of the balance term
   const void *x, *dy;           // [T, d] layer dtype
   const float* Wg;              // [E, d]
