@@ -12,11 +12,14 @@
 //   1. per 64-token block, count pairs per expert (LDS integer atomics:
 //      counts do not depend on order) -- or take the counts the gate kernel
 //      already produced;
-//   2. one block scans: counts, kept = min(counts, C), offsets = exclusive scan
-//      of kept, and for every block the number of earlier pairs per expert;
+//   2. scan: counts, kept = min(counts, C), offsets = exclusive scan of kept,
+//      and for every block the number of earlier pairs per expert;
 //   3. one wave per 64-token block ranks each pair among the earlier tokens of
 //      the block with the same expert (ballot match on the expert id bits),
 //      adds the block base, and scatters kept pairs to their rows.
+// Up to kDispatchLdsBases histogram entries, steps 2 and 3 run in one launch
+// (dispatch_blocks_kernel: every workgroup reduces the histogram for its own
+// block); beyond, as a scan kernel and a scatter kernel.
 #include "kernels.h"
 #include "block_ops.h"
 
@@ -49,34 +52,16 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
 // expert's total.  Pass 2: thread (c, e) walks its range again and writes
 // base[b][e] = pairs of expert e in blocks before b.  kept = min(count, C);
 // offsets = exclusive scan of kept, offsets[E] = routed rows, offsets[E + 1] =
-// routed + shared rows.  With INLDS, base, skept and soff are LDS and base
-// (nb * E entries) is first filled with the histogram.  sh: 2 * kMaxExperts
-// ints of LDS.  Integer sums: exact in any order.  Ends with a barrier and
-// returns counts[tid] to threads tid < E.
-template <bool INLDS>
-__device__ __forceinline__ int scan_hist(const int32_t* __restrict__ ghist, int nb, int E,
+// routed + shared rows.  sh: 2 * kMaxExperts ints of LDS.  Integer sums:
+// exact in any order.  Ends with a barrier and returns counts[tid] to threads
+// tid < E.
+__device__ __forceinline__ int scan_hist(const int32_t* __restrict__ hist, int nb, int E,
                                          int64_t T, int capacity, int shared, int32_t* base,
                                          int32_t* __restrict__ counts,
                                          int32_t* __restrict__ kept,
-                                         int32_t* __restrict__ offsets, int32_t* skept,
-                                         int32_t* soff, int32_t* sh, int32_t* wsum) {
+                                         int32_t* __restrict__ offsets, int32_t* sh,
+                                         int32_t* wsum) {
   const int tid = threadIdx.x;
-  if constexpr (INLDS) {
-    // coalesced copy; all of a thread's loads are issued before the stores
-    constexpr int CP = kDispatchLdsBases / kMaxExperts;
-    const int n = nb * E;
-    int v[CP];
-#pragma unroll
-    for (int c = 0; c < CP; ++c)
-      v[c] = tid + c * kMaxExperts < n ? ghist[tid + c * kMaxExperts] : 0;
-#pragma unroll
-    for (int c = 0; c < CP; ++c)
-      if (tid + c * kMaxExperts < n) base[tid + c * kMaxExperts] = v[c];
-    __syncthreads();
-  }
-  // read from LDS (INLDS) or global memory, chosen at compile time so each
-  // access is a plain LDS or global instruction
-  const int32_t* hist = INLDS ? base : ghist;
   const int chunks = max(1, min(kMaxExperts / E, nb));
   const int len = (nb + chunks - 1) / chunks;
   const int P = chunks + 1;  // odd row stride of the expert-major range sums
@@ -115,22 +100,14 @@ __device__ __forceinline__ int scan_hist(const int32_t* __restrict__ ghist, int 
     kp = capacity < 0 ? cnt : min(cnt, capacity);
     counts[tid] = cnt;
     kept[tid] = kp;
-    if (INLDS) skept[tid] = kp;
   }
   int ktot;
   const int kx = block_excl_scan(kp, wsum, ktot);
-  if (tid < E) {
-    offsets[tid] = kx;
-    if (INLDS) soff[tid] = kx;
-  }
+  if (tid < E) offsets[tid] = kx;
   if (tid == 0) {
     const int end = ktot + (shared ? static_cast<int32_t>(T) : 0);
     offsets[E] = ktot;
     offsets[E + 1] = end;
-    if (INLDS) {
-      soff[E] = ktot;
-      soff[E + 1] = end;
-    }
   }
   __syncthreads();
   return cnt;  // counts[tid] for tid < E
@@ -143,8 +120,8 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
   __shared__ int32_t sh[2 * kMaxExperts];
   __shared__ int32_t wsum[kMaxExperts / 64];
   __shared__ double wsd[kMaxExperts / 64];
-  const int cnt = scan_hist<false>(hist, nb, E, T, capacity, shared, base, counts, kept, offsets,
-                                   nullptr, nullptr, sh, wsum);
+  const int cnt = scan_hist(hist, nb, E, T, capacity, shared, base, counts, kept, offsets, sh,
+                            wsum);
   if (cv2) counts_cv2(cnt, E, cv2, wsd);
 }
 

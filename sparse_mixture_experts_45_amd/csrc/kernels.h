@@ -94,7 +94,7 @@ struct FfnArgs {
   int32_t* ksem;     // [kSplitSlots] arrival counters of split tiles (ntiles + 1)
 };
 
-// Everything the single-block dispatch reads and writes.
+// Everything the fused dispatch reads and writes.
 struct DispatchArgs {
   const int32_t* topk_idx;  // [T, k]
   const float* topk_w;      // [T, k]
