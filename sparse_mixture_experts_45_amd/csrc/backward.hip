@@ -590,14 +590,20 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int
 }
 
 template <typename T>
-void run_wgrad(const WgradArgs& w, int groups, int gshape, hipStream_t st) {
+void run_wgrad(const WgradArgs& w, int groups, int64_t rows_avg, hipStream_t st) {
   if (groups <= 0 || w.M <= 0 || w.N <= 0) return;
   if constexpr (sizeof(T) == 2) {
-    // bf16 with the forward on the 256- or 128-row LDS-DMA tiers: the same
-    // tiles, with each group's K range
+    // bf16: the LDS-DMA GEMM with each group's K range (the padded rows are
+    // multiples of 64 whatever the layer's tier).  Tiles cover the weights,
+    // M x N per group: 256 x 256 when they fill at least two rounds of one
+    // block per CU, else 128 x 128.  Chosen from measurements: with 64 < rows
+    // per expert < 256 (a few K steps per tile) wgrad_kernel below, four
+    // resident blocks per CU, overlaps the short K loops better.
     const WgradGemm g{w.A, w.lda, w.B, w.ldb, w.poff, w.g0, groups, w.M, w.N, w.C};
-    if (wgrad_dma_fits(gshape, g)) {
-      (void)launch_wgrad_dma(gshape, g, st);
+    const int64_t large = int64_t(groups) * ceil_div(w.M, 256) * ceil_div(w.N, 256);
+    const int shape = large >= 512 ? kGemmDmaLarge : kGemmDmaMid;
+    if ((rows_avg >= 256 || rows_avg <= 64) && wgrad_dma_fits(shape, g)) {
+      (void)launch_wgrad_dma(shape, g, st);
       return;
     }
   }
@@ -674,22 +680,22 @@ void run_bwd(const BwdArgs& b, int part, hipStream_t st) {
   if (b.dW1) {  // dW1[e] [F, d] = dz^T x
     w.A = b.ZT, w.lda = b.Rp, w.B = b.XT, w.ldb = b.Rp, w.g0 = 0, w.M = b.F, w.N = b.d;
     w.C = b.dW1;
-    run_wgrad<T>(w, b.E, b.gshape, st);
+    run_wgrad<T>(w, b.E, b.rows_avg, st);
   }
   if (b.dWs1 && b.Fs > 0) {
     w.A = b.ZT, w.lda = b.Rp, w.B = b.XT, w.ldb = b.Rp, w.g0 = b.E, w.M = b.Fs, w.N = b.d;
     w.C = b.dWs1;
-    run_wgrad<T>(w, 1, b.gshape, st);
+    run_wgrad<T>(w, 1, b.T, st);
   }
   if (b.dW2) {  // dW2[e] [d, F] = (gate dy)^T h
     w.A = b.DT, w.lda = b.Rp, w.B = b.HT, w.ldb = b.Rp, w.g0 = 0, w.M = b.d, w.N = b.F;
     w.C = b.dW2;
-    run_wgrad<T>(w, b.E, b.gshape, st);
+    run_wgrad<T>(w, b.E, b.rows_avg, st);
   }
   if (b.dWs2 && b.Fs > 0) {
     w.A = b.DT, w.lda = b.Rp, w.B = b.HT, w.ldb = b.Rp, w.g0 = b.E, w.M = b.d, w.N = b.Fs;
     w.C = b.dWs2;
-    run_wgrad<T>(w, 1, b.gshape, st);
+    run_wgrad<T>(w, 1, b.T, st);
   }
   if (b.db1 || b.dbs1)
     seg_sum_kernel<T><<<dim3(static_cast<unsigned>(ceil_div(ldh, 4)), G), 256, 0, st>>>(

@@ -153,8 +153,8 @@ hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& a, hipStream_t st);
 
 // Weight gradients on the LDS-DMA GEMM (bf16): C[g] [M, N] = A[:, Kg] B[:, Kg]^T
 // for groups g = 0 .. groups-1, Kg = columns poff[g0 + g] .. poff[g0 + g + 1]
-// (multiples of 64) of A [M, lda] and B [N, ldb].  `shape` is the forward's
-// tile tier (large or mid); wgrad_dma_fits says whether this path applies.
+// (multiples of 64) of A [M, lda] and B [N, ldb].  `shape` picks the 256- or
+// 128-row tile configuration; wgrad_dma_fits says whether this path applies.
 struct WgradGemm {
   const void* A;
   int64_t lda;
@@ -175,8 +175,8 @@ hipError_t launch_wgrad_dma(int shape, const WgradGemm& w, hipStream_t st);
 enum { kBwdRouter = 1, kBwdDx = 2, kBwdExpertWeights = 3 };
 struct BwdArgs {
   int64_t T;
+  int64_t rows_avg;             // routed rows per expert, at most, on average
   int d, F, E, k, Fs, dtype, renorm, nb;
-  int gshape;                   // the forward's GEMM tile tier (GemmShape)
   float alpha;                  // coefficient of the balance term
   const void *x, *dy;           // [T, d] layer dtype
   const float* Wg;              // [E, d]

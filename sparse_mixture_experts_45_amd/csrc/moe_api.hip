@@ -553,7 +553,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     return MOE_OK;
   }
   BwdArgs b{};
-  b.gshape = L.gp.shape;
+  b.rows_avg = routed_rows_max(cfg) / std::max(1, cfg->n_experts);
   b.T = T;
   b.d = cfg->d_model;
   b.F = cfg->d_ff;
