@@ -41,8 +41,8 @@ struct DmaCfg {
 };
 constexpr DmaCfg kDmaLarge{256, 256, 256, 64, 2, 2, 4, 2, 0, 2, 4, 256};  // >= 768 rows per expert
 constexpr DmaCfg kDmaMid{128, 128, 128, 64, 2, 2, 4, 2, 0, 2, 4, 512};    // >= 256
-constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 4, 1, 4, 2, 1, 1, 4, 0};     // >= 48
-constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 4, 1, 4, 2, 0, 1, 4, 0};    // fewer: weight streaming
+constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 3, 1, 4, 2, 1, 1, 4, 0};     // >= 48 (3 stages: 2 blocks per CU)
+constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 3, 1, 4, 2, 0, 1, 4, 0};    // fewer: weight streaming
 
 // K split of a last, partly filled round.  When a launch's tiles leave the
 // final round of resident blocks (`slots` of them) at most half full, each of
