@@ -59,7 +59,7 @@ static_assert(kDmaLarge.SPLIT <= kSplitSlots && kDmaMid.SPLIT <= kSplitSlots, "s
 
 struct GemmPlan {
   int shape;        // GemmShape
-  int BM, BN_up, BN_down;
+  int BM;             // rows per tile (the row-tile list is cut at BM)
   int64_t tiles_max;  // upper bound on row tiles over all groups
   int64_t kpart_floats;  // fp32 partial tiles of the K split (0: no split)
 };
