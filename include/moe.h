@@ -1,5 +1,6 @@
 /*
- * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer forward.
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer: forward,
+ * expert-choice routing and the training backward.
  *
  * The layer (pages: botmartz "Mixture of Experts (MoE) and Mixtral", sections
  * "MoE Architecture" and "Expert Routing"; roadtointelligence "Mixture of
@@ -29,6 +30,8 @@
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is only
  *    enqueued: no call synchronises, reads device memory on the host or
  *    allocates, so a sequence of calls can be captured in a HIP graph.
+ *  - Results are reproducible bit for bit for the same inputs and config: no
+ *    floating-point atomics, every sum in a fixed order.
  *  - Arguments are validated before anything is enqueued; a failed check
  *    returns a negative moe_status and enqueues nothing.  A failed launch
  *    returns MOE_ERR_HIP (hipGetLastError has the detail).  Nothing is printed.
