@@ -63,9 +63,13 @@ SMALL = [
     S("router_splitk_e160", T=200, d=1024, F=64, E=160, k=6),
     S("router_e300", T=70, d=128, F=64, E=300, k=4, router_bias="none"),
     S("router_f32_splitk", T=64, d=2048, F=64, E=8, k=2, dtype="f32"),
-    # 129 blocks x 64 experts: the per-block bases no longer fit one block's
-    # LDS, so the multi-kernel dispatch runs
+    # 129 blocks x 64 experts: past the fused dispatch's 8192 histogram
+    # entries, so the scan and scatter kernels run
     S("dispatch_multiblock", T=8256, d=64, F=64, E=64, k=2, capacity=300),
+    # 1024 64-token blocks x 8 experts: the fused dispatch at its limit, 1024
+    # workgroups each reducing the whole histogram (ranges of 8 blocks)
+    S("dispatch_fused_max", T=65536, d=64, F=64, E=8, k=2, capacity=16500,
+      router_bias="zipf1.1"),
 ]
 
 
