@@ -112,19 +112,29 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(
 
 // Bias gradients: out_g[c] = sum of in[c][poff[g] .. poff[g + 1]) for group g
 // (routed groups g < E write out + g * C, the shared group out_sh, with Cs
-// values).  One wave per (c, g), lanes strided over the segment.
+// values).  One wave per (c, g); each lane adds 16-byte chunks of the segment
+// (segments start at multiples of 64 elements and the row stride is one, so
+// the chunks are aligned), then the wave sums the lanes: a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void seg_sum_kernel(const T* __restrict__ in, int64_t ldi,
                                                       const int32_t* __restrict__ poff, int E,
                                                       int C, int Cs, T* __restrict__ out,
                                                       T* __restrict__ out_sh) {
+  constexpr int V = 16 / sizeof(T);  // elements per chunk
   const int g = blockIdx.y, c = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int Cg = g < E ? C : Cs;
   T* o = g < E ? (out ? out + static_cast<int64_t>(g) * C : nullptr) : out_sh;
   if (c >= Cg || !o) return;
-  const T* row = in + static_cast<int64_t>(c) * ldi;
+  const int p0 = poff[g], n = (poff[g + 1] - p0) / V;
+  const uint4* row = reinterpret_cast<const uint4*>(in + static_cast<int64_t>(c) * ldi + p0);
   float s = 0.f;
-  for (int col = poff[g] + lane; col < poff[g + 1]; col += 64) s += to_f32<T>(row[col]);
+#pragma unroll 4
+  for (int i = lane; i < n; i += 64) {
+    const uint4 u = row[i];
+    const T* v = reinterpret_cast<const T*>(&u);
+#pragma unroll
+    for (int j = 0; j < V; ++j) s += to_f32<T>(v[j]);
+  }
   s = wave_sum(s);
   if (lane == 0) o[c] = from_f32<T>(s);
 }
