@@ -12,7 +12,7 @@
 //   dX_r   = dz_r W1[e]                       same pass, second GEMM
 //   dx_t   = sum over t's rows of dX_r + sum_e dl[t, e] W_g[e]       dx_kernel
 //   dW1[e] = sum_r dz_r^T x_t,  dW2[e] = sum_r (g dy_t)^T h_r        wgrad_kernel
-//   db1[e] = sum_r dz_r,        db2[e] = sum_r g dy_t                seg_sum_kernel
+//   db1[e] = sum_r dz_r,        db2[e] = sum_r g dy_t                transposes + seg_finish_kernel
 //   dg     = <dy_t, o_r> = <dy_t, y_rows[r]> / g                     gate_grad_kernel
 //   dp     = renormalisation backward of dg, plus the balance term,
 //   dl     = p (dp - <p, dp>)                                       router_bwd_kernel
@@ -60,14 +60,19 @@ __global__ __launch_bounds__(kMaxExperts) void poff_kernel(const int32_t* __rest
 // columns.  A block covers 64 padded columns (inside one group, as every group
 // spans a multiple of 64) and 64 values of c, moved as 16-byte chunks through
 // a padded LDS tile (the padding keeps the column reads on distinct banks).
-// C and lds are multiples of the chunk width.
+// C and lds are multiples of the chunk width.  With psum, also the sum over
+// the block's 64 rows of each c: psum[col0 / 64][c] (rows 16 q .. 16 q + 15
+// added in order by quarter q, then the quarters in order), for the bias
+// gradients (seg_finish_kernel).
 template <typename T>
 __global__ __launch_bounds__(256) void gather_transpose_kernel(
     const T* __restrict__ src, int64_t lds, int C, const int32_t* __restrict__ row_token,
     const float* __restrict__ row_gate, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ poff, int G, T* __restrict__ out, int64_t ldo) {
+    const int32_t* __restrict__ poff, int G, T* __restrict__ out, int64_t ldo,
+    float* __restrict__ psum) {
   constexpr int V = 16 / sizeof(T), CPR = 64 / V, LDT = 64 + V;
   __shared__ __align__(16) T tile[64 * LDT];
+  __shared__ float qsum[4][64];
   const int col0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   if (col0 >= poff[G]) return;
   int lo = 0, hi = G;  // poff[lo] <= col0 < poff[hi]
@@ -99,6 +104,17 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(
     *reinterpret_cast<uint4*>(&tile[i * LDT + ch * V]) = v.u;
   }
   __syncthreads();
+  if (psum) {
+    const int cc = threadIdx.x & 63, qq = threadIdx.x >> 6;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sq += to_f32<T>(tile[(qq * 16 + i) * LDT + cc]);
+    qsum[qq][cc] = sq;
+    __syncthreads();
+    if (threadIdx.x < 64 && c0 + cc < C)
+      psum[static_cast<int64_t>(col0 / 64) * C + c0 + cc] =
+          ((qsum[0][cc] + qsum[1][cc]) + qsum[2][cc]) + qsum[3][cc];
+  }
   for (int q = threadIdx.x; q < 64 * CPR; q += 256) {
     const int cc = q / CPR, ch = q % CPR;  // output row c0 + cc, columns col0 + ch V ..
     const int c = c0 + cc;
@@ -110,33 +126,23 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(
   }
 }
 
-// Bias gradients: out_g[c] = sum of in[c][poff[g] .. poff[g + 1]) for group g
-// (routed groups g < E write out + g * C, the shared group out_sh, with Cs
-// values).  One wave per (c, g); each lane adds 16-byte chunks of the segment
-// (segments start at multiples of 64 elements and the row stride is one, so
-// the chunks are aligned), then the wave sums the lanes: a fixed order.
+// Bias gradients from the transpose's block sums: out_g[c] = sum over group
+// g's 64-row blocks (poff[g] / 64 .. poff[g + 1] / 64) of psum[block][c], in
+// block order (routed groups g < E write out + g * C, the shared group out_sh,
+// with Cs values).  ldp = the row length of psum.
 template <typename T>
-__global__ __launch_bounds__(256) void seg_sum_kernel(const T* __restrict__ in, int64_t ldi,
-                                                      const int32_t* __restrict__ poff, int E,
-                                                      int C, int Cs, T* __restrict__ out,
-                                                      T* __restrict__ out_sh) {
-  constexpr int V = 16 / sizeof(T);  // elements per chunk
-  const int g = blockIdx.y, c = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+__global__ __launch_bounds__(256) void seg_finish_kernel(const float* __restrict__ psum, int ldp,
+                                                         const int32_t* __restrict__ poff, int E,
+                                                         int C, int Cs, T* __restrict__ out,
+                                                         T* __restrict__ out_sh) {
+  const int g = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
   const int Cg = g < E ? C : Cs;
   T* o = g < E ? (out ? out + static_cast<int64_t>(g) * C : nullptr) : out_sh;
   if (c >= Cg || !o) return;
-  const int p0 = poff[g], n = (poff[g + 1] - p0) / V;
-  const uint4* row = reinterpret_cast<const uint4*>(in + static_cast<int64_t>(c) * ldi + p0);
   float s = 0.f;
-#pragma unroll 4
-  for (int i = lane; i < n; i += 64) {
-    const uint4 u = row[i];
-    const T* v = reinterpret_cast<const T*>(&u);
-#pragma unroll
-    for (int j = 0; j < V; ++j) s += to_f32<T>(v[j]);
-  }
-  s = wave_sum(s);
-  if (lane == 0) o[c] = from_f32<T>(s);
+  for (int blk = poff[g] / 64; blk < poff[g + 1] / 64; ++blk)
+    s += psum[static_cast<int64_t>(blk) * ldp + c];
+  o[c] = from_f32<T>(s);
 }
 
 struct WgradArgs {
@@ -669,21 +675,30 @@ void run_bwd(const BwdArgs& b, int part, hipStream_t st) {
   poff_kernel<<<1, kMaxExperts, 0, st>>>(b.offsets, G, b.poff);
   const unsigned pcols = static_cast<unsigned>(b.Rp / 64);
   auto gt = [&](const void* src, int64_t lds, int C, const int32_t* rt, const float* gate,
-                void* out) {
+                void* out, float* psum) {
     const dim3 grid(pcols, static_cast<unsigned>(ceil_div(C, 64)));
     gather_transpose_kernel<T><<<grid, 256, 0, st>>>(static_cast<const T*>(src), lds, C, rt, gate,
                                                      b.offsets, b.poff, G,
-                                                     static_cast<T*>(out), b.Rp);
+                                                     static_cast<T*>(out), b.Rp, psum);
+  };
+  // bias gradients: the transposes' 64-row block sums, added per group
+  auto finish = [&](int C, int Cout, int Cs, void* out, void* out_sh) {
+    const int cmax = Cout > Cs ? Cout : Cs;
+    seg_finish_kernel<T><<<dim3(static_cast<unsigned>(ceil_div(cmax, 256)), G), 256, 0, st>>>(
+        b.bsum, C, b.poff, b.E, Cout, Cs, static_cast<T*>(out), static_cast<T*>(out_sh));
   };
   const bool w1 = b.dW1 || b.dWs1 || b.db1 || b.dbs1;
   const bool w2 = b.dW2 || b.dWs2 || b.db2 || b.dbs2;
+  const bool s1 = b.db1 || b.dbs1, s2 = b.db2 || b.dbs2;
   if (w1) {
-    gt(b.Z, ldh, ldh, nullptr, nullptr, b.ZT);        // dz^T
-    if (b.dW1 || b.dWs1) gt(b.x, b.d, b.d, b.row_token, nullptr, b.XT);  // x rows^T
+    gt(b.Z, ldh, ldh, nullptr, nullptr, b.ZT, s1 ? b.bsum : nullptr);  // dz^T
+    if (s1) finish(ldh, b.F, b.Fs, b.db1, b.dbs1);
+    if (b.dW1 || b.dWs1) gt(b.x, b.d, b.d, b.row_token, nullptr, b.XT, nullptr);  // x rows^T
   }
   if (w2) {
-    gt(b.dy, b.d, b.d, b.row_token, b.row_gate, b.DT);  // (gate dy)^T
-    if (b.dW2 || b.dWs2) gt(b.H, ldh, ldh, nullptr, nullptr, b.HT);  // h^T
+    gt(b.dy, b.d, b.d, b.row_token, b.row_gate, b.DT, s2 ? b.bsum : nullptr);  // (gate dy)^T
+    if (s2) finish(b.d, b.d, b.d, b.db2, b.dbs2);
+    if (b.dW2 || b.dWs2) gt(b.H, ldh, ldh, nullptr, nullptr, b.HT, nullptr);  // h^T
   }
   WgradArgs w{};
   w.poff = b.poff;
@@ -707,14 +722,6 @@ void run_bwd(const BwdArgs& b, int part, hipStream_t st) {
     w.C = b.dWs2;
     run_wgrad<T>(w, 1, b.T, st);
   }
-  if (b.db1 || b.dbs1)
-    seg_sum_kernel<T><<<dim3(static_cast<unsigned>(ceil_div(ldh, 4)), G), 256, 0, st>>>(
-        static_cast<const T*>(b.ZT), b.Rp, b.poff, b.E, b.F, b.Fs, static_cast<T*>(b.db1),
-        static_cast<T*>(b.dbs1));
-  if (b.db2 || b.dbs2)
-    seg_sum_kernel<T><<<dim3(static_cast<unsigned>(ceil_div(b.d, 4)), G), 256, 0, st>>>(
-        static_cast<const T*>(b.DT), b.Rp, b.poff, b.E, b.d, b.d, static_cast<T*>(b.db2),
-        static_cast<T*>(b.dbs2));
 }
 
 }  // namespace

@@ -202,6 +202,7 @@ struct BwdArgs {
   int32_t* poff;                // [G + 1] padded column offsets
   int64_t Rp;                   // columns of the transposed buffers (multiple of 64)
   void *ZT, *HT, *XT, *DT;      // [ldh, Rp], [ldh, Rp], [d, Rp], [d, Rp]
+  float* bsum;                  // [Rp / 64, max(ldh, d)] 64-row block sums (bias gradients)
   // outputs, NULL = not wanted
   void* dx;
   float *dWg, *dbg;

@@ -20,7 +20,7 @@ struct Layout {
   bool train;
   int wg_split;
   int64_t wg_chunk, Rp;
-  size_t Z, probs, dg, dl, aux_dp, wg_part, poff, ZT, HT, XT, DT;
+  size_t Z, probs, dg, dl, aux_dp, wg_part, poff, ZT, HT, XT, DT, bsum;
 };
 
 bool expert_choice(const moe_config* c) { return c->routing == MOE_ROUTE_EXPERT; }
@@ -204,6 +204,7 @@ Layout layout(const moe_config* c, bool train = false) {
     L.HT = take(elt * ldh * L.Rp);
     L.XT = take(elt * d * L.Rp);
     L.DT = take(elt * d * L.Rp);
+    L.bsum = take(sizeof(float) * (L.Rp / 64) * std::max<int64_t>(ldh, d));
   }
   L.total = o;
   return L;
@@ -597,6 +598,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   b.HT = at(ws, L.HT);
   b.XT = at(ws, L.XT);
   b.DT = at(ws, L.DT);
+  b.bsum = reinterpret_cast<float*>(at(ws, L.bsum));
   b.dx = g.dx;
   b.dWg = g.dWg;
   b.dbg = g.dbg;
