@@ -396,30 +396,54 @@ __global__ __launch_bounds__(64) void ec_router_bwd_kernel(const float* __restri
   for (int e = lane; e < E; e += 64) dl[t * E + e] = pp[e] * (dp[e] - s);
 }
 
-// part[s][e][j] = sum over the tokens of chunk s of dl[t][e] x[t][j]; column
-// j = d is the bias (x = 1).  Eight experts per block; the dl loads are uniform.
+// Partial router weight gradients: part[s][e][j] = sum over the tokens of
+// chunk s of dl[t][e] * x[t][j] (x[t][d] = 1 gives the bias), tokens in order.
+// A thread owns 8 consecutive columns and 8 experts: one 16-byte x load and
+// the block's 8 dl values feed 64 products per token.
 template <typename T>
 __global__ __launch_bounds__(256) void router_wgrad_part_kernel(const T* __restrict__ x,
                                                                 const float* __restrict__ dl,
                                                                 int64_t Tn, int d, int E,
                                                                 int64_t chunk,
                                                                 float* __restrict__ part) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
+  constexpr int V = 16 / sizeof(T);  // x elements per 16-byte load
+  static_assert(V <= 8, "columns per thread");
+  constexpr int NC = 8;              // columns per thread (two loads for fp32)
+  const int j0 = (blockIdx.x * 256 + threadIdx.x) * NC;
   const int e0 = blockIdx.y * 8;
   const int64_t s = blockIdx.z, t0 = s * chunk, t1 = min(Tn, t0 + chunk);
-  float acc[8];
+  if (j0 > d) return;
+  float acc[8][NC];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  for (int q = 0; q < 8; ++q)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[q][c] = 0.f;
   for (int64_t t = t0; t < t1; ++t) {
-    const float xv = j < d ? to_f32<T>(x[t * d + j]) : (j == d ? 1.f : 0.f);
+    float xv[NC];
+    if (j0 < d) {  // d is a multiple of 8: the chunk lies inside the row
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (e0 + q < E) acc[q] += dl[t * E + e0 + q] * xv;
+      for (int h = 0; h < NC / V; ++h) {
+        const uint4 u = *reinterpret_cast<const uint4*>(x + t * d + j0 + h * V);
+        const T* v = reinterpret_cast<const T*>(&u);
+#pragma unroll
+        for (int c = 0; c < V; ++c) xv[h * V + c] = to_f32<T>(v[c]);
+      }
+    } else {  // j0 == d: the bias column, then nothing
+#pragma unroll
+      for (int c = 0; c < NC; ++c) xv[c] = c == 0 ? 1.f : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float g = e0 + q < E ? dl[t * E + e0 + q] : 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[q][c] += g * xv[c];
+    }
   }
-  if (j <= d)
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (e0 + q < E) part[(s * E + e0 + q) * (d + 1) + j] = acc[q];
+  for (int q = 0; q < 8; ++q)
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (e0 + q < E && j0 + c <= d) part[(s * E + e0 + q) * (d + 1) + j0 + c] = acc[q][c];
 }
 
 // dWg[e][j] (j < d) and dbg[e] (j = d) = sum over the chunks, in chunk order.
@@ -650,7 +674,7 @@ void run_bwd(const BwdArgs& b, int part, hipStream_t st) {
       router_bwd_kernel<<<static_cast<unsigned>(b.T), 64, 0, st>>>(
           b.probs, b.topk_idx, b.topk_w, b.dg, b.aux_dp, b.E, b.k, b.renorm, b.dl);
     if (b.dWg || b.dbg) {
-      const dim3 grid(static_cast<unsigned>(ceil_div(b.d + 1, 256)),
+      const dim3 grid(static_cast<unsigned>(ceil_div(b.d + 1, 256 * 8)),
                       static_cast<unsigned>(ceil_div(b.E, 8)), static_cast<unsigned>(b.wg_split));
       router_wgrad_part_kernel<T><<<grid, 256, 0, st>>>(static_cast<const T*>(b.x), b.dl, b.T,
                                                         b.d, b.E, b.wg_chunk, b.wg_part);

@@ -193,7 +193,7 @@ Layout layout(const moe_config* c, bool train = false) {
     L.dl = take(sizeof(float) * T * E);
     L.aux_dp = take(sizeof(float) * E);
     // router weight gradient: enough token chunks for ~512 blocks
-    const int64_t col_blocks = ceil_div(d + 1, 256) * ceil_div(E, 8);
+    const int64_t col_blocks = ceil_div(d + 1, 256 * 8) * ceil_div(E, 8);  // 8 columns a thread
     L.wg_split = static_cast<int>(std::max<int64_t>(
         1, std::min<int64_t>(ceil_div(512, col_blocks), ceil_div(std::max<int64_t>(T, 1), 64))));
     L.wg_chunk = ceil_div(std::max<int64_t>(T, 1), L.wg_split);
