@@ -418,8 +418,7 @@ __global__ __launch_bounds__(256) void router_wgrad_part_kernel(const T* __restr
   for (int q = 0; q < 8; ++q)
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[q][c] = 0.f;
-  for (int64_t t = t0; t < t1; ++t) {
-    float xv[NC];
+  auto load_x = [&](int64_t t, float (&xv)[NC]) {
     if (j0 < d) {  // d is a multiple of 8: the chunk lies inside the row
 #pragma unroll
       for (int h = 0; h < NC / V; ++h) {
@@ -432,6 +431,41 @@ __global__ __launch_bounds__(256) void router_wgrad_part_kernel(const T* __restr
 #pragma unroll
       for (int c = 0; c < NC; ++c) xv[c] = c == 0 ? 1.f : 0.f;
     }
+  };
+  // four tokens' loads go out together (one memory latency per four tokens);
+  // the products are still added token by token
+  constexpr int U = 4;
+  // all eight experts present and their dl rows 16-byte aligned (E % 4 == 0)
+  const bool full8 = e0 + 8 <= E && E % 4 == 0;
+  int64_t t = t0;
+  for (; t + U <= t1; t += U) {
+    float xv[U][NC], g[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_x(t + u, xv[u]);
+    if (full8) {  // block-uniform: one 8-value scalar load per token
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float4* p = reinterpret_cast<const float4*>(dl + (t + u) * E + e0);
+        const float4 a = p[0], b = p[1];
+        g[u][0] = a.x, g[u][1] = a.y, g[u][2] = a.z, g[u][3] = a.w;
+        g[u][4] = b.x, g[u][5] = b.y, g[u][6] = b.z, g[u][7] = b.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) g[u][q] = e0 + q < E ? dl[(t + u) * E + e0 + q] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[q][c] += g[u][q] * xv[u][c];
+  }
+  for (; t < t1; ++t) {
+    float xv[NC];
+    load_x(t, xv);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const float g = e0 + q < E ? dl[t * E + e0 + q] : 0.f;
