@@ -318,10 +318,24 @@ __global__ __launch_bounds__(kMaxExperts) void aux_prep_kernel(const double* __r
                                                                float alpha,
                                                                float* __restrict__ aux_dp) {
   __shared__ double wsd[kMaxExperts / 64];
+  __shared__ double rsum[kMaxExperts];
   const int e = threadIdx.x;
+  // thread (c, e') adds expert e' over range c of the blocks; thread e then
+  // adds its ranges in order (fp64 throughout)
+  const int chunks = max(1, min(kMaxExperts / E, nb));
+  const int len = (nb + chunks - 1) / chunks;
+  const int c1 = threadIdx.x / E, e1 = threadIdx.x - c1 * E;
+  if (c1 < chunks) {
+    double r = 0.0;
+    const int b0 = c1 * len, b1 = min(nb, b0 + len);
+#pragma unroll 4
+    for (int b = b0; b < b1; ++b) r += stat_part[static_cast<int64_t>(b) * E + e1];
+    rsum[e1 * chunks + c1] = r;
+  }
+  __syncthreads();
   double m = 0.0;
   if (e < E) {
-    for (int b = 0; b < nb; ++b) m += stat_part[static_cast<int64_t>(b) * E + e];
+    for (int c = 0; c < chunks; ++c) m += rsum[e * chunks + c];
     m /= static_cast<double>(T);
   }
   const double mbar = block_sum_d(m, wsd) / E;
