@@ -81,18 +81,32 @@ __device__ inline double block_sum_d(double v, double* wsd) {
 }
 
 // Load statistics from the gate's per-block probability sums (fp64):
-// mean_prob[e] = (sum over the nb blocks, in block order) / T, and balance =
+// mean_prob[e] = (sum over the nb blocks, a fixed order) / T, and balance =
 // unbiased variance of mean_prob over the E experts.  Either output may be null;
-// T = 0 gives NaN means, E = 1 a NaN variance.
+// T = 0 gives NaN means, E = 1 a NaN variance.  Called by every thread of a
+// block of kMaxExperts threads.
 __device__ inline void load_stats(const double* __restrict__ stat_part, int nb, int E, int64_t T,
                                   float* __restrict__ mean_prob, float* __restrict__ balance,
                                   double* wsd) {
   const int e = threadIdx.x;
+  // thread (c, e') adds expert e' over range c of the blocks; thread e then
+  // adds its ranges in order
+  __shared__ double rsum[kMaxExperts];
+  const int chunks = max(1, min(kMaxExperts / E, nb));
+  const int len = (nb + chunks - 1) / chunks;
+  const int c1 = threadIdx.x / E, e1 = threadIdx.x - c1 * E;
+  if (c1 < chunks) {
+    double r = 0.0;
+    const int b0 = c1 * len, b1 = min(nb, b0 + len);
+#pragma unroll 4
+    for (int b = b0; b < b1; ++b) r += stat_part[static_cast<int64_t>(b) * E + e1];
+    rsum[e1 * chunks + c1] = r;
+  }
+  __syncthreads();
   double mp = 0.0;
   if (e < E) {
     double acc = 0.0;
-#pragma unroll 8
-    for (int b = 0; b < nb; ++b) acc += stat_part[static_cast<int64_t>(b) * E + e];
+    for (int c = 0; c < chunks; ++c) acc += rsum[e * chunks + c];
     mp = acc / static_cast<double>(T);
     if (mean_prob) mean_prob[e] = static_cast<float>(mp);
   }
