@@ -477,7 +477,8 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     const bf16* bw;    // weight rows of this group
     const bf16* bias;  // bias of this group, or null
     int ldb;           // elements between B rows (K, or ldb for kWgrad)
-    uint32_t aoff;     // bytes from A to the tile's first K column (kWgrad)
+    int64_t aoff;      // bytes from A to the tile's first row (contiguous A) and
+                       // first K column (kWgrad); A offsets below are relative
     int64_t ooff;      // output elements before the group's matrix (kWgrad)
   };
   // Tile fields are the same for the whole block: readfirstlane keeps them in
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
       c.bw = static_cast<const bf16*>(a.W) + k0;
       c.bias = nullptr;
       c.ldb = static_cast<int>(a.ldb);
-      c.aoff = static_cast<uint32_t>(k0) * 2u;
+      c.aoff = (static_cast<int64_t>(c.row0) * a.lda + k0) * 2;
       c.ooff = static_cast<int64_t>(g) * a.M * a.N;
       return c;
     }
@@ -521,14 +522,16 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     c.bias = static_cast<const bf16*>(sh ? a.bias_sh : a.bias);
     if (c.bias && !sh) c.bias += static_cast<int64_t>(group) * c.N;
     c.ldb = c.K;
-    c.aoff = 0;
+    c.aoff = MD::gather ? 0 : static_cast<int64_t>(c.row0) * a.lda * 2;
     c.ooff = 0;
     return c;
   };
-  // token row (up-projection) or H row (down-projection) behind A row r
+  // token row (gathered A) behind tile row r, or r itself for contiguous A
+  // (whose tile base holds the first row): gathered A must span < 4 GiB, a
+  // contiguous one only a tile
   auto arow_of = [&](const Tile& c, int r) -> int {
     const int rr = min(r, c.rows - 1);
-    return MD::gather ? a.row_token[c.row0 + rr] : c.row0 + rr;
+    return MD::gather ? a.row_token[c.row0 + rr] : rr;
   };
   // Load instruction j of this wave fills tile rows (wave + j NW) RPI ...; the
   // first JA instructions hold A rows, the rest B rows.  Sources are kept as
@@ -762,6 +765,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     if (has_next) {
 #pragma unroll
       for (int j = 0; j < JPW; ++j) src[j] = j < JA ? a_off(j, ntok[j]) : b_off(nxt, j);
+      abase = static_cast<const char*>(a.A) + nxt.aoff;
       bbase = reinterpret_cast<const char*>(nxt.bw);
       bstep = BT ? static_cast<uint32_t>(nxt.N) * 2 : 2;
       const int KTn = nxt.K / BK;
@@ -1050,11 +1054,12 @@ static void run_wgrad_dma(const WgradGemm& w, hipStream_t st) {
 
 bool wgrad_dma_fits(int shape, const WgradGemm& w) {
   if (shape != kGemmDmaLarge && shape != kGemmDmaMid) return false;
-  // 16-byte LDS-DMA chunks along K, 32-bit byte offsets inside A and B
+  // 16-byte LDS-DMA chunks along K; 32-bit byte offsets inside a row tile of
+  // A (whose base is per tile) and inside B
   const bool k16 = w.lda % 8 == 0 && w.ldb % 8 == 0 &&
                    reinterpret_cast<uintptr_t>(w.A) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(w.B) % 16 == 0;
-  return k16 && int64_t(w.M) * w.lda * 2 < (int64_t(1) << 31) &&
+  return k16 && int64_t(kDmaLarge.BM) * w.lda * 2 < (int64_t(1) << 31) &&
          int64_t(w.N) * w.ldb * 2 < (int64_t(1) << 31) && int64_t(w.M) * w.N < (int64_t(1) << 31);
 }
 

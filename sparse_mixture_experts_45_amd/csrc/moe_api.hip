@@ -67,7 +67,13 @@ GemmPlan gemm_plan(const moe_config* c) {
   GemmPlan g{};
   const int64_t rmax = routed_rows_max(c);
   const int64_t avg = rmax / c->n_experts;
-  const bool k64 = c->d_model % 64 == 0 && c->d_ff % 64 == 0 && c->shared_d_ff % 64 == 0;
+  // The LDS-DMA tiers read 64-element K steps and address gathered token rows
+  // (x, dy: [T, d]) and one expert's weights ([F, d] or [d, F]) with 32-bit
+  // byte offsets; other shapes take the tiers with 64-bit addressing.
+  const int64_t four_gib = int64_t(1) << 32;
+  const int64_t fmax = std::max<int64_t>(c->d_ff, c->shared_d_ff);
+  const bool k64 = c->d_model % 64 == 0 && c->d_ff % 64 == 0 && c->shared_d_ff % 64 == 0 &&
+                   c->T * c->d_model * 2 <= four_gib && fmax * c->d_model * 2 <= four_gib;
   // expert choice gives every expert exactly C rows: whole 256-row tiles pay
   // when their padding is at most 1/8 of the rows
   const int64_t C = expert_choice(c) ? ec_capacity(c) : 0;
