@@ -99,13 +99,18 @@ WORKLOADS = {
                                       router_bias="zipf1.1"),
     "deepseek_e256_top8": LayerShape("deepseek_e256_top8", T=512, d=7168, F=2048,
                                      E=256, k=8, Fs=2048),
+    # one expert-parallel rank's share of the DeepSeek-shaped layer on 8 GPUs
+    # with 512 tokens each: its 32 experts receive the 4096 rows routed to
+    # them (about 128 each) and stream 1.9 GB of weights; a top-1 router over
+    # the 32 local experts stands in for the remote routing and the exchange
+    "deepseek_ep8_rank": LayerShape("deepseek_ep8_rank", T=4096, d=7168, F=2048, E=32, k=1),
     # expert-choice routing on the Switch-style shape: each of the 64 experts
     # takes its top floor(T*k/E) = 256 tokens (capacity factor k = 2)
     "expert_choice_t8192_e64": LayerShape("expert_choice_t8192_e64", T=8192, d=1024,
                                           F=4096, E=64, k=2, routing="expert"),
 }
 WORKLOAD_ORDER = ["tiny_f32", "page1_b4s512", "mixtral_t4096",
-                  "switch_e64_top1_cap", "deepseek_e256_top8"]
+                  "switch_e64_top1_cap", "deepseek_e256_top8", "deepseek_ep8_rank"]
 
 
 def workload(name_or_index) -> LayerShape:

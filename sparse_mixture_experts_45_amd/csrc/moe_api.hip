@@ -78,10 +78,21 @@ GemmPlan gemm_plan(const moe_config* c) {
   // when their padding is at most 1/8 of the rows
   const int64_t C = expert_choice(c) ? ec_capacity(c) : 0;
   const bool ec_whole = C >= 256 && (ceil_div(C, 256) * 256 - C) * 8 <= C;
+  // 256 x 256 tiles read an expert's weights once per 256 rows, against two
+  // to four times for the narrower tiers; they pay from 128 rows per expert
+  // once the smaller of the two GEMMs still has >= 128 of them (the K split
+  // fills the rest of the machine).  Under a capacity limit the rows per
+  // expert are only bounded above (a skewed router leaves most experts far
+  // below it), so such layers keep the row-count thresholds.
+  const bool uncapped = c->capacity < 0 && !expert_choice(c);
+  const int64_t large_rows = int64_t(c->n_experts) * ceil_div(std::max<int64_t>(avg, 1), 256);
+  const bool large_fills =
+      uncapped && avg >= 128 &&
+      large_rows * std::min(ceil_div(fmax, 256), ceil_div(int64_t(c->d_model), 256)) >= 128;
   if (c->dtype == MOE_F32) {
     g.shape = kGemmF32;
     g.BM = 64;
-  } else if (k64 && (avg >= 768 || ec_whole)) {
+  } else if (k64 && (avg >= 768 || ec_whole || large_fills)) {
     g.shape = kGemmDmaLarge;
     g.BM = kDmaLarge.BM;
     g.kpart_floats = int64_t(kDmaLarge.SPLIT) * kDmaLarge.BM *

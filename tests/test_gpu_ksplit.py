@@ -41,7 +41,10 @@ def tier_of(shape):
                                                                  shape.E * shape.capacity)
         whole = False
     avg = rows // shape.E
-    if avg >= 768 or whole:
+    fills = (shape.routing != "expert" and shape.capacity < 0 and avg >= 128 and
+             shape.E * -(-max(avg, 1) // 256) *
+             min(-(-max(shape.F, shape.Fs) // 256), -(-shape.d // 256)) >= 128)
+    if avg >= 768 or whole or fills:
         return "large"
     return "mid" if avg >= 256 else None
 

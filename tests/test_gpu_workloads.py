@@ -1,4 +1,4 @@
-"""GPU parity at the five full workload sizes, in the launch configuration the
+"""GPU parity at the six full workload sizes, in the launch configuration the
 benchmark times (moe_forward with the library's own tile choice).
 
 Routing, counts, kept counts and the load statistics are checked for every
@@ -19,7 +19,7 @@ from gpu_common import cfg_of, check_routing, check_y, device_inputs, gpu_forwar
 pytestmark = pytest.mark.gpu
 
 SAMPLES = {"tiny_f32": None, "page1_b4s512": 96, "mixtral_t4096": 24,
-           "switch_e64_top1_cap": 64, "deepseek_e256_top8": 32}
+           "switch_e64_top1_cap": 64, "deepseek_e256_top8": 32, "deepseek_ep8_rank": 32}
 
 
 def sample_tokens(shape, ref, n):
