@@ -1025,6 +1025,7 @@ static void run_pass(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN, C.OCC, C.PERSIST, C.WMD, C.WND, C.SPLIT, \
           M1, BT>(gp, f, st)
     case kGemmDmaLarge: MOE_RUN_DMA(kDmaLarge); break;
+    case kGemmDmaTall: MOE_RUN_DMA(kDmaTall); break;
     case kGemmDmaMid: MOE_RUN_DMA(kDmaMid); break;
     case kGemmDmaSmall: MOE_RUN_DMA(kDmaSmall); break;
     default: MOE_RUN_DMA(kDmaSkinny); break;

@@ -26,7 +26,8 @@ enum GemmShape {
   kGemmDmaLarge = 4,   // bf16, K multiple of 64, LDS-DMA tiles (kDma* below)
   kGemmDmaMid = 5,
   kGemmDmaSmall = 6,
-  kGemmDmaSkinny = 7
+  kGemmDmaSkinny = 7,
+  kGemmDmaTall = 8
 };
 
 // Tile configurations of the LDS-DMA grouped GEMM.  The host plan (row-tile
@@ -43,6 +44,9 @@ constexpr DmaCfg kDmaLarge{256, 256, 256, 64, 2, 2, 4, 2, 0, 2, 4, 256};  // >= 
 constexpr DmaCfg kDmaMid{128, 128, 128, 64, 2, 2, 4, 2, 0, 2, 4, 512};    // >= 256
 constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 3, 1, 4, 2, 1, 1, 4, 0};     // >= 48 (3 stages: 2 blocks per CU)
 constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 3, 1, 4, 2, 0, 1, 4, 0};    // fewer: weight streaming
+// 192-row tiles where an expert's rows (about 128-165) fit one: a quarter
+// fewer MFMAs on padding rows than 256
+constexpr DmaCfg kDmaTall{192, 256, 256, 64, 2, 2, 4, 2, 0, 2, 4, 256};
 
 // K split of a last, partly filled round.  When a launch's tiles leave the
 // final round of resident blocks (`slots` of them) at most half full, each of
@@ -55,7 +59,9 @@ constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 3, 1, 4, 2, 0, 1, 4, 0};    // few
 constexpr int kSplitMax = 4;       // parts per tile
 constexpr int kSplitMinSteps = 32;  // K steps per part, at least (the fences cost)
 constexpr int kSplitSlots = 512;   // counters kept after the tile count (>= every SPLIT)
-static_assert(kDmaLarge.SPLIT <= kSplitSlots && kDmaMid.SPLIT <= kSplitSlots, "split slots");
+static_assert(kDmaLarge.SPLIT <= kSplitSlots && kDmaMid.SPLIT <= kSplitSlots &&
+                  kDmaTall.SPLIT <= kSplitSlots,
+              "split slots");
 
 struct GemmPlan {
   int shape;        // GemmShape

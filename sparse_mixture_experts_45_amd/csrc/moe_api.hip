@@ -2,6 +2,8 @@
 // Nothing here allocates, synchronises or reads device memory.
 #include <string.h>
 
+#include <cmath>
+
 #include "kernels.h"
 
 using namespace moe;
@@ -93,10 +95,13 @@ GemmPlan gemm_plan(const moe_config* c) {
     g.shape = kGemmF32;
     g.BM = 64;
   } else if (k64 && (avg >= 768 || ec_whole || large_fills)) {
-    g.shape = kGemmDmaLarge;
-    g.BM = kDmaLarge.BM;
-    g.kpart_floats = int64_t(kDmaLarge.SPLIT) * kDmaLarge.BM *
-                     std::max(kDmaLarge.BNU, kDmaLarge.BND);
+    // 192-row tiles when an expert's rows, two standard deviations of an
+    // even routing above the mean, fit one of them
+    const bool tall = large_fills && avg + 2.0 * std::sqrt(static_cast<double>(avg)) <= 192.0;
+    const DmaCfg& L = tall ? kDmaTall : kDmaLarge;
+    g.shape = tall ? kGemmDmaTall : kGemmDmaLarge;
+    g.BM = L.BM;
+    g.kpart_floats = int64_t(L.SPLIT) * L.BM * std::max(L.BNU, L.BND);
   } else if (k64 && avg >= 256) {
     g.shape = kGemmDmaMid;
     g.BM = kDmaMid.BM;
