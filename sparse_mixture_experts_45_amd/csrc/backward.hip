@@ -684,12 +684,14 @@ void run_wgrad(const WgradArgs& w, int groups, int64_t rows_avg, hipStream_t st)
     // bf16: the LDS-DMA GEMM with each group's K range (the padded rows are
     // multiples of 64 whatever the layer's tier).  Tiles cover the weights,
     // M x N per group: 256 x 256 when they fill at least two rounds of one
-    // block per CU, else 128 x 128.  Chosen from measurements: with 64 < rows
-    // per expert < 256 (a few K steps per tile) wgrad_kernel below, four
-    // resident blocks per CU, overlaps the short K loops better.
+    // block per CU (256 x 128 with two 4-wave blocks per CU when a group has
+    // at most 64 rows: its tiles are almost all epilogue writes), else
+    // 128 x 128.  Chosen from measurements: with 64 < rows per expert < 256 (a
+    // few K steps per tile) wgrad_kernel below, four resident blocks per CU,
+    // overlaps the short K loops better.
     const WgradGemm g{w.A, w.lda, w.B, w.ldb, w.poff, w.g0, groups, w.M, w.N, w.C};
     const int64_t large = int64_t(groups) * ceil_div(w.M, 256) * ceil_div(w.N, 256);
-    const int shape = large >= 512 ? kGemmDmaLarge : kGemmDmaMid;
+    const int shape = large < 512 ? kGemmDmaMid : rows_avg <= 64 ? kGemmDmaSmall : kGemmDmaLarge;
     if ((rows_avg >= 256 || rows_avg <= 64) && wgrad_dma_fits(shape, g)) {
       (void)launch_wgrad_dma(shape, g, st);
       return;

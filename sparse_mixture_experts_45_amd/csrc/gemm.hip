@@ -1054,7 +1054,7 @@ static void run_wgrad_dma(const WgradGemm& w, hipStream_t st) {
 }
 
 bool wgrad_dma_fits(int shape, const WgradGemm& w) {
-  if (shape != kGemmDmaLarge && shape != kGemmDmaMid) return false;
+  if (shape != kGemmDmaLarge && shape != kGemmDmaMid && shape != kGemmDmaSmall) return false;
   // 16-byte LDS-DMA chunks along K; 32-bit byte offsets inside a row tile of
   // A (whose base is per tile) and inside B
   const bool k16 = w.lda % 8 == 0 && w.ldb % 8 == 0 &&
@@ -1069,6 +1069,11 @@ hipError_t launch_wgrad_dma(int shape, const WgradGemm& w, hipStream_t st) {
   if (shape == kGemmDmaLarge) {
     constexpr DmaCfg C = kDmaLarge;
     run_wgrad_dma<C.BM, C.BNU, C.BK, C.NS, C.WM, C.WN, C.OCC>(w, st);
+  } else if (shape == kGemmDmaSmall) {
+    // groups of at most a few rows (one or two K steps): 256 x 128 tiles of 4
+    // waves with 32-wide K steps, two blocks per CU, so one block's loads
+    // overlap the other's epilogue writes
+    run_wgrad_dma<256, 128, 32, 2, 2, 2, 2>(w, st);
   } else {
     constexpr DmaCfg C = kDmaMid;
     run_wgrad_dma<C.BM, C.BNU, C.BK, C.NS, C.WM, C.WN, C.OCC>(w, st);

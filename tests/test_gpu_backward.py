@@ -155,11 +155,13 @@ def test_forward_train_output_equals_forward():
     assert torch.equal(y.view(torch.int16), ref["y_raw"].view(torch.int16))
 
 
-@pytest.mark.parametrize("name,n_tok", [("page1_b4s512", 48), ("mixtral_t4096", 12)])
+@pytest.mark.parametrize("name,n_tok", [("page1_b4s512", 48), ("mixtral_t4096", 12),
+                                        ("deepseek_e256_top8", 12)])
 def test_backward_workload(name, n_tok):
     """Full-size shapes: dx on sampled tokens, entries of two experts' weight
     gradients (and the bias gradients at those entries), and, for page-1, the
-    router gradients from every token's dl."""
+    router gradients from every token's dl.  The DeepSeek shape (16 rows per
+    expert) runs the weight gradients with one or two K steps per tile."""
     shape = workload(name)
     say("workload", shape)
     inp = make_inputs(shape, 0)
