@@ -93,6 +93,9 @@ TALL = [
     (L("tall_up2", T=4096, d=4096, F=1024, E=32, k=1, router_bias="none"), (2, 1)),
     (L("tall_down2", T=4096, d=1024, F=4096, E=32, k=1, act="relu", router_bias="none"),
      (1, 2)),
+    # a shared expert narrower than the routed ones: 22 more row tiles, no
+    # split, and the input-gradient pass skips the tiles past its width
+    (L("tall_shared", T=4096, d=1024, F=1024, E=32, k=1, Fs=512, router_bias="none"), (1, 1)),
 ]
 
 
