@@ -220,14 +220,19 @@ def traffic_summarize(args):
         total += fb + wb
     rec["traffic_bytes_per_call"] = round(total)
     wl = args.workload
+    # the profiler runs that wrote the two databases: output directory and
+    # file prefix read back from their paths
+    runs = []
+    for db in (fetch_db, write_db):
+        rel = os.path.relpath(os.path.abspath(db), ROOT)
+        runs.append((rel, os.path.dirname(rel), os.path.basename(rel)[:-len("_results.db")]))
     cmds = [
         "cd /tmp && export TMPDIR=/tmp   # then, from the repository root:",
-        "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/traffic_fetch -o run -- "
-        "python3 bench.py --traffic-probe --workload %s" % wl,
-        "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/traffic_write -o run -- "
-        "python3 bench.py --traffic-probe --workload %s" % wl,
-        "python3 bench.py --workload %s --traffic-summarize "
-        "gpurun_out/traffic_fetch/run_results.db gpurun_out/traffic_write/run_results.db" % wl,
+        "rocprofv3 --pmc FETCH_SIZE -d %s -o %s -- "
+        "python3 bench.py --traffic-probe --workload %s" % (runs[0][1], runs[0][2], wl),
+        "rocprofv3 --pmc WRITE_SIZE -d %s -o %s -- "
+        "python3 bench.py --traffic-probe --workload %s" % (runs[1][1], runs[1][2], wl),
+        "python3 bench.py --workload %s --traffic-summarize %s %s" % (wl, runs[0][0], runs[1][0]),
     ]
     lines = [
         "# HBM traffic of the expert grouped GEMM: %s" % wl, "",
