@@ -887,11 +887,13 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
                                                            RowTile* __restrict__ tiles,
                                                            int32_t* __restrict__ ntiles,
                                                            float* __restrict__ row_gate) {
+  // block 0 builds the tile list; every block fills the gates of its
+  // kMaxExperts rows (the grid covers the host's bound on the row count)
   __shared__ int32_t wsum[kMaxExperts / 64];
-  build_tile_list(offsets, G, BM, tiles, ntiles, wsum);
-  const int g = threadIdx.x;
+  if (blockIdx.x == 0) build_tile_list(offsets, G, BM, tiles, ntiles, wsum);
   const int routed = offsets[E], nrows = offsets[G];
-  for (int r = g; r < nrows; r += kMaxExperts)
+  const int r = static_cast<int>(blockIdx.x) * kMaxExperts + static_cast<int>(threadIdx.x);
+  if (r < nrows)
     row_gate[r] = r >= routed ? 1.0f
                   : k > 0     ? topk_w[static_cast<int64_t>(row_token[r]) * k + row_slot[r]]
                               : topk_w[r];
@@ -1084,7 +1086,9 @@ hipError_t launch_wgrad_dma(int shape, const WgradGemm& w, hipStream_t st) {
 hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const int G = f.E + (f.Fs > 0 ? 1 : 0);
   if (!f.tiles_ready)
-    build_tiles_kernel<<<1, kMaxExperts, 0, st>>>(f.offsets, G, gp.BM, f.E,
+    build_tiles_kernel<<<static_cast<unsigned>(std::max<int64_t>(1, ceil_div(f.rows_max,
+                                                                              kMaxExperts))),
+                         kMaxExperts, 0, st>>>(f.offsets, G, gp.BM, f.E,
                                                   f.row_gates ? 0 : f.k, f.row_token,
                                                   f.row_slot, f.topk_w, f.tiles, f.ntiles,
                                                   f.row_gate);

@@ -91,6 +91,7 @@ struct FfnArgs {
   RowTile* tiles;    // [tiles_max]
   int32_t* ntiles;   // [1 + kSplitSlots]: the tile count, then the split counters
   float* row_gate;   // [rows_max]
+  int64_t rows_max;  // bound on the routed plus shared rows (grid of the tile-list kernel)
   int tiles_ready;   // tiles, ntiles and row_gate already written by the dispatch
   int row_gates;     // topk_w holds one gate per routed row (expert choice)
   int pass;          // kPassForward, kPassForwardTrain (also keeps z in Z) or

@@ -283,6 +283,7 @@ moe_status run_ffn(const moe_config* c, const Layout& L, const void* x, const mo
   f.ntiles = reinterpret_cast<int32_t*>(at(ws, L.ntiles));
   f.row_gate = reinterpret_cast<float*>(at(ws, L.row_gate));
   f.tiles_ready = tiles_ready ? 1 : 0;
+  f.rows_max = L.rows_max;
   f.row_gates = expert_choice(c) ? 1 : 0;
   f.pass = pass;
   f.Z = pass == kPassForwardTrain ? at(ws, L.Z) : nullptr;
