@@ -12,7 +12,13 @@ Measurement legs:
   * roofline: the expert grouped GEMM (one moe_expert_ffn call: the up- and
     down-projection kernels) timed with HIP events on the stream it runs on,
     over --steps calls, against the bf16 MFMA peak (or HBM peak when the
-    workload is weight-bandwidth bound).
+    workload is weight-bandwidth bound).  The default workload is the
+    Mixtral-shaped layer (T=4096, d=4096, d_ff=14336, 8 experts, top-2), where
+    the expert GEMM is bound by the matrix cores.
+  * roofline_hbm: the same measurement on a second, weight-streaming workload
+    (default: the DeepSeek-shaped layer, T=512, 256 experts top-8 plus a
+    shared expert, 15 GB of bf16 expert weights) against the HBM peak, with
+    that layer's own forward time.
   * cpu_baseline: the fp64 oracle on a bounded sample of the same batch, on
     the host cores (rank 0, one GPU only).
 """
@@ -41,7 +47,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="page1_b4s512")
+    p.add_argument("--workload", default="mixtral_t4096")
+    p.add_argument("--hbm-workload", default="deepseek_e256_top8",
+                   help="second workload whose expert FFN is timed against the HBM peak "
+                        "(roofline_hbm); 'none' to skip")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -53,6 +62,10 @@ def parse():
                         "copy of known size, then moe_expert_ffn calls")
     p.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="turn the two probe databases into the stored traffic summary")
+    p.add_argument("--trace-summarize", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"),
+                   help="turn a rocprofv3 --kernel-trace --stats run of this bench (its "
+                        "kernel_stats.csv and the JSON line it printed) into the stored "
+                        "kernel-trace summary")
     p.add_argument("--backward", action="store_true",
                    help="time a training step (moe_forward_train + moe_backward with every "
                         "gradient and the balance term) instead of the forward")
@@ -259,6 +272,73 @@ def traffic_summarize(args):
     print(json.dumps(rec))
 
 
+def trace_path(workload):
+    return os.path.join(ROOT, "profiles", "kernel_trace_%s.md" % workload)
+
+
+def trace_summarize(args):
+    """Kernel-trace summary of one profiled bench run: every kernel's call count
+    and durations from rocprofv3's kernel_stats.csv, and the expert FFN per call
+    (row-tile list + up GEMM + down GEMM averages) turned into the roofline
+    fraction with the algorithmic work of the workload the run reported."""
+    import csv
+    stats_csv, bench_json = args.trace_summarize
+    line = [ln for ln in open(bench_json) if ln.lstrip().startswith("{")][-1]
+    run = json.loads(line)
+    from moe_synth import workload
+    shape = workload(run["config"]["workload"])
+    kept_rows, hit = run["config"]["kept_rows"], run["config"]["experts_hit"]
+    rows = list(csv.DictReader(open(stats_csv)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    up = [r for r in rows if "grouped_gemm" in r["Name"] and gemm_mode(r["Name"]) == GEMM_MODE_UP]
+    dn = [r for r in rows if "grouped_gemm" in r["Name"] and gemm_mode(r["Name"]) == GEMM_MODE_DOWN]
+    tl = [r for r in rows if "build_tiles_kernel" in r["Name"]]
+    if len(up) != 1 or len(dn) != 1:
+        sys.exit("expected one up- and one down-projection GEMM kernel in %s" % stats_csv)
+    us = lambda r: float(r["AverageNs"]) / 1e3  # noqa: E731
+    ffn_us = us(up[0]) + us(dn[0]) + (us(tl[0]) if tl else 0.0)
+    flop, nbytes = algorithmic(shape, kept_rows, hit)
+    rel = os.path.relpath(os.path.abspath(stats_csv), ROOT)
+    s = shape
+    lines = [
+        "# Kernel trace: bench.py forward, %s (T=%d, d=%d, d_ff=%d, E=%d, top-%d, %s, %s%s%s)"
+        % (s.name, s.T, s.d, s.F, s.E, s.k, s.act.upper() if s.act == "gelu" else "ReLU",
+           s.dtype, ", capacity %d" % s.capacity if s.capacity >= 0 else "",
+           ", shared expert d_ff %d" % s.Fs if s.Fs else ""), "",
+        "Commands (from the repository root, on one MI355X; `cd /tmp && export TMPDIR=/tmp` "
+        "first for the profiler's scratch files):", "", "```",
+        "rocprofv3 --kernel-trace --stats -d %s -o run -- python3 bench.py --workload %s "
+        "--hbm-workload none --no-cpu-baseline --steps 20 --warmup 5 > %s"
+        % (os.path.dirname(rel), s.name, os.path.relpath(os.path.abspath(bench_json), ROOT)),
+        "python3 bench.py --trace-summarize %s %s"
+        % (rel, os.path.relpath(os.path.abspath(bench_json), ROOT)),
+        "```", "",
+        "| kernel | calls | avg (us) | min (us) | max (us) | share |",
+        "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f %% |" % (
+            r["Name"], r["Calls"], us(r), float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            100.0 * float(r["TotalDurationNs"]) / total))
+    lines += ["", "Expert FFN per call (averages): row-tile list %.2f + up-projection %.2f + "
+              "down-projection %.2f = %.2f us." % (us(tl[0]) if tl else 0.0, us(up[0]),
+                                                   us(dn[0]), ffn_us),
+              "Algorithmic work of the call (%d kept routed rows, %d experts hit): %.4g FLOP, "
+              "%.4g bytes." % (kept_rows, hit, flop, nbytes),
+              "From the trace: %.1f TFLOP/s = %.4f of the 2500 TFLOP/s bf16 peak; %.1f GB/s = "
+              "%.4f of the 8000 GB/s HBM peak." % (
+                  flop / (ffn_us * 1e-6) / 1e12, flop / (ffn_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                  nbytes / (ffn_us * 1e-6) / 1e9, nbytes / (ffn_us * 1e-6) / 1e9 / PEAK_HBM_GBS),
+              "The same run's bench line (events around graph replays, no profiler): "
+              "expert FFN %.4f ms, roofline fraction %.4f (%s bound); layer %.4f ms per call, "
+              "%.1f tokens/s." % (run["roofline"]["kernel_ms"], run["roofline"]["frac"],
+                                  run["roofline"]["bound"], run["ms_per_step"], run["value"]),
+              ""]
+    with open(trace_path(s.name), "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def algorithmic(shape, kept_rows, hit_experts):
     """Active FLOPs and algorithmic HBM bytes of one expert-FFN call."""
     elt = 2 if shape.dtype == "bf16" else 4
@@ -267,9 +347,10 @@ def algorithmic(shape, kept_rows, hit_experts):
     if shape.Fs:
         flop += 4.0 * shape.T * shape.d * shape.Fs
         wbytes += (2.0 * shape.d * shape.Fs + shape.Fs + shape.d) * elt
-    # activations: read x rows once, write y rows once (fp32 expert rows)
-    nrows = kept_rows + (shape.T if shape.Fs else 0)
-    abytes = shape.T * shape.d * elt + nrows * shape.d * 4
+    # activations: x read once and the layer output y written once, both in the
+    # layer dtype (the grouped rows, H and the fp32 expert rows are
+    # intermediates of this implementation, not algorithmic bytes)
+    abytes = 2 * shape.T * shape.d * elt
     return flop, wbytes + abytes
 
 
@@ -402,10 +483,123 @@ def bench_backward(args):
     print(json.dumps(out), flush=True)
 
 
+def time_layer(moe, torch, shape, dev, steps, warmup, use_graph):
+    """moe_forward over `steps` calls (replayed from a HIP graph when use_graph),
+    bracketed by device synchronisation.  Returns (seconds, kept [E] counts)."""
+    tdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    cfg = layer_config(moe, torch, shape)
+    ws = moe.workspace(cfg)
+    T, E = shape.T, shape.E
+    x = dev["x"]
+    y = torch.empty((T, shape.d), dtype=tdt, device="cuda")
+    st = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+              kept=torch.empty(E, dtype=torch.int32, device="cuda"))
+    stream = torch.cuda.Stream()
+
+    def step():
+        moe.moe_forward(cfg, dev, x, y, st, ws, stream=stream)
+
+    torch.cuda.synchronize()
+    graph = None
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            step()
+    torch.cuda.synchronize()
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                graph.replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` layer calls
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kept = st["kept"].cpu().numpy()
+    del graph, ws
+    return elapsed, kept
+
+
+def ffn_roofline(moe, torch, shape, dev, kept, steps, use_graph):
+    """The expert FFN (one moe_expert_ffn call: row-tile list, up-projection GEMM,
+    down-projection GEMM) timed with HIP events on the stream it is launched on:
+    FFN_REPS back-to-back calls per graph replay, `steps` replays.  Returns the
+    roofline object against the bf16 MFMA peak or the HBM peak, whichever bounds
+    the call's algorithmic work."""
+    kept_rows = int(kept.sum())
+    hit = int((kept > 0).sum())
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        fargs = ffn_call(moe, torch, shape, dev, stream=stream)
+        for _ in range(3):
+            moe.moe_expert_ffn(*fargs, stream=stream)
+    torch.cuda.synchronize()
+    # FFN_REPS moe_expert_ffn calls (tile list, up GEMM, down GEMM each)
+    # replayed from one graph: the events bracket the kernels without host
+    # launch gaps, and the graph's own launch latency is paid once per
+    # FFN_REPS calls, as in a model whose layers share one graph
+    ffn_graph = None
+    if use_graph:
+        ffn_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ffn_graph, stream=stream):
+            for _ in range(FFN_REPS):
+                moe.moe_expert_ffn(*fargs, stream=stream)
+        torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            a.record(stream)
+            if ffn_graph is not None:
+                ffn_graph.replay()
+            else:
+                for _ in range(FFN_REPS):
+                    moe.moe_expert_ffn(*fargs, stream=stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / FFN_REPS
+    del ffn_graph, fargs
+
+    flop, nbytes = algorithmic(shape, kept_rows, hit)
+    ai = flop / nbytes
+    if ai >= RIDGE:
+        peak = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
+        achieved = flop / (ffn_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    else:
+        achieved = nbytes / (ffn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    traffic = stored_traffic(shape.name)
+    roof["traffic"] = None if traffic is None else float(traffic)
+    roof.update(kernel="expert FFN: one moe_expert_ffn call (row-tile list, up-projection "
+                       "GEMM, down-projection GEMM), timed as %d back-to-back calls"
+                       % FFN_REPS, kernel_ms=round(ffn_ms, 4),
+                algorithmic_flop=flop, algorithmic_bytes=nbytes,
+                achieved_tflops=round(flop / (ffn_ms * 1e-3) / 1e12, 2),
+                achieved_gbs=round(nbytes / (ffn_ms * 1e-3) / 1e9, 1))
+    return roof
+
+
 def main():
     args = parse()
     if args.traffic_summarize:
         traffic_summarize(args)
+        return
+    if args.trace_summarize:
+        trace_summarize(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the MoE layer here is the data-parallel "
@@ -427,100 +621,13 @@ def main():
     shape = workload(args.workload)
     inp = make_inputs(shape, args.seed)
     dev = to_device(inp, "cuda")
-    tdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
-    cfg = layer_config(moe, torch, shape)
-    ws = moe.workspace(cfg)
     T, k, E = shape.T, shape.k, shape.E
-    x = dev["x"]
-    y = torch.empty((T, shape.d), dtype=tdt, device="cuda")
-    st = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
-              kept=torch.empty(E, dtype=torch.int32, device="cuda"))
-    stream = torch.cuda.Stream()
-
-    def step():
-        moe.moe_forward(cfg, dev, x, y, st, ws, stream=stream)
-
-    torch.cuda.synchronize()
-    graph = None
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            step()
-    torch.cuda.synchronize()
-    if args.graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            step()
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            for _ in range(2):
-                graph.replay()
-        torch.cuda.synchronize()
-
-    # ---- timed region: exactly K steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        for _ in range(args.steps):
-            if graph is not None:
-                graph.replay()
-            else:
-                step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed, kept = time_layer(moe, torch, shape, dev, args.steps, args.warmup, args.graph)
     ms_per_step = elapsed * 1e3 / args.steps
-
-    kept = st["kept"].cpu().numpy()
     kept_rows = int(kept.sum())
     hit = int((kept > 0).sum())
-
-    # ---- expert grouped GEMM (one moe_expert_ffn call) timed with HIP events
-    with torch.cuda.stream(stream):
-        fargs = ffn_call(moe, torch, shape, dev, stream=stream)
-        for _ in range(3):
-            moe.moe_expert_ffn(*fargs, stream=stream)
-    torch.cuda.synchronize()
-    # FFN_REPS moe_expert_ffn calls (tile list, up GEMM, down GEMM each)
-    # replayed from one graph: the events bracket the kernels without host
-    # launch gaps, and the graph's own launch latency is paid once per
-    # FFN_REPS calls, as in a model whose layers share one graph
-    ffn_graph = None
-    if args.graph:
-        ffn_graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(ffn_graph, stream=stream):
-            for _ in range(FFN_REPS):
-                moe.moe_expert_ffn(*fargs, stream=stream)
-        torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    with torch.cuda.stream(stream):
-        for a, b in evs:
-            a.record(stream)
-            if ffn_graph is not None:
-                ffn_graph.replay()
-            else:
-                for _ in range(FFN_REPS):
-                    moe.moe_expert_ffn(*fargs, stream=stream)
-            b.record(stream)
-    torch.cuda.synchronize()
-    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / FFN_REPS
-
-    flop, nbytes = algorithmic(shape, kept_rows, hit)
-    ai = flop / nbytes
-    if ai >= RIDGE:
-        peak = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
-        achieved = flop / (ffn_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
-    else:
-        achieved = nbytes / (ffn_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
-    traffic = stored_traffic(shape.name)
-    roof["traffic"] = None if traffic is None else float(traffic)
-    roof.update(kernel="expert FFN: one moe_expert_ffn call (row-tile list, up-projection "
-                       "GEMM, down-projection GEMM), timed as %d back-to-back calls"
-                       % FFN_REPS, kernel_ms=round(ffn_ms, 4),
-                algorithmic_flop=flop, algorithmic_bytes=nbytes)
+    roof = ffn_roofline(moe, torch, shape, dev, kept, args.steps, args.graph)
+    flop, _ = algorithmic(shape, kept_rows, hit)
 
     value = T * args.steps / elapsed
     out = {
@@ -533,13 +640,28 @@ def main():
         "config": {"workload": shape.name, "tokens": T, "d_model": shape.d, "d_ff": shape.F,
                    "n_experts": E, "top_k": k, "capacity": shape.capacity,
                    "shared_d_ff": shape.Fs, "act": shape.act, "routing": shape.routing,
-                   "hip_graph": bool(graph),
+                   "hip_graph": bool(args.graph),
                    "kept_rows": kept_rows, "experts_hit": hit},
         "layer_tflops": round(flop / (ms_per_step * 1e-3) / 1e12, 2),
         "roofline": roof,
     }
+    del dev
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, inp, args.cpu_seconds)
+    del inp
+    if args.hbm_workload and args.hbm_workload != "none" and args.hbm_workload != shape.name:
+        # the weight-streaming workload, measured the same way on its own inputs
+        s2 = workload(args.hbm_workload)
+        dev2 = to_device(make_inputs(s2, args.seed), "cuda")
+        el2, kept2 = time_layer(moe, torch, s2, dev2, args.steps, args.warmup, args.graph)
+        r2 = ffn_roofline(moe, torch, s2, dev2, kept2, args.steps, args.graph)
+        r2.update(workload=s2.name, layer_ms=round(el2 * 1e3 / args.steps, 4),
+                  layer_tokens_per_s=round(s2.T * args.steps / el2, 1),
+                  kept_rows=int(kept2.sum()), experts_hit=int((kept2 > 0).sum()))
+        out["roofline_hbm"] = r2
+        del dev2
+        torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 

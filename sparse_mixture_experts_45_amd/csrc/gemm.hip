@@ -710,16 +710,16 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
             mine[((i * NI + j) * 4 + c) * NT + tid] =
                 make_float4(acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
                             acc[i][j][4 * c + 3]);
-      // Each wave waits until its stores have reached the L2; after the
-      // barrier one thread writes this XCD's L2 back (agent-scope release) and
-      // counts the arrival; the last part invalidates its stale L2 lines
+      // Each wave waits until its stores have reached the L2; the workgroup
+      // barrier (with its workgroup-scope fences) orders every wave's stores
+      // before thread 0's agent-scope release, which writes this XCD's L2 back,
+      // and the arrival count; the last part invalidates its stale L2 lines
       // (agent-scope acquire) before any wave reads the other parts' slots.
       // One release per part and one acquire per tile: each is a whole-L2
       // operation, so no wave beyond the first does either.
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __syncthreads();
       if (tid == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         // the write-back has completed before the arrival is counted (an

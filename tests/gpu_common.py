@@ -115,7 +115,30 @@ def rel_l2(a, b):
     return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
 
 
+def check_rows(shape, got, ref, what="y"):
+    """Row by row (first axis; the rest flattened): rows the reference sets to
+    exactly zero are exactly zero here, and every other row is within 5x the
+    layer tolerance of its reference row, so a wrong row, row tile or column
+    band cannot hide under a global norm over many correct rows."""
+    if ref.size == 0:
+        return 0.0
+    g2 = np.asarray(got, np.float64).reshape(ref.shape[0], -1)
+    r2 = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
+    nz = np.linalg.norm(r2, axis=1)
+    zero = nz == 0
+    assert np.all(g2[zero] == 0.0), (what, "rows that must be zero", np.nonzero(zero)[0][:8])
+    tol = 5 * (Y_F32_REL_L2 if shape.dtype == "f32" else Y_BF16_REL_L2)
+    if not (~zero).any():
+        return 0.0
+    r = np.linalg.norm(g2[~zero] - r2[~zero], axis=1) / nz[~zero]
+    worst = int(np.argmax(r))
+    assert float(r[worst]) <= tol, (what, "row", int(np.nonzero(~zero)[0][worst]), float(r[worst]))
+    return float(r[worst])
+
+
 def check_y(shape, got, ref, what="y"):
+    """Global rel-L2 (and max-abs for fp32) at the layer tolerance, and the
+    per-row check above."""
     if ref.size == 0:
         return
     r = rel_l2(got, ref)
@@ -124,6 +147,7 @@ def check_y(shape, got, ref, what="y"):
         assert r <= Y_F32_REL_L2 and m <= Y_F32_MAX_ABS, (what, r, m)
     else:
         assert r <= Y_BF16_REL_L2, (what, r)
+    check_rows(shape, got, ref, what)
     return r
 
 

@@ -24,19 +24,39 @@ def test_more_than_one_gpu_is_refused():
 def test_algorithmic_work_page1():
     """page-1 shape: 4096 kept rows of d=768, d_ff=3072, 8 experts hit:
     FLOP = 4 * rows * d * d_ff; bytes = bf16 W1, b1, W2, b2 of 8 experts + bf16 x
-    + fp32 expert rows."""
+    read once + bf16 y written once (no intermediates)."""
     s = workload("page1_b4s512")
     flop, nbytes = bench.algorithmic(s, 4096, 8)
     assert flop == 4.0 * 4096 * 768 * 3072
     w = 8 * (2 * 768 * 3072 + 3072 + 768) * 2
-    assert nbytes == w + 2048 * 768 * 2 + 4096 * 768 * 4
+    assert nbytes == w + 2 * 2048 * 768 * 2
 
 
 def test_algorithmic_work_shared_expert():
     s = workload("deepseek_e256_top8")
     flop, nbytes = bench.algorithmic(s, 4096, 256)
     assert flop == 4.0 * 4096 * 7168 * 2048 + 4.0 * 512 * 7168 * 2048
-    assert nbytes > 257 * 2 * 7168 * 2048 * 2
+    w = 257 * (2 * 7168 * 2048 + 2048 + 7168) * 2
+    assert nbytes == w + 2 * 512 * 7168 * 2
+
+
+def test_default_workloads():
+    """The default bench line is the Mixtral-shaped layer (matrix-core bound) with
+    the DeepSeek-shaped layer (weight streaming) as its second roofline."""
+    old = sys.argv
+    sys.argv = ["bench.py"]
+    try:
+        a = bench.parse()
+    finally:
+        sys.argv = old
+    assert a.workload == "mixtral_t4096"
+    assert a.hbm_workload == "deepseek_e256_top8"
+    s = workload(a.workload)
+    flop, nbytes = bench.algorithmic(s, s.T * s.k, s.E)
+    assert flop / nbytes > bench.RIDGE
+    s2 = workload(a.hbm_workload)
+    flop2, nbytes2 = bench.algorithmic(s2, s2.T * s2.k, s2.E)
+    assert flop2 / nbytes2 < bench.RIDGE
 
 
 @pytest.mark.parametrize("name,mode", [

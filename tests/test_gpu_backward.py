@@ -16,7 +16,7 @@ import torch
 import oracle
 import sparse_mixture_experts_45_amd as moe
 from moe_synth import LayerShape, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs, workload
-from gpu_common import cfg_of, device_inputs, rel_l2, say, torch_dtype
+from gpu_common import cfg_of, check_rows, device_inputs, rel_l2, say, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -61,10 +61,14 @@ def gpu_backward(shape, dev, dy_dev, alpha, names=None):
 
 
 def check(shape, got, want, what):
+    """Global rel-L2 at the layer tolerance and, per row (per token for dx, per
+    expert or weight row for the parameter gradients), within 5x of it."""
     tol = F32_REL_L2 if shape.dtype == "f32" else BF16_REL_L2
     assert np.all(np.isfinite(got)), what
     r = rel_l2(got, want)
     assert r <= tol, (what, r)
+    if want.ndim >= 2:
+        check_rows(shape, got, want, what)
     return r
 
 

@@ -178,7 +178,12 @@ def test_dispatch_stage(shape):
 
 @pytest.mark.parametrize("shape", [S("ffn_bf16", T=260, d=136, F=200, E=6, k=2, Fs=72),
                                    S("ffn_f32", dtype="f32", T=100, d=72, F=136, E=5, k=2,
-                                     capacity=30, Fs=40)],
+                                     capacity=30, Fs=40),
+                                   # more than 2048 grouped rows: the row gates of the
+                                   # tile-list kernel span three and four blocks
+                                   S("ffn_bf16_2400_rows", T=1200, d=128, F=192, E=6, k=2),
+                                   S("ffn_bf16_3600_rows_shared", T=1200, d=128, F=192, E=6,
+                                     k=2, Fs=64, capacity=350)],
                          ids=lambda s: s.name)
 def test_expert_ffn_stage(shape):
     """Per-row gated expert outputs from the oracle's grouping and gates."""
@@ -210,6 +215,43 @@ def test_expert_ffn_stage(shape):
             ref[row] = oracle.expert_row(shape, inp, t, e, g)
     check_y(shape, got[:len(ref)], ref, "y_rows")
     assert np.all(got[len(ref):] == 0.0)
+
+
+@pytest.mark.parametrize("Fs", [0, 64])
+def test_expert_ffn_stage_expert_choice(Fs):
+    """moe_expert_ffn under expert choice (one gate per routed row, rows e*C + j
+    = the j-th token expert e took, ascending) over 2400 routed rows (+ 1000
+    shared rows): every row against the oracle's gated expert output."""
+    shape = S("ffn_ec", T=1000, d=128, F=192, E=8, k=2, capacity=300, Fs=Fs,
+              routing="expert")
+    say("case", shape)
+    inp = make_inputs(shape, 5)
+    r = oracle.ec_route(shape, inp)
+    T, E, C = shape.T, shape.E, r["C"]
+    toks = [np.nonzero(r["sel"][:, e])[0] for e in range(E)]
+    assert all(len(t) == C for t in toks)
+    nrows = E * C + (T if Fs else 0)
+    row_token = np.concatenate(toks + ([np.arange(T)] if Fs else [])).astype(np.int32)
+    gates = np.concatenate([r["p"][toks[e], e] for e in range(E)]).astype(np.float32)
+    offsets = (np.arange(E + 2) * C).astype(np.int32)
+    offsets[E + 1] = nrows
+    dev = device_inputs(inp)
+    c = cfg_of(shape)
+    ws = moe.workspace(c)
+    y_rows = torch.zeros((nrows, shape.d), dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn(c, dev["x"], dev, torch.from_numpy(offsets).cuda(),
+                       torch.from_numpy(row_token).cuda(), None,
+                       torch.from_numpy(gates).cuda(), y_rows, ws)
+    torch.cuda.synchronize()
+    got = y_rows.cpu().numpy().astype(np.float64)
+    ref = np.zeros((nrows, shape.d))
+    for row in range(nrows):
+        t = int(row_token[row])
+        if row >= E * C:
+            ref[row] = oracle.expert_row(shape, inp, t, -1, 1.0)
+        else:
+            ref[row] = oracle.expert_row(shape, inp, t, row // C, float(gates[row]))
+    check_y(shape, got, ref, "y_rows")
 
 
 @pytest.mark.parametrize("dtype,shared", [("f32", 0), ("bf16", 24), ("f32", 16)])

@@ -4,8 +4,12 @@ benchmark times (moe_forward with the library's own tile choice).
 Routing, counts, kept counts and the load statistics are checked for every
 token; the grouping arrays are checked in full through moe_dispatch fed the
 oracle's routing; layer outputs are checked on a sample of tokens the oracle
-computes one by one (spread over the batch, plus, with a capacity limit,
-dropped tokens and the last tokens kept by the fullest expert).
+computes one by one: spread over the batch; the tokens behind the first and
+last grouped row of every 32-row block of every expert (and of the shared
+expert), so every row tile of every tile height the library uses (all
+multiples of 32 rows), including the tiles of a K-split last round, has rows
+checked at both ends; with a capacity limit also dropped tokens and the last
+tokens kept by the fullest expert.  Each sampled token is compared row by row.
 """
 import numpy as np
 import pytest
@@ -22,10 +26,30 @@ SAMPLES = {"tiny_f32": None, "page1_b4s512": 96, "mixtral_t4096": 24,
            "switch_e64_top1_cap": 64, "deepseek_e256_top8": 32, "deepseek_ep8_rank": 32}
 
 
+TILE_GRAIN = 32  # every row-tile height of the grouped GEMM is a multiple of this
+
+
+def tile_boundary_tokens(shape, ref):
+    """Tokens of the first and last grouped row of every TILE_GRAIN-row block of
+    every group (routed experts, then the shared expert), from the oracle's
+    grouping."""
+    d = oracle.dispatch(shape, ref["topk_idx"], ref["keep"])
+    off = d["offsets"]
+    groups = shape.E + (1 if shape.Fs else 0)
+    toks = set()
+    for g in range(groups):
+        a, b = int(off[g]), int(off[g + 1])
+        for r0 in range(a, b, TILE_GRAIN):
+            toks.add(int(d["row_token"][r0]))
+            toks.add(int(d["row_token"][min(r0 + TILE_GRAIN, b) - 1]))
+    return toks
+
+
 def sample_tokens(shape, ref, n):
     if n is None:
         return np.arange(shape.T)
     toks = set(np.linspace(0, shape.T - 1, n).astype(int).tolist())
+    toks.update(tile_boundary_tokens(shape, ref))
     if shape.capacity >= 0:
         dropped = np.nonzero(ref["keep"].min(axis=1) == 0)[0]
         toks.update(dropped[:8].tolist())

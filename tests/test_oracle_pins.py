@@ -311,6 +311,62 @@ def test_dispatch_grouping():
     assert np.array_equal(d["row_token"][off[shape.E]:], np.arange(shape.T))
 
 
+def _torch_expert_rows(shape, inp, toks, e):
+    """E_e(x_t) for the listed tokens as torch CPU library calls, fp64
+    (e = -1: the shared expert)."""
+    dt = shape.dtype
+    x = widen(inp["x"], dt)[toks]
+    act = (lambda z: Fn.gelu(z)) if shape.act == "gelu" else torch.relu
+    if e < 0:
+        W1, b1, W2, b2 = (widen(inp[n], dt) for n in ("Ws1", "bs1", "Ws2", "bs2"))
+    else:
+        W1, W2 = widen(inp["W1"], dt)[e], widen(inp["W2"], dt)[e]
+        b1 = None if inp["b1"] is None else widen(inp["b1"], dt)[e]
+        b2 = None if inp["b2"] is None else widen(inp["b2"], dt)[e]
+    return Fn.linear(act(Fn.linear(x, W1, b1)), W2, b2).numpy()
+
+
+@pytest.mark.parametrize("k,Fs", [(2, 8), (3, 0), (1, 8)])
+def test_combine_over_grouped_rows(k, Fs):
+    """The output equation y_t = sum_i g_i E_{e_i}(x_t) (+ S(x_t)) assembled by the
+    gather combine: expert rows computed with torch library calls, each scaled by
+    its gate and placed at the row the dispatch grouping gives it (dropped slots
+    get none, shared rows start at offsets[E]), summed by oracle.combine.  The
+    sum must equal the same equation written per token with the keep mask."""
+    shape = small(T=48, E=5, k=k, capacity=14, Fs=Fs, router_bias="zipf1.1")
+    inp = make_inputs(shape, 19)
+    r = oracle.route(shape, inp)
+    d = oracle.dispatch(shape, r["topk_idx"], r["keep"])
+    T, E = shape.T, shape.E
+    assert (r["keep"] == 0).any(), "the case must drop some slots"
+    off = d["offsets"]
+    nrows = int(off[E + 1])
+    y_rows = np.full((nrows, shape.d), np.nan)
+    for e in range(E):
+        rows = np.arange(off[e], off[e + 1])
+        if rows.size == 0:
+            continue
+        toks, slots = d["row_token"][rows], d["row_slot"][rows]
+        gates = r["topk_w"][toks, slots][:, None]
+        y_rows[rows] = gates * _torch_expert_rows(shape, inp, toks, e)
+    if Fs:
+        y_rows[off[E]:off[E] + T] = _torch_expert_rows(shape, inp, np.arange(T), -1)
+    assert not np.isnan(y_rows).any()
+    got = oracle.combine(shape, y_rows, d["inv"], off)
+    # the same equation per token: kept slots only, gates not renormalised again
+    want = np.zeros((T, shape.d))
+    for t in range(T):
+        for i in range(k):
+            if r["keep"][t, i]:
+                e = int(r["topk_idx"][t, i])
+                want[t] += r["topk_w"][t, i] * _torch_expert_rows(shape, inp, [t], e)[0]
+    if Fs:
+        want += _torch_expert_rows(shape, inp, np.arange(T), -1)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    # and the oracle's own per-token layer output
+    assert np.allclose(got, oracle.experts(shape, inp, r), rtol=0, atol=1e-12)
+
+
 # -------------------------------------------------------------- statistics
 def test_balance_is_torch_std_squared():
     shape = small(T=64, E=8, router_bias="zipf1.1")
