@@ -62,9 +62,9 @@ def parse():
                         "copy of known size, then moe_expert_ffn calls")
     p.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="turn the two probe databases into the stored traffic summary")
-    p.add_argument("--trace-summarize", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"),
+    p.add_argument("--trace-summarize", nargs=2, metavar=("RESULTS_DB", "BENCH_JSON"),
                    help="turn a rocprofv3 --kernel-trace --stats run of this bench (its "
-                        "kernel_stats.csv and the JSON line it printed) into the stored "
+                        "results database and the JSON line it printed) into the stored "
                         "kernel-trace summary")
     p.add_argument("--backward", action="store_true",
                    help="time a training step (moe_forward_train + moe_backward with every "
@@ -276,63 +276,78 @@ def trace_path(workload):
     return os.path.join(ROOT, "profiles", "kernel_trace_%s.md" % workload)
 
 
+def _kernel_durations(db):
+    """{kernel name: [durations in ns]} of every dispatch in a rocprofv3 database."""
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, duration from kernels").fetchall()
+    con.close()
+    out = {}
+    for name, dur in rows:
+        out.setdefault(name, []).append(float(dur))
+    return out
+
+
 def trace_summarize(args):
     """Kernel-trace summary of one profiled bench run: every kernel's call count
-    and durations from rocprofv3's kernel_stats.csv, and the expert FFN per call
+    and durations from the rocprofv3 database, and the expert FFN per call
     (row-tile list + up GEMM + down GEMM averages) turned into the roofline
     fraction with the algorithmic work of the workload the run reported."""
-    import csv
-    stats_csv, bench_json = args.trace_summarize
+    db, bench_json = args.trace_summarize
     line = [ln for ln in open(bench_json) if ln.lstrip().startswith("{")][-1]
     run = json.loads(line)
     from moe_synth import workload
     shape = workload(run["config"]["workload"])
     kept_rows, hit = run["config"]["kept_rows"], run["config"]["experts_hit"]
-    rows = list(csv.DictReader(open(stats_csv)))
-    total = sum(float(r["TotalDurationNs"]) for r in rows)
-    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    up = [r for r in rows if "grouped_gemm" in r["Name"] and gemm_mode(r["Name"]) == GEMM_MODE_UP]
-    dn = [r for r in rows if "grouped_gemm" in r["Name"] and gemm_mode(r["Name"]) == GEMM_MODE_DOWN]
-    tl = [r for r in rows if "build_tiles_kernel" in r["Name"]]
+    durs = _kernel_durations(db)
+    total = sum(sum(v) for v in durs.values())
+    names = sorted(durs, key=lambda n: -sum(durs[n]))
+    gemm = lambda mode: [n for n in names  # noqa: E731
+                         if "grouped_gemm" in n and gemm_mode(n) == mode]
+    up, dn = gemm(GEMM_MODE_UP), gemm(GEMM_MODE_DOWN)
+    tl = [n for n in names if "build_tiles_kernel" in n]
     if len(up) != 1 or len(dn) != 1:
-        sys.exit("expected one up- and one down-projection GEMM kernel in %s" % stats_csv)
-    us = lambda r: float(r["AverageNs"]) / 1e3  # noqa: E731
-    ffn_us = us(up[0]) + us(dn[0]) + (us(tl[0]) if tl else 0.0)
+        sys.exit("expected one up- and one down-projection GEMM kernel in %s" % db)
+    avg = lambda n: float(np.mean(durs[n])) / 1e3  # noqa: E731  (us)
+    t_tl = avg(tl[0]) if tl else 0.0
+    ffn_us = avg(up[0]) + avg(dn[0]) + t_tl
     flop, nbytes = algorithmic(shape, kept_rows, hit)
-    rel = os.path.relpath(os.path.abspath(stats_csv), ROOT)
+    rel_db = os.path.relpath(os.path.abspath(db), ROOT)
+    rel_json = os.path.relpath(os.path.abspath(bench_json), ROOT)
     s = shape
+    tflops = flop / (ffn_us * 1e-6) / 1e12
+    gbs = nbytes / (ffn_us * 1e-6) / 1e9
     lines = [
         "# Kernel trace: bench.py forward, %s (T=%d, d=%d, d_ff=%d, E=%d, top-%d, %s, %s%s%s)"
-        % (s.name, s.T, s.d, s.F, s.E, s.k, s.act.upper() if s.act == "gelu" else "ReLU",
+        % (s.name, s.T, s.d, s.F, s.E, s.k, "GELU" if s.act == "gelu" else "ReLU",
            s.dtype, ", capacity %d" % s.capacity if s.capacity >= 0 else "",
            ", shared expert d_ff %d" % s.Fs if s.Fs else ""), "",
         "Commands (from the repository root, on one MI355X; `cd /tmp && export TMPDIR=/tmp` "
         "first for the profiler's scratch files):", "", "```",
-        "rocprofv3 --kernel-trace --stats -d %s -o run -- python3 bench.py --workload %s "
+        "rocprofv3 --kernel-trace --stats -d %s -o %s -- python3 bench.py --workload %s "
         "--hbm-workload none --no-cpu-baseline --steps 20 --warmup 5 > %s"
-        % (os.path.dirname(rel), s.name, os.path.relpath(os.path.abspath(bench_json), ROOT)),
-        "python3 bench.py --trace-summarize %s %s"
-        % (rel, os.path.relpath(os.path.abspath(bench_json), ROOT)),
+        % (os.path.dirname(rel_db), os.path.basename(rel_db)[:-len("_results.db")], s.name,
+           rel_json),
+        "python3 bench.py --trace-summarize %s %s" % (rel_db, rel_json),
         "```", "",
         "| kernel | calls | avg (us) | min (us) | max (us) | share |",
         "|---|---|---|---|---|---|"]
-    for r in rows:
-        lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f %% |" % (
-            r["Name"], r["Calls"], us(r), float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
-            100.0 * float(r["TotalDurationNs"]) / total))
+    for n in names:
+        v = durs[n]
+        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %.1f %% |" % (
+            n, len(v), avg(n), min(v) / 1e3, max(v) / 1e3, 100.0 * sum(v) / total))
     lines += ["", "Expert FFN per call (averages): row-tile list %.2f + up-projection %.2f + "
-              "down-projection %.2f = %.2f us." % (us(tl[0]) if tl else 0.0, us(up[0]),
-                                                   us(dn[0]), ffn_us),
+              "down-projection %.2f = %.2f us." % (t_tl, avg(up[0]), avg(dn[0]), ffn_us),
+              "",
               "Algorithmic work of the call (%d kept routed rows, %d experts hit): %.4g FLOP, "
-              "%.4g bytes." % (kept_rows, hit, flop, nbytes),
+              "%.4g bytes." % (kept_rows, hit, flop, nbytes), "",
               "From the trace: %.1f TFLOP/s = %.4f of the 2500 TFLOP/s bf16 peak; %.1f GB/s = "
-              "%.4f of the 8000 GB/s HBM peak." % (
-                  flop / (ffn_us * 1e-6) / 1e12, flop / (ffn_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
-                  nbytes / (ffn_us * 1e-6) / 1e9, nbytes / (ffn_us * 1e-6) / 1e9 / PEAK_HBM_GBS),
-              "The same run's bench line (events around graph replays, no profiler): "
-              "expert FFN %.4f ms, roofline fraction %.4f (%s bound); layer %.4f ms per call, "
-              "%.1f tokens/s." % (run["roofline"]["kernel_ms"], run["roofline"]["frac"],
-                                  run["roofline"]["bound"], run["ms_per_step"], run["value"]),
+              "%.4f of the 8000 GB/s HBM peak." % (tflops, tflops / PEAK_BF16_TFLOPS, gbs,
+                                                    gbs / PEAK_HBM_GBS), "",
+              "The profiled run's own bench line (HIP events around graph replays, under the "
+              "profiler): expert FFN %.4f ms, roofline fraction %.4f (%s bound); layer %.4f ms "
+              "per call, %.1f tokens/s." % (run["roofline"]["kernel_ms"], run["roofline"]["frac"],
+                                            run["roofline"]["bound"], run["ms_per_step"],
+                                            run["value"]),
               ""]
     with open(trace_path(s.name), "w") as fh:
         fh.write("\n".join(lines))

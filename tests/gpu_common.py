@@ -115,24 +115,31 @@ def rel_l2(a, b):
     return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
 
 
-def check_rows(shape, got, ref, what="y"):
-    """Row by row (first axis; the rest flattened): rows the reference sets to
-    exactly zero are exactly zero here, and every other row is within 5x the
-    layer tolerance of its reference row, so a wrong row, row tile or column
-    band cannot hide under a global norm over many correct rows."""
+def check_rows(shape, got, ref, what="y", exact_zero=True):
+    """Row by row (first axis; the rest flattened): every row within 5x the layer
+    tolerance of its reference row, relative to the larger of the row's norm
+    and a tenth of the RMS row norm (a row far smaller than the rest, such as
+    the router-gradient row of an expert almost no token picks, carries
+    rounding relative to the larger terms it was computed from); with
+    exact_zero, rows the reference sets to exactly zero (dropped tokens) must
+    be exactly zero here.  A wrong row, row tile or column band cannot hide
+    under a global norm over many correct rows."""
     if ref.size == 0:
         return 0.0
     g2 = np.asarray(got, np.float64).reshape(ref.shape[0], -1)
     r2 = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
     nz = np.linalg.norm(r2, axis=1)
-    zero = nz == 0
-    assert np.all(g2[zero] == 0.0), (what, "rows that must be zero", np.nonzero(zero)[0][:8])
-    tol = 5 * (Y_F32_REL_L2 if shape.dtype == "f32" else Y_BF16_REL_L2)
-    if not (~zero).any():
+    if exact_zero:
+        zero = nz == 0
+        assert np.all(g2[zero] == 0.0), (what, "rows that must be zero", np.nonzero(zero)[0][:8])
+    rms = float(np.sqrt(np.mean(nz ** 2)))
+    if rms == 0.0:
+        assert np.all(g2 == 0.0), (what, "reference is all zero")
         return 0.0
-    r = np.linalg.norm(g2[~zero] - r2[~zero], axis=1) / nz[~zero]
+    tol = 5 * (Y_F32_REL_L2 if shape.dtype == "f32" else Y_BF16_REL_L2)
+    r = np.linalg.norm(g2 - r2, axis=1) / np.maximum(nz, 0.1 * rms)
     worst = int(np.argmax(r))
-    assert float(r[worst]) <= tol, (what, "row", int(np.nonzero(~zero)[0][worst]), float(r[worst]))
+    assert float(r[worst]) <= tol, (what, "row", worst, float(r[worst]))
     return float(r[worst])
 
 

@@ -68,7 +68,7 @@ def check(shape, got, want, what):
     r = rel_l2(got, want)
     assert r <= tol, (what, r)
     if want.ndim >= 2:
-        check_rows(shape, got, want, what)
+        check_rows(shape, got, want, what, exact_zero=False)
     return r
 
 
