@@ -20,7 +20,8 @@
  *  - All array arguments are DEVICE pointers, row-major and contiguous, owned
  *    by the caller.  The library allocates and frees nothing, keeps no state
  *    between calls and is re-entrant; two calls that share a workspace or an
- *    output buffer on different streams race.
+ *    output buffer on different streams race.  (moe_forward_noalloc is the
+ *    one exception: it keeps a static device scratch array per GPU.)
  *  - Expert weights use the nn.Linear layout [out, in]: W1 [E, d_ff, d_model],
  *    W2 [E, d_model, d_ff]; b1 [E, d_ff], b2 [E, d_model].  They, x and y are
  *    fp32 (MOE_F32) or bf16 (MOE_BF16, raw 16-bit patterns) as cfg->dtype
@@ -61,7 +62,9 @@ typedef enum {
   MOE_ERR_INVALID_ARG = -1, /* null required pointer, bad size, misalignment */
   MOE_ERR_UNSUPPORTED = -2, /* valid but outside the limits above */
   MOE_ERR_WORKSPACE = -3,   /* ws NULL, misaligned or smaller than needed */
-  MOE_ERR_HIP = -4          /* a HIP launch failed */
+  MOE_ERR_HIP = -4,         /* a HIP launch failed */
+  MOE_ERR_SCRATCH = -5      /* moe_forward_noalloc: the layer needs more workspace than
+                               MOE_NOALLOC_SCRATCH_BYTES */
 } moe_status;
 
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
@@ -196,6 +199,30 @@ moe_status moe_combine(const moe_config *cfg, const float *y_rows, const int32_t
  */
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
                        moe_stats *stats, void *ws, size_t ws_bytes, void *stream);
+
+/* Device scratch that moe_forward_noalloc uses in place of a workspace. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same layer, same kernels and same results bit for bit as moe_forward, with
+ * the workspace taken from a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends.  The
+ * caller still passes x, y and the weights (and the optional stats).
+ *  - Rejects a config with moe_workspace_bytes(cfg) > MOE_NOALLOC_SCRATCH_BYTES
+ *    with MOE_ERR_SCRATCH before enqueuing anything.
+ *  - Calls no hipMalloc, hipFree or allocating routine.  The first call on a
+ *    device (with that device current) looks up the array's address there
+ *    (hipGetSymbolAddress) and keeps it; make that first call outside graph
+ *    capture.
+ *  - Every call on one GPU shares that GPU's array and leaves its contents
+ *    behind; nothing in it needs to start at zero (the kernels clear what
+ *    they count).  Calls that overlap on one GPU (different streams, or
+ *    threads racing on one stream) race on the array: serialise them.
+ */
+moe_status moe_forward_noalloc(const moe_config *cfg, const moe_weights *w, const void *x,
+                               void *y, moe_stats *stats, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Training: forward that keeps what the backward needs, and the backward.

@@ -20,7 +20,7 @@ __all__ = [
     "moe_weights", "moe_stats", "config", "library", "moe_workspace_bytes", "moe_route",
     "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_status_string",
     "workspace", "LIB_PATH", "moe_grads", "moe_train_workspace_bytes", "moe_forward_train",
-    "moe_backward", "train_workspace",
+    "moe_backward", "train_workspace", "moe_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.so")
@@ -29,7 +29,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_GELU, MOE_ACT_RELU = 0, 1
 MOE_ROUTE_TOKEN, MOE_ROUTE_EXPERT = 0, 1
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
-           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
+           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_SCRATCH"}
+MOE_NOALLOC_SCRATCH_BYTES = 128 << 20  # include/moe.h
 
 
 class MoeError(RuntimeError):
@@ -86,10 +87,12 @@ def library() -> C.CDLL:
         lib.moe_train_workspace_bytes.argtypes = [CP]
         lib.moe_train_workspace_bytes.restype = S
         lib.moe_forward_train.argtypes = lib.moe_forward.argtypes
+        lib.moe_forward_noalloc.argtypes = [CP, C.POINTER(moe_weights), P, P,
+                                            C.POINTER(moe_stats), P]
         lib.moe_backward.argtypes = [CP, C.POINTER(moe_weights), P, P, C.c_float,
                                      C.POINTER(moe_grads), P, S, P]
         for f in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
-                  "moe_forward_train", "moe_backward"):
+                  "moe_forward_train", "moe_backward", "moe_forward_noalloc"):
             getattr(lib, f).restype = C.c_int
         lib.moe_status_string.argtypes = [C.c_int]
         lib.moe_status_string.restype = C.c_char_p
@@ -193,6 +196,17 @@ def moe_forward(cfg, weights: dict, x, y, stats: Optional[dict] = None, ws=None,
                        "ec_idx", "ec_w")])
     _check("moe_forward", library().moe_forward(
         C.byref(cfg), C.byref(w), _ptr(x), _ptr(y), C.byref(st), wp, wn, _stream(stream)))
+
+
+def moe_forward_noalloc(cfg, weights: dict, x, y, stats: Optional[dict] = None, stream=None):
+    """moe_forward with the library's static per-GPU scratch as workspace (no
+    device allocation by the library or here)."""
+    w = _weights(weights)
+    st = moe_stats(*[_ptr((stats or {}).get(n)) for n in
+                      ("topk_idx", "topk_w", "counts", "kept", "mean_prob", "balance", "cv2",
+                       "ec_idx", "ec_w")])
+    _check("moe_forward_noalloc", library().moe_forward_noalloc(
+        C.byref(cfg), C.byref(w), _ptr(x), _ptr(y), C.byref(st), _stream(stream)))
 
 
 def moe_train_workspace_bytes(cfg: moe_config) -> int:

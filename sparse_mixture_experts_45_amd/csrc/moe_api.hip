@@ -3,10 +3,17 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "kernels.h"
 
 using namespace moe;
+
+// Workspace of moe_forward_noalloc: one static array per GPU, held until the
+// process ends.  In host code its name is only a stand-in for the device
+// array: the address on each device comes from hipGetSymbolAddress, looked up
+// once per device (with it current) and kept below.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -24,6 +31,23 @@ struct Layout {
   int64_t wg_chunk, Rp;
   size_t Z, probs, dg, dl, aux_dp, wg_part, poff, ZT, HT, XT, DT, bsum;
 };
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+moe_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return MOE_OK;
+}
 
 bool expert_choice(const moe_config* c) { return c->routing == MOE_ROUTE_EXPERT; }
 
@@ -668,6 +692,17 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   return s;
 }
 
+moe_status moe_forward_noalloc(const moe_config* cfg, const moe_weights* w, const void* x,
+                               void* y, moe_stats* stats, void* stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  const size_t need = layout(cfg).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((s = noalloc_scratch(&ws)) != MOE_OK) return s;
+  return moe_forward(cfg, w, x, y, stats, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 const char* moe_status_string(moe_status s) {
   switch (s) {
     case MOE_OK: return "ok";
@@ -675,6 +710,9 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
     case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH:
+      return "moe_forward_noalloc: the layer needs more workspace than its static scratch "
+             "(MOE_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

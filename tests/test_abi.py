@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4):
+    for s in (0, -1, -2, -3, -4, -5):
         assert moe.moe_status_string(s)
     assert moe.moe_status_string(0) == "ok"
 
@@ -163,3 +163,14 @@ def test_training_entry_points_check_arguments(lib):
                             fake, n - 1, None) == -3
     assert lib.moe_forward_train(C.byref(c), C.byref(w), fake, fake, None, fake,
                                  lib.moe_workspace_bytes(C.byref(c)), None) == -3
+
+
+def test_noalloc_checks_before_touching_a_device(lib):
+    """moe_forward_noalloc rejects an invalid config, and a layer whose workspace
+    exceeds its static scratch, on the host, before any HIP call."""
+    bad = cfg(top_k=9)
+    assert lib.moe_forward_noalloc(C.byref(bad), None, None, None, None, None) == -1
+    big = moe.config(4096, 4096, 14336, 8, 2)
+    assert moe.moe_workspace_bytes(big) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(C.byref(big), None, None, None, None, None) == -5
+    assert "scratch" in moe.moe_status_string(-5)
