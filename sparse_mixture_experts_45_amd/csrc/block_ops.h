@@ -32,10 +32,12 @@ __device__ inline int block_excl_scan(int v, int32_t* wsum, int& total) {
 
 // Group g (expert g, or the shared expert as group E) owns rows
 // off[g] .. off[g+1] and is cut into ceil(rows / BM) tiles of at most BM rows;
-// tiles are listed group by group, row-ascending.  `off` may sit in global
-// memory or LDS.  ntiles[0] gets the tile count, ntiles[1 .. kSplitSlots]
-// (the grouped GEMM's split counters) zero.
-__device__ inline void build_tile_list(const int32_t* off, int G, int BM,
+// with extra > 0, a group whose last tile would hold at most `extra` rows
+// merges them into its previous tile instead (that tile then holds up to
+// BM + extra rows).  Tiles are listed group by group, row-ascending.  `off`
+// may sit in global memory or LDS.  ntiles[0] gets the tile count,
+// ntiles[1 .. kSplitSlots] (the grouped GEMM's split counters) zero.
+__device__ inline void build_tile_list(const int32_t* off, int G, int BM, int extra,
                                        RowTile* __restrict__ tiles, int32_t* __restrict__ ntiles,
                                        int32_t* wsum) {
   const int g = threadIdx.x;
@@ -43,6 +45,7 @@ __device__ inline void build_tile_list(const int32_t* off, int G, int BM,
   if (g < G) {
     rows = off[g + 1] - off[g];
     m = (rows + BM - 1) / BM;
+    if (extra > 0 && m >= 2 && rows - (m - 1) * BM <= extra) --m;
   }
   int total;
   const int start = block_excl_scan(m, wsum, total);
@@ -52,7 +55,7 @@ __device__ inline void build_tile_list(const int32_t* off, int G, int BM,
       RowTile t;
       t.group = g;
       t.row0 = r0 + j * BM;
-      t.rows = min(BM, rows - j * BM);
+      t.rows = j + 1 < m ? BM : rows - j * BM;
       t.first = start;
       t.count = m;
       t.pad0 = t.pad1 = t.pad2 = 0;

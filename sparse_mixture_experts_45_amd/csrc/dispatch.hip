@@ -400,7 +400,7 @@ __global__ __launch_bounds__(1024) void dispatch_blocks_kernel(DispatchArgs a) {
       a.offsets[E + 1] = soff[E + 1];
     }
     if (a.cv2) counts_cv2(cnt, E, a.cv2, wsd);
-    build_tile_list(soff, E + (a.shared ? 1 : 0), a.BM, a.tiles, a.ntiles, wsum);
+    build_tile_list(soff, E + (a.shared ? 1 : 0), a.BM, a.extra, a.tiles, a.ntiles, wsum);
   }
   if (!scatter) return;
   int nbits = 1;

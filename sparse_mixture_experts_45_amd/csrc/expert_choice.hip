@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kMaxExperts) void ec_finish_kernel(EcArgs a) {
     a.offsets[E + 1] = end;
   }
   __syncthreads();
-  build_tile_list(soff, E + (a.shared ? 1 : 0), a.BM, a.tiles, a.ntiles, wsum);
+  build_tile_list(soff, E + (a.shared ? 1 : 0), a.BM, a.extra, a.tiles, a.ntiles, wsum);
   if (a.shared)
     for (int64_t t = tid; t < a.T; t += kMaxExperts) {
       a.row_token[routed + t] = static_cast<int32_t>(t);

@@ -125,19 +125,34 @@ __device__ __forceinline__ void split_plan(int total, int slots, int smax, int* 
   *S = s;
 }
 
-// XCD i % 8 runs the blocks with id i: block ids are remapped so each XCD walks
-// a contiguous range of [0, total).
+// XCD i % 8 runs the blocks with id i (in id order); block ids are remapped so
+// each XCD walks tiles of [0, total) that share weight columns and token rows
+// in its L2.  Contiguous (CHUNKED false): each XCD walks one contiguous range.
+// CHUNKED: each XCD walks chunks of kChunk consecutive tiles, chunk c on XCD
+// c % 8; the tiles an XCD runs at once (one per CU) come from one chunk, and
+// every XCD draws chunks from the whole list, so a group whose tiles cost more
+// (heavy tiles) is not left to one XCD.  A last partial round of chunks is cut
+// into one contiguous range per XCD.
+constexpr int kChunk = 32;
+template <bool CHUNKED>
 __device__ __forceinline__ int xcd_order(int pid, int total) {
-  const int q = total / kXcd, r = total % kXcd;
-  const int x = pid % kXcd, local = pid / kXcd;
-  return x * q + min(x, r) + local;  // bijection onto [0, total)
+  const int full = CHUNKED ? total / (kXcd * kChunk) * (kXcd * kChunk) : 0;
+  if (pid < full) {
+    const int x = pid % kXcd, local = pid / kXcd;
+    return (local / kChunk * kXcd + x) * kChunk + local % kChunk;  // bijection onto [0, full)
+  }
+  const int rest = total - full, p = pid - full;
+  const int q = rest / kXcd, r = rest % kXcd;
+  const int x = p % kXcd, local = p / kXcd;
+  return full + x * q + min(x, r) + local;  // bijection onto [full, total)
 }
 
 // Tile id -> (row tile, n tile), each XCD on a contiguous range of the tile list.
+template <bool CHUNKED = false>
 __device__ __forceinline__ void decode_tile(const GemmArgs& a, int pid, int total, int* rt,
                                             int* nt) {
   const int NT = a.n_tiles_n;
-  const int v = xcd_order(pid, total);
+  const int v = xcd_order<CHUNKED>(pid, total);
   const RowTile& t = a.tiles[v / NT];
   const int m = t.count;
   const int ve = v - t.first * NT;           // index inside the group
@@ -409,8 +424,14 @@ __device__ __forceinline__ void sched_steps() {
 // next tile (its token rows, its gates) is already loaded; after the K loop
 // the next tile's first stages are issued before tile t's epilogue runs, so
 // load latency hides under the epilogue instead of idling the CU.
+//
+// Heavy tiles (XR = 1): a row tile may hold up to BM + 32 WM rows, the rows
+// past BM forming one more 32-row block per wave row (rows BM + 32 wm ..).
+// The tile list merges an expert's last few rows (at most 32 WM) into its
+// previous tile instead of giving them a tile of their own; tiles of at most
+// BM rows skip the extra block's loads and MFMAs.
 template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int MODE,
-          bool BT>
+          bool BT, int XR = 0>
 __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(GemmArgs a) {
   using MD = ModeOf<MODE>;
   // BT: the group's B is stored [K, N] (row k holds N contiguous values), as
@@ -422,20 +443,28 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
   constexpr int NT = NW * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MI = WTM / 32, NI = WTN / 32;
+  constexpr int BMX = BM + XR * WM * 32;   // A rows a tile can hold
+  constexpr int MIX = MI + XR;             // row blocks per wave, the extra one included
   constexpr int RB = BK * 2;               // bytes per LDS tile row
   constexpr int CPR = BK / 8;              // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;            // rows per wave instruction
-  constexpr int ROWS = BM + BN;            // A rows then B rows
+  constexpr int ROWS = BMX + BN;           // A rows then B rows
   constexpr int JPW = ROWS / RPI / NW;     // load instructions per wave per stage
   constexpr int STAGE = ROWS * RB;         // bytes
   constexpr int KS = BK / 16;              // k16 MFMA steps per stage
-  constexpr int GPT = (BM + NT - 1) / NT;  // gates per thread
+  constexpr int GPT = (BMX + NT - 1) / NT;  // gates per thread
   static_assert(ROWS % (RPI * NW) == 0 && MI >= 1 && NI >= 1, "tile shape");
+  // the extra rows take whole load instructions; heavy tiles skip none of them
+  // and lighter ones skip all, which the vmcnt waits of a 2-stage ring (all
+  // vmcnt(0)) do not count
+  static_assert(XR == 0 || (NS == 2 && (XR * WM * 32) % (RPI * NW) == 0 && !BT &&
+                            MODE != kWgrad && !PERSIST),
+                "heavy tiles: 2-stage ring, forward modes, one tile per block");
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(NS >= 2 && JPW * (NS - 2) < 64, "stages");
 
   extern __shared__ __align__(16) char smem[];
-  __shared__ float gate_s[2][BM];
+  __shared__ float gate_s[2][BMX];
   __shared__ int split_last;
 
   const int total = MODE == kWgrad ? a.E * a.tiles_m * a.n_tiles_n : *a.ntiles * a.n_tiles_n;
@@ -452,12 +481,14 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane / CPR;  // row inside a load instruction's rows
-  int aoffs[MI], boffs[NI];
+  int aoffs[MIX], boffs[NI];
   const int lrow = lane & 31;
+  // A row of row block i of this wave (the extra block: BM + 32 wm ..)
+  auto arow_blk = [&](int i) { return i < MI ? wm * WTM + i * 32 : BM + wm * 32; };
 #pragma unroll
-  for (int i = 0; i < MI; ++i) aoffs[i] = (wm * WTM + i * 32 + lrow) * RB;
+  for (int i = 0; i < MIX; ++i) aoffs[i] = (arow_blk(i) + lrow) * RB;
 #pragma unroll
-  for (int j = 0; j < NI; ++j) boffs[j] = (BM + wn * WTN + j * 32 + lrow) * RB;
+  for (int j = 0; j < NI; ++j) boffs[j] = (BMX + wn * WTN + j * 32 + lrow) * RB;
   const int rsw = swz<CPR>(lrow);  // the same for every fragment row of this lane
   // BT fragment reads: lane l takes rows 8 (l / 32) + (l % 16) / 4 (+ 4 for the
   // second read) and 4 columns from 16 ((l / 16) % 2) + 4 (l % 4) of its
@@ -468,7 +499,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int col = wn * WTN + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      btoffs[j] = BM * RB + trow * (BN * 2) + (((col >> 3) ^ swzt(trow)) << 4) + (col & 7) * 2;
+      btoffs[j] = BMX * RB + trow * (BN * 2) + (((col >> 3) ^ swzt(trow)) << 4) + (col & 7) * 2;
     }
   }
 
@@ -488,7 +519,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     if constexpr (MODE == kWgrad) {
       // group-major, row tiles fastest: neighbouring blocks share B's column tile
       const int per = a.tiles_m * a.n_tiles_n;
-      const int v = xcd_order(tt, total);
+      const int v = xcd_order<false>(tt, total);
       const int g = v / per, rr = v - g * per;
       const int nt = rr / a.tiles_m, mt = rr - nt * a.tiles_m;
       const int k0 = __builtin_amdgcn_readfirstlane(a.poff[a.g0 + g]);
@@ -506,7 +537,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
       return c;
     }
     int rt, nt;
-    decode_tile(a, tt, total, &rt, &nt);
+    decode_tile<(XR > 0)>(a, tt, total, &rt, &nt);  // heavy tiles: chunks across XCDs
     rt = __builtin_amdgcn_readfirstlane(rt);
     nt = __builtin_amdgcn_readfirstlane(nt);
     const RowTile& rtile = a.tiles[rt];
@@ -534,9 +565,11 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     return MD::gather ? a.row_token[c.row0 + rr] : rr;
   };
   // Load instruction j of this wave fills tile rows (wave + j NW) RPI ...; the
-  // first JA instructions hold A rows, the rest B rows.  Sources are kept as
-  // 32-bit byte offsets from the tensor (A) or the group's weights (B).
-  constexpr int JA = BM / (RPI * NW);
+  // first JA instructions hold A rows (the last JX of them the extra rows of
+  // heavy tiles), the rest B rows.  Sources are kept as 32-bit byte offsets
+  // from the tensor (A) or the group's weights (B).
+  constexpr int JA = BMX / (RPI * NW);
+  constexpr int JX = (BMX - BM) / (RPI * NW);
   static_assert(BM % (RPI * NW) == 0, "A rows per load instruction");
   auto a_off = [&](int j, int arow) -> uint32_t {
     const int r = (wave + j * NW) * RPI + lr;
@@ -547,14 +580,14 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
     if constexpr (BT) {
       // this lane's 16 bytes of the B region: row kr, chunk position pos, which
       // holds global chunk pos ^ swzt(kr) (clamped to a valid column chunk)
-      const int o = ((wave + j * NW) * RPI - BM) * RB + lane * 16;
+      const int o = ((wave + j * NW) * RPI - BMX) * RB + lane * 16;
       const int kr = o / (BN * 2), pos = (o % (BN * 2)) >> 4;
       const int nn = min(c.n0 + ((pos ^ swzt(kr)) << 3), c.N - 8);
       return static_cast<uint32_t>(kr) * static_cast<uint32_t>(c.N * 2) + nn * 2;
     } else {
       const int r = (wave + j * NW) * RPI + lr;
       const int chunk = (lane % CPR) ^ swz<CPR>(r);
-      const int nn = min(c.n0 + r - BM, c.N - 1);
+      const int nn = min(c.n0 + r - BMX, c.N - 1);
       return static_cast<uint32_t>(nn) * static_cast<uint32_t>(c.ldb * 2) + chunk * 16;
     }
   };
@@ -570,7 +603,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
   if constexpr (MD::gated) {
 #pragma unroll
     for (int g = 0; g < GPT; ++g)
-      if (tid + g * NT < BM) gate_s[0][tid + g * NT] = gate_of(cur, tid + g * NT);
+      if (tid + g * NT < BMX) gate_s[0][tid + g * NT] = gate_of(cur, tid + g * NT);
   }
   const char* abase = static_cast<const char*>(a.A) + cur.aoff;
   const char* bbase = reinterpret_cast<const char*>(cur.bw);
@@ -582,12 +615,14 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
   }
   // bytes per k of B: 2 (K-contiguous rows) or one [K, N] row
   uint32_t bstep = BT ? static_cast<uint32_t>(cur.N) * 2 : 2;
+  bool heavy = XR > 0 && cur.rows > BM;
   auto issue = [&](int stage, int k0) {
 #pragma unroll
     for (int j = 0; j < JPW; ++j)
-      lds_dma16((j < JA ? abase : bbase) + src[j] +
-                    static_cast<uint32_t>(k0) * (j < JA ? 2u : bstep),
-                smem + stage * STAGE + (wave + j * NW) * RPI * RB);
+      if (XR == 0 || heavy || j < JA - JX || j >= JA)
+        lds_dma16((j < JA ? abase : bbase) + src[j] +
+                      static_cast<uint32_t>(k0) * (j < JA ? 2u : bstep),
+                  smem + stage * STAGE + (wave + j * NW) * RPI * RB);
   };
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
@@ -606,268 +641,289 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
 #pragma unroll
     for (int g = 0; g < GPT; ++g) ngate[g] = 0.f;
 
-    f32x16 acc[MI][NI];
+    // The tile's K loop, K split and epilogue over MU row blocks per wave (MI,
+    // or MIX for a heavy tile; each path keeps only its own accumulators).
+    // Returns true when this block is done (a part of a split tile that did
+    // not arrive last).
+    auto body = [&](auto mu) -> bool {
+      constexpr int MU = decltype(mu)::value;
+      f32x16 acc[MU][NI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-    const int KT = ksteps;
-    for (int kt = 0; kt < KT; ++kt) {
-      // this lane's loads of stage kt have landed once at most the loads of the
-      // later stages already issued (min(NS - 2, KT - 1 - kt) of them) are
-      // pending; the first step of a tile waits for everything (the previous
-      // tile's epilogue stores were issued after this tile's first stages)
-      if (kt == 0) {
-        wait_vmcnt<0>();
-      } else if (kt + NS - 2 < KT) {
-        wait_vmcnt<JPW * (NS - 2)>();
-      } else if constexpr (NS > 2) {
-        if (kt + 1 == KT) wait_vmcnt<0>();
-        else if constexpr (NS > 3) {
-          if (kt + 2 == KT) wait_vmcnt<JPW>();
-          else wait_vmcnt<0>();
-        } else {
-          wait_vmcnt<0>();
-        }
-      }
-      // Every lane's loads of stage kt landed; every wave finished reading stage
-      // kt - 1.  A plain s_barrier: a workgroup fence would also wait for the
-      // later stages.
-      __builtin_amdgcn_s_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      if (kt == 0 && has_next) {
-        // next tile's token rows and gates: loaded now, used after the K loop
-#pragma unroll
-        for (int j = 0; j < JA; ++j) ntok[j] = arow_of(nxt, (wave + j * NW) * RPI + lr);
-        if constexpr (MD::gated) {
-#pragma unroll
-          for (int g = 0; g < GPT; ++g)
-            if (tid + g * NT < BM) ngate[g] = gate_of(nxt, tid + g * NT);
-        }
-      }
-      if (kt + NS - 1 < KT) issue((kt + NS - 1) % NS, (kb + kt + NS - 1) * BK);
-      const char* st = smem + (kt % NS) * STAGE;
-      // fragments of k16 step s + 1 are read while the MFMAs of step s run
-      bf16x8_t fa[2][MI], fb[2][NI];
-      auto frags = [&](int s, int buf) {
-        const int cb = ((2 * s + (lane >> 5)) ^ rsw) * 16;
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-          fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + aoffs[i] + cb);
-        if constexpr (BT) {
-#pragma unroll
-          for (int j = 0; j < NI; ++j) {
-            const char* p = st + btoffs[j] + s * 16 * (BN * 2);
-            const i16x4 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * (BN * 2));
-            fb[buf][j] = __builtin_bit_cast(
-                bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < NI; ++j)
-            fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boffs[j] + cb);
-        }
-      };
-      frags(0, 0);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (s + 1 < KS) frags(s + 1, (s + 1) & 1);
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NI; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
-                                                                acc[i][j], 0, 0, 0);
-      }
-      // Instruction order for the scheduler: the first step's fragment reads,
-      // then each step's MFMAs with the next step's reads spread between them.
-      constexpr int NRD = MI + (BT ? 2 : 1) * NI;  // fragment reads per k16 step
-      __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
-      sched_steps<0, KS - 1, NRD, MI * NI>();
-      __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
-    }
-    // Every wave is done reading this tile's stages (and every load of it has
-    // landed: the last iteration waited for all of them).
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (!PERSIST && part >= 0) {
-      // Park this part's accumulators in its slot, lane-major (one 16-byte
-      // store per lane: 1 KiB per wave instruction).  The last part to arrive
-      // adds the S slots in part order (its own from registers) and goes on to
-      // the epilogue; the others are done.
-      constexpr int F4 = MI * NI * 4;  // float4 per lane
-      const int u = static_cast<int>(blockIdx.x) - D, ti = u / S;
-      float4* mine = reinterpret_cast<float4*>(a.kpart) + static_cast<int64_t>(u) * F4 * NT;
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MU; ++i)
 #pragma unroll
         for (int j = 0; j < NI; ++j)
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            mine[((i * NI + j) * 4 + c) * NT + tid] =
-                make_float4(acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
-                            acc[i][j][4 * c + 3]);
-      // Each wave waits until its stores have reached the L2; the workgroup
-      // barrier (with its workgroup-scope fences) orders every wave's stores
-      // before thread 0's agent-scope release, which writes this XCD's L2 back,
-      // and the arrival count; the last part invalidates its stale L2 lines
-      // (agent-scope acquire) before any wave reads the other parts' slots.
-      // One release per part and one acquire per tile: each is a whole-L2
-      // operation, so no wave beyond the first does either.
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        // the write-back has completed before the arrival is counted (an
-        // explicit wait: the compiler drops its own here, as its counter model
-        // already saw vmcnt at zero)
-        wait_vmcnt<0>();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const int before =
-            __hip_atomic_fetch_add(a.ksem + ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        split_last = before == S - 1;
-        if (before == S - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      }
-      __syncthreads();
-      if (!split_last) return;
-      const float4* slots0 =
-          reinterpret_cast<const float4*>(a.kpart) + static_cast<int64_t>(ti) * S * F4 * NT;
+          for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+      const int KT = ksteps;
+        for (int kt = 0; kt < KT; ++kt) {
+          // this lane's loads of stage kt have landed once at most the loads of the
+          // later stages already issued (min(NS - 2, KT - 1 - kt) of them) are
+          // pending; the first step of a tile waits for everything (the previous
+          // tile's epilogue stores were issued after this tile's first stages)
+          if (kt == 0) {
+            wait_vmcnt<0>();
+          } else if (kt + NS - 2 < KT) {
+            wait_vmcnt<JPW * (NS - 2)>();
+          } else if constexpr (NS > 2) {
+            if (kt + 1 == KT) wait_vmcnt<0>();
+            else if constexpr (NS > 3) {
+              if (kt + 2 == KT) wait_vmcnt<JPW>();
+              else wait_vmcnt<0>();
+            } else {
+              wait_vmcnt<0>();
+            }
+          }
+          // Every lane's loads of stage kt landed; every wave finished reading stage
+          // kt - 1.  A plain s_barrier: a workgroup fence would also wait for the
+          // later stages.
+          __builtin_amdgcn_s_barrier();
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          if (kt == 0 && has_next) {
+            // next tile's token rows and gates: loaded now, used after the K loop
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+            for (int j = 0; j < JA; ++j) ntok[j] = arow_of(nxt, (wave + j * NW) * RPI + lr);
+            if constexpr (MD::gated) {
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          f32x16 sum;
+              for (int g = 0; g < GPT; ++g)
+                if (tid + g * NT < BMX) ngate[g] = gate_of(nxt, tid + g * NT);
+            }
+          }
+          if (kt + NS - 1 < KT) issue((kt + NS - 1) % NS, (kb + kt + NS - 1) * BK);
+          const char* st = smem + (kt % NS) * STAGE;
+          // fragments of k16 step s + 1 are read while the MFMAs of step s run
+          bf16x8_t fa[2][MU], fb[2][NI];
+          auto frags = [&](int s, int buf) {
+            const int cb = ((2 * s + (lane >> 5)) ^ rsw) * 16;
 #pragma unroll
-          for (int q = 0; q < 16; ++q) sum[q] = 0.f;
-          for (int p = 0; p < S; ++p) {
-            if (p == part) {
+            for (int i = 0; i < MU; ++i)
+              fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + aoffs[i] + cb);
+            if constexpr (BT) {
 #pragma unroll
-              for (int q = 0; q < 16; ++q) sum[q] += acc[i][j][q];
+              for (int j = 0; j < NI; ++j) {
+                const char* p = st + btoffs[j] + s * 16 * (BN * 2);
+                const i16x4 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * (BN * 2));
+                fb[buf][j] = __builtin_bit_cast(
+                    bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              }
             } else {
 #pragma unroll
-              for (int c = 0; c < 4; ++c) {
-                const float4 v = slots0[(static_cast<int64_t>(p) * F4 + (i * NI + j) * 4 + c) * NT + tid];
-                sum[4 * c] += v.x;
-                sum[4 * c + 1] += v.y;
-                sum[4 * c + 2] += v.z;
-                sum[4 * c + 3] += v.w;
+              for (int j = 0; j < NI; ++j)
+                fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + boffs[j] + cb);
+            }
+          };
+          frags(0, 0);
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            if (s + 1 < KS) frags(s + 1, (s + 1) & 1);
+#pragma unroll
+            for (int i = 0; i < MU; ++i)
+#pragma unroll
+              for (int j = 0; j < NI; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
+                                                                    acc[i][j], 0, 0, 0);
+          }
+          // Instruction order for the scheduler: the first step's fragment reads,
+          // then each step's MFMAs with the next step's reads spread between them.
+          constexpr int NRD = MU + (BT ? 2 : 1) * NI;  // fragment reads per k16 step
+          __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+          sched_steps<0, KS - 1, NRD, MU * NI>();
+          __builtin_amdgcn_sched_group_barrier(0x008, MU * NI, 0);
+        }
+      // Every wave is done reading this tile's stages (and every load of it has
+      // landed: the last iteration waited for all of them).
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (!PERSIST && part >= 0) {
+        // Park this part's accumulators in its slot, lane-major (one 16-byte
+        // store per lane: 1 KiB per wave instruction).  The last part to arrive
+        // adds the S slots in part order (its own from registers) and goes on to
+        // the epilogue; the others are done.
+        // a slot holds MIX row blocks (heavy or not, the parts of one tile agree)
+        constexpr int F4S = MIX * NI * 4;  // float4 per lane of a slot
+        const int u = static_cast<int>(blockIdx.x) - D, ti = u / S;
+        float4* mine = reinterpret_cast<float4*>(a.kpart) + static_cast<int64_t>(u) * F4S * NT;
+#pragma unroll
+        for (int i = 0; i < MU; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              mine[((i * NI + j) * 4 + c) * NT + tid] =
+                  make_float4(acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
+                              acc[i][j][4 * c + 3]);
+        // Each wave waits until its stores have reached the L2; the workgroup
+        // barrier (with its workgroup-scope fences) orders every wave's stores
+        // before thread 0's agent-scope release, which writes this XCD's L2 back,
+        // and the arrival count; the last part invalidates its stale L2 lines
+        // (agent-scope acquire) before any wave reads the other parts' slots.
+        // One release per part and one acquire per tile: each is a whole-L2
+        // operation, so no wave beyond the first does either.
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (tid == 0) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          // the write-back has completed before the arrival is counted (an
+          // explicit wait: the compiler drops its own here, as its counter model
+          // already saw vmcnt at zero)
+          wait_vmcnt<0>();
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          const int before =
+              __hip_atomic_fetch_add(a.ksem + ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          split_last = before == S - 1;
+          if (before == S - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        __syncthreads();
+        if (!split_last) return true;
+        const float4* slots0 =
+            reinterpret_cast<const float4*>(a.kpart) + static_cast<int64_t>(ti) * S * F4S * NT;
+#pragma unroll
+        for (int i = 0; i < MU; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            f32x16 sum;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) sum[q] = 0.f;
+            for (int p = 0; p < S; ++p) {
+              if (p == part) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) sum[q] += acc[i][j][q];
+              } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                  const float4 v =
+                      slots0[(static_cast<int64_t>(p) * F4S + (i * NI + j) * 4 + c) * NT + tid];
+                  sum[4 * c] += v.x;
+                  sum[4 * c + 1] += v.y;
+                  sum[4 * c + 2] += v.z;
+                  sum[4 * c + 3] += v.w;
+                }
+              }
+            }
+            acc[i][j] = sum;
+          }
+        if (tid == 0) a.ksem[ti] = 0;  // ready for the next launch (kernel end orders it)
+      }
+      if (has_next) {
+#pragma unroll
+        for (int j = 0; j < JPW; ++j) src[j] = j < JA ? a_off(j, ntok[j]) : b_off(nxt, j);
+        abase = static_cast<const char*>(a.A) + nxt.aoff;
+        bbase = reinterpret_cast<const char*>(nxt.bw);
+        bstep = BT ? static_cast<uint32_t>(nxt.N) * 2 : 2;
+        const int KTn = nxt.K / BK;
+#pragma unroll
+        for (int p = 0; p < NS - 1; ++p)
+          if (p < KTn) issue(p, p * BK);
+        if constexpr (MD::gated) {
+#pragma unroll
+          for (int g = 0; g < GPT; ++g)
+            if (tid + g * NT < BMX) gate_s[gb ^ 1][tid + g * NT] = ngate[g];
+        }
+      }
+
+      // epilogue of tile t (gates of this tile are in gate_s[gb]).  Stores address
+      // the tile from one uniform base with 32-bit offsets; a full tile takes the
+      // path without bounds checks; the activation is chosen once per tile.
+      float bv[NI];
+      int ncol[NI];
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        ncol[j] = wn * WTN + j * 32 + (lane & 31);  // column inside the tile
+        const int n = cur.n0 + ncol[j];
+        bv[j] = (cur.bias && n < cur.N) ? bf16_to_f32(cur.bias[n].bits) : 0.f;
+      }
+      constexpr int OE = MD::out_f32 ? 4 : 2;  // output element bytes
+      char* obase = static_cast<char*>(a.out) +
+                    (cur.ooff + static_cast<int64_t>(cur.row0) * a.ldo + cur.n0) * OE;
+      char* xbase = MODE == kUpTrain ? static_cast<char*>(a.aux) +
+                                           (static_cast<int64_t>(cur.row0) * a.ldo + cur.n0) * OE
+                                     : nullptr;
+      const uint32_t ldo = static_cast<uint32_t>(a.ldo);
+      // CHK: some columns of the tile lie past N.  Rows are checked per 32-row
+      // block, only in blocks that reach past the tile's rows.
+      auto epilogue = [&](auto checked, auto relu) {
+        constexpr bool CHK = decltype(checked)::value;
+        constexpr bool RELU = decltype(relu)::value;
+#pragma unroll
+        for (int i = 0; i < MU; ++i) {
+          const bool rchk = arow_blk(i) + 32 > cur.rows;
+#pragma unroll
+         for (int qh = 0; qh < 16; qh += 8) {
+          // kDz: eight rows' pre-activations are loaded before any of their
+          // results is stored (a load after a possibly aliasing store would wait
+          // out a full memory latency)
+          uint16_t zr[MODE == kDz ? 8 : 1][MODE == kDz ? NI : 1];
+          if constexpr (MODE == kDz) {
+#pragma unroll
+            for (int qq = 0; qq < 8; ++qq) {
+              const int q = qh + qq;
+              // partial tiles read a clamped valid element (no branch); the
+              // value is used only where the result is stored
+              const int m = arow_blk(i) + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+              const uint32_t orow = static_cast<uint32_t>(rchk ? min(m, cur.rows - 1) : m) * ldo;
+#pragma unroll
+              for (int j = 0; j < NI; ++j) {
+                const int nc = CHK ? min(ncol[j], cur.N - 1 - cur.n0) : ncol[j];
+                zr[qq][j] = *reinterpret_cast<const uint16_t*>(
+                    obase + (orow + static_cast<uint32_t>(nc)) * OE);
               }
             }
           }
-          acc[i][j] = sum;
-        }
-      if (tid == 0) a.ksem[ti] = 0;  // ready for the next launch (kernel end orders it)
-    }
-    if (has_next) {
 #pragma unroll
-      for (int j = 0; j < JPW; ++j) src[j] = j < JA ? a_off(j, ntok[j]) : b_off(nxt, j);
-      abase = static_cast<const char*>(a.A) + nxt.aoff;
-      bbase = reinterpret_cast<const char*>(nxt.bw);
-      bstep = BT ? static_cast<uint32_t>(nxt.N) * 2 : 2;
-      const int KTn = nxt.K / BK;
-#pragma unroll
-      for (int p = 0; p < NS - 1; ++p)
-        if (p < KTn) issue(p, p * BK);
-      if constexpr (MD::gated) {
-#pragma unroll
-        for (int g = 0; g < GPT; ++g)
-          if (tid + g * NT < BM) gate_s[gb ^ 1][tid + g * NT] = ngate[g];
-      }
-    }
-
-    // epilogue of tile t (gates of this tile are in gate_s[gb]).  Stores address
-    // the tile from one uniform base with 32-bit offsets; a full tile takes the
-    // path without bounds checks; the activation is chosen once per tile.
-    float bv[NI];
-    int ncol[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      ncol[j] = wn * WTN + j * 32 + (lane & 31);  // column inside the tile
-      const int n = cur.n0 + ncol[j];
-      bv[j] = (cur.bias && n < cur.N) ? bf16_to_f32(cur.bias[n].bits) : 0.f;
-    }
-    constexpr int OE = MD::out_f32 ? 4 : 2;  // output element bytes
-    char* obase = static_cast<char*>(a.out) +
-                  (cur.ooff + static_cast<int64_t>(cur.row0) * a.ldo + cur.n0) * OE;
-    char* xbase = MODE == kUpTrain ? static_cast<char*>(a.aux) +
-                                         (static_cast<int64_t>(cur.row0) * a.ldo + cur.n0) * OE
-                                   : nullptr;
-    const uint32_t ldo = static_cast<uint32_t>(a.ldo);
-    auto epilogue = [&](auto checked, auto relu) {
-      constexpr bool CHK = decltype(checked)::value;
-      constexpr bool RELU = decltype(relu)::value;
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-#pragma unroll
-       for (int qh = 0; qh < 16; qh += 8) {
-        // kDz: eight rows' pre-activations are loaded before any of their
-        // results is stored (a load after a possibly aliasing store would wait
-        // out a full memory latency)
-        uint16_t zr[MODE == kDz ? 8 : 1][MODE == kDz ? NI : 1];
-        if constexpr (MODE == kDz) {
-#pragma unroll
-          for (int qq = 0; qq < 8; ++qq) {
-            const int q = qh + qq;
-            // partial tiles read a clamped valid element (no branch); the
-            // value is used only where the result is stored
-            const int m = wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-            const uint32_t orow = static_cast<uint32_t>(CHK ? min(m, cur.rows - 1) : m) * ldo;
+          for (int q = qh; q < qh + 8; ++q) {
+            const int m = arow_blk(i) + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+            if (rchk && m >= cur.rows) continue;
+            const uint32_t orow = static_cast<uint32_t>(m) * ldo;
+            const float g = MD::gated ? gate_s[gb][m] : 1.f;
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
-              const int nc = CHK ? min(ncol[j], cur.N - 1 - cur.n0) : ncol[j];
-              zr[qq][j] = *reinterpret_cast<const uint16_t*>(
-                  obase + (orow + static_cast<uint32_t>(nc)) * OE);
+              if (CHK && cur.n0 + ncol[j] >= cur.N) continue;
+              const float z = acc[i][j][q] + bv[j];
+              const uint32_t off = (orow + static_cast<uint32_t>(ncol[j])) * OE;
+              if constexpr (MD::fwd_act) {
+                const float h = RELU ? fmaxf(z, 0.f) : gelu_erf(z);
+                *reinterpret_cast<uint16_t*>(obase + off) = f32_to_bf16(h);
+                if constexpr (MODE == kUpTrain)
+                  *reinterpret_cast<uint16_t*>(xbase + off) = f32_to_bf16(z);
+              } else if constexpr (MODE == kDz) {
+                const float pre = bf16_to_f32(zr[q - qh][j]);
+                const float da = RELU ? (pre > 0.f ? 1.f : 0.f) : gelu_erf_grad(pre);
+                *reinterpret_cast<uint16_t*>(obase + off) = f32_to_bf16(g * z * da);
+              } else if constexpr (MODE == kWgrad) {
+                *reinterpret_cast<uint16_t*>(obase + off) = f32_to_bf16(z);
+              } else {
+                *reinterpret_cast<float*>(obase + off) = g * z;
+              }
             }
           }
+         }
+          // one 32-row block at a time: keeps the epilogue's temporaries few
+          __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int q = qh; q < qh + 8; ++q) {
-          const int m = wm * WTM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-          if (CHK && m >= cur.rows) continue;
-          const uint32_t orow = static_cast<uint32_t>(m) * ldo;
-          const float g = MD::gated ? gate_s[gb][m] : 1.f;
-#pragma unroll
-          for (int j = 0; j < NI; ++j) {
-            if (CHK && cur.n0 + ncol[j] >= cur.N) continue;
-            const float z = acc[i][j][q] + bv[j];
-            const uint32_t off = (orow + static_cast<uint32_t>(ncol[j])) * OE;
-            if constexpr (MD::fwd_act) {
-              const float h = RELU ? fmaxf(z, 0.f) : gelu_erf(z);
-              *reinterpret_cast<uint16_t*>(obase + off) = f32_to_bf16(h);
-              if constexpr (MODE == kUpTrain)
-                *reinterpret_cast<uint16_t*>(xbase + off) = f32_to_bf16(z);
-            } else if constexpr (MODE == kDz) {
-              const float pre = bf16_to_f32(zr[q - qh][j]);
-              const float da = RELU ? (pre > 0.f ? 1.f : 0.f) : gelu_erf_grad(pre);
-              *reinterpret_cast<uint16_t*>(obase + off) = f32_to_bf16(g * z * da);
-            } else if constexpr (MODE == kWgrad) {
-              *reinterpret_cast<uint16_t*>(obase + off) = f32_to_bf16(z);
-            } else {
-              *reinterpret_cast<float*>(obase + off) = g * z;
-            }
-          }
-        }
-       }
-        // one 32-row block at a time: keeps the epilogue's temporaries few
-        __builtin_amdgcn_sched_barrier(0);
+      };
+      // A tile whose columns all lie past its group's N (the shared expert's
+      // narrower projection) stores nothing; the clamps of the partial-tile
+      // path assume at least one valid column.
+      const bool full = cur.n0 + BN <= cur.N;  // every column of the tile is stored
+      if (cur.n0 >= cur.N) {
+      } else if ((MD::fwd_act || MODE == kDz) && a.act == MOE_ACT_RELU) {
+        if (full) epilogue(std::false_type{}, std::true_type{});
+        else epilogue(std::true_type{}, std::true_type{});
+      } else {
+        if (full) epilogue(std::false_type{}, std::false_type{});
+        else epilogue(std::true_type{}, std::false_type{});
       }
+      return false;
     };
-    // A tile whose columns all lie past its group's N (the shared expert's
-    // narrower projection) stores nothing; the clamps of the partial-tile
-    // path assume at least one valid column.
-    const bool full = cur.rows == BM && cur.n0 + BN <= cur.N;
-    if (cur.n0 >= cur.N) {
-    } else if ((MD::fwd_act || MODE == kDz) && a.act == MOE_ACT_RELU) {
-      if (full) epilogue(std::false_type{}, std::true_type{});
-      else epilogue(std::true_type{}, std::true_type{});
+    bool done;
+    if constexpr (XR > 0) {
+      done = heavy ? body(std::integral_constant<int, MIX>{})
+                   : body(std::integral_constant<int, MI>{});
     } else {
-      if (full) epilogue(std::false_type{}, std::false_type{});
-      else epilogue(std::true_type{}, std::false_type{});
+      done = body(std::integral_constant<int, MI>{});
     }
+    if (done) return;
     if (!has_next) break;
     cur = nxt;
     t = tn;
@@ -880,7 +936,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
 // and each row's gate: topk_w[token, slot] (k > 0) or topk_w[row] (k = 0,
 // one gate per routed row); 1 for the shared expert's rows.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
-                                                           int G, int BM, int E, int k,
+                                                           int G, int BM, int extra, int E, int k,
                                                            const int32_t* __restrict__ row_token,
                                                            const int32_t* __restrict__ row_slot,
                                                            const float* __restrict__ topk_w,
@@ -890,7 +946,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   // block 0 builds the tile list; every block fills the gates of its
   // kMaxExperts rows (the grid covers the host's bound on the row count)
   __shared__ int32_t wsum[kMaxExperts / 64];
-  if (blockIdx.x == 0) build_tile_list(offsets, G, BM, tiles, ntiles, wsum);
+  if (blockIdx.x == 0) build_tile_list(offsets, G, BM, extra, tiles, ntiles, wsum);
   const int routed = offsets[E], nrows = offsets[G];
   const int r = static_cast<int>(blockIdx.x) * kMaxExperts + static_cast<int>(threadIdx.x);
   if (r < nrows)
@@ -975,11 +1031,11 @@ static int cu_count() {
 // count; otherwise one block per tile, plus up to `slots` more for the K split
 // of a last round (split: partial tiles reserved, 0 for none).
 template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int MODE,
-          bool BT>
+          bool BT, int XR = 0>
 static void launch_dma(GemmArgs g, int64_t tiles, int split, hipStream_t st) {
   if (tiles <= 0) return;
-  auto kern = grouped_gemm_dma_kernel<BM, BN, BK, NS, WM, WN, OCC, PERSIST, MODE, BT>;
-  const size_t lds = static_cast<size_t>(NS) * (BM + BN) * BK * 2;
+  auto kern = grouped_gemm_dma_kernel<BM, BN, BK, NS, WM, WN, OCC, PERSIST, MODE, BT, XR>;
+  const size_t lds = static_cast<size_t>(NS) * (BM + XR * WM * 32 + BN) * BK * 2;
   static int per_cu = [&] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -1004,13 +1060,13 @@ static void launch_dma(GemmArgs g, int64_t tiles, int split, hipStream_t st) {
 }
 
 template <int BM, int BNU, int BND, int BK, int NS, int WM, int WN, int OCC, int PERSIST,
-          int WMD, int WND, int SPLIT, int M1, bool BT>
+          int WMD, int WND, int SPLIT, int M1, bool BT, int XR = 0>
 static void run_dma(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const GemmArgs u = up_args(f, BNU);
-  launch_dma<BM, BNU, BK, NS, WM, WN, OCC, PERSIST, M1, BT>(u, gp.tiles_max * u.n_tiles_n, SPLIT,
-                                                            st);
+  launch_dma<BM, BNU, BK, NS, WM, WN, OCC, PERSIST, M1, BT, XR>(u, gp.tiles_max * u.n_tiles_n,
+                                                                SPLIT, st);
   const GemmArgs dn = down_args(f, BND);
-  launch_dma<BM, BND, BK, NS, WMD, WND, OCC, PERSIST, kDown, BT>(
+  launch_dma<BM, BND, BK, NS, WMD, WND, OCC, PERSIST, kDown, BT, XR>(
       dn, gp.tiles_max * dn.n_tiles_n, SPLIT, st);
 }
 
@@ -1026,7 +1082,19 @@ static void run_pass(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
 #define MOE_RUN_DMA(C)                                                                     \
   run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN, C.OCC, C.PERSIST, C.WMD, C.WND, C.SPLIT, \
           M1, BT>(gp, f, st)
-    case kGemmDmaLarge: MOE_RUN_DMA(kDmaLarge); break;
+    case kGemmDmaLarge:
+      // the forward's tile list may hold heavy tiles (rows past BM)
+      if constexpr (M1 == kUp && !BT) {
+        constexpr DmaCfg C = kDmaLarge;
+        static_assert(C.WM == C.WMD && C.NS == 2 && !C.PERSIST, "heavy tiles");
+        if (gp.extra > 0) {
+          run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN, C.OCC, C.PERSIST, C.WMD, C.WND,
+                  C.SPLIT, M1, BT, 1>(gp, f, st);
+          break;
+        }
+      }
+      MOE_RUN_DMA(kDmaLarge);
+      break;
     case kGemmDmaTall: MOE_RUN_DMA(kDmaTall); break;
     case kGemmDmaMid: MOE_RUN_DMA(kDmaMid); break;
     case kGemmDmaSmall: MOE_RUN_DMA(kDmaSmall); break;
@@ -1088,7 +1156,8 @@ hipError_t launch_ffn(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   if (!f.tiles_ready)
     build_tiles_kernel<<<static_cast<unsigned>(std::max<int64_t>(1, ceil_div(f.rows_max,
                                                                               kMaxExperts))),
-                         kMaxExperts, 0, st>>>(f.offsets, G, gp.BM, f.E,
+                         kMaxExperts, 0, st>>>(f.offsets, G, gp.BM,
+                                                  f.pass == kPassForward ? gp.extra : 0, f.E,
                                                   f.row_gates ? 0 : f.k, f.row_token,
                                                   f.row_slot, f.topk_w, f.tiles, f.ntiles,
                                                   f.row_gate);

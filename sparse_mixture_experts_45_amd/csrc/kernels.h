@@ -66,6 +66,8 @@ static_assert(kDmaLarge.SPLIT <= kSplitSlots && kDmaMid.SPLIT <= kSplitSlots &&
 struct GemmPlan {
   int shape;        // GemmShape
   int BM;             // rows per tile (the row-tile list is cut at BM)
+  int extra;          // rows past BM a group's last tile may take instead of a tile of
+                      // their own (heavy tiles of the forward's 256-row tier), or 0
   int64_t tiles_max;  // upper bound on row tiles over all groups
   int64_t kpart_floats;  // fp32 partial tiles of the K split (0: no split)
 };
@@ -108,7 +110,7 @@ struct DispatchArgs {
   const int32_t* hist;      // [nb, E] pairs per 64-token block and expert
   const double* stat_part;  // [nb, E] per-block sums of router probabilities
   int64_t T;
-  int nb, E, k, capacity, shared, BM;
+  int nb, E, k, capacity, shared, BM, extra;
   int32_t *counts, *kept, *offsets, *row_token, *row_slot, *inv;
   float* row_gate;
   RowTile* tiles;
@@ -138,7 +140,7 @@ hipError_t launch_dispatch_blocks(const DispatchArgs& a, hipStream_t st);
 // Everything the expert-choice selection and its finishing block read and write.
 struct EcArgs {
   int64_t T;
-  int E, Ce, W, shared, BM, nb;  // Ce tokens per expert; W = ceil(T / 32) bitmap words
+  int E, Ce, W, shared, BM, extra, nb;  // Ce tokens per expert; W = ceil(T / 32) bitmap words
   int32_t *row_token, *offsets, *counts, *kept;  // counts, kept optional
   float* row_gate;
   uint32_t* sel;   // [E, W] selection bitmap

@@ -194,6 +194,14 @@ Layout layout(const moe_config* c, bool train = false) {
   L.train = train;
   L.rp = route_plan(c);
   L.gp = gemm_plan(c);
+  if (!train && L.gp.shape == kGemmDmaLarge) {
+    // the forward's 256-row tiles take up to one more 32-row block per wave
+    // row: a group's last rows, when they are that few, join its previous
+    // tile; the K split's partial tiles grow by those rows
+    L.gp.extra = kDmaLarge.WM * 32;
+    L.gp.kpart_floats = int64_t(kDmaLarge.SPLIT) * (kDmaLarge.BM + L.gp.extra) *
+                        std::max(kDmaLarge.BNU, kDmaLarge.BND);
+  }
   const int64_t T = c->T, E = c->n_experts, k = L.rp.k;
   const bool ec = expert_choice(c);
   L.ec_C = ec ? ec_capacity(c) : 0;
@@ -340,6 +348,7 @@ moe_status forward_expert_choice(const moe_config* c, const Layout& L, const moe
   a.W = L.ec_W;
   a.shared = c->shared_d_ff > 0;
   a.BM = L.gp.BM;
+  a.extra = L.gp.extra;
   a.nb = L.rp.nb;
   a.row_token = reinterpret_cast<int32_t*>(at(ws, L.row_token));
   a.offsets = reinterpret_cast<int32_t*>(at(ws, L.offsets));
@@ -419,6 +428,7 @@ moe_status forward_token(const moe_config* cfg, const Layout& L, const moe_weigh
     d.capacity = cfg->capacity;
     d.shared = cfg->shared_d_ff > 0;
     d.BM = L.gp.BM;
+    d.extra = L.gp.extra;
     d.counts = counts;
     d.kept = kept;
     d.offsets = offsets;

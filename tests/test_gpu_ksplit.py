@@ -58,11 +58,24 @@ def split_plan(total, slots, smax):
     return s if s >= 2 else 1
 
 
-def planned_splits(shape, kept):
+HEAVY_ROWS = 64  # the forward's 256-row tiles take a group's last <= 64 rows
+
+
+def row_tiles(rows, BM, extra):
+    """Row tiles of one group: ceil(rows / BM), less one when the last would hold
+    at most `extra` rows (they join the previous tile)."""
+    m = -(-int(rows) // BM)
+    return m - 1 if extra and m >= 2 and rows - (m - 1) * BM <= extra else m
+
+
+def planned_splits(shape, kept, forward=True):
     """S of the up- and the down-projection launch, from the kept rows per expert."""
-    BM, BN, per_cu = TIERS[tier_of(shape)]
+    tier = tier_of(shape)
+    BM, BN, per_cu = TIERS[tier]
+    extra = HEAVY_ROWS if forward and tier == "large" else 0
     slots = torch.cuda.get_device_properties(0).multi_processor_count * per_cu
-    rt = sum(-(-int(r) // BM) for r in kept) + (-(-shape.T // BM) if shape.Fs else 0)
+    rt = sum(row_tiles(r, BM, extra) for r in kept) + (row_tiles(shape.T, BM, extra)
+                                                       if shape.Fs else 0)
     out = []
     for N, K, Ks in ((max(shape.F, shape.Fs), shape.d, shape.d), (shape.d, shape.F, shape.Fs)):
         kt = (min(K, Ks) if shape.Fs else K) // BK
@@ -83,6 +96,11 @@ CASES = [
     (L("large_up2", T=768, d=4096, F=512, E=2, k=2), (2, 1)),
     (L("large_down4_shared", T=768, d=256, F=8192, E=2, k=2, Fs=8192), (1, 4)),
     (L("large_ec_up2", T=1024, d=4096, F=512, E=4, k=1, routing="expert"), (2, 1)),
+    # 800 rows per expert (k = E): 3 x 256 + 32, so each expert's last tile is
+    # a heavy one of 288 rows, and it is split along K (up-projection; then the
+    # down-projection with a heavy shared-expert tile too)
+    (L("large_up2_heavy", T=800, d=4096, F=512, E=2, k=2), (2, 1)),
+    (L("large_down4_heavy_shared", T=800, d=256, F=8192, E=2, k=2, Fs=8192), (1, 4)),
 ]
 
 
@@ -138,7 +156,7 @@ def test_split_forward_tall(shape, splits):
     assert torch.equal(g["y_raw"].view(torch.int16), g2["y_raw"].view(torch.int16))
 
 
-BWD = CASES[:4] + TALL
+BWD = CASES[:4] + TALL  # the training forward uses no heavy tiles
 
 
 @pytest.mark.parametrize("shape,splits", BWD, ids=[c[0].name for c in BWD])
