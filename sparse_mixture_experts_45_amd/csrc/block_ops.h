@@ -33,22 +33,29 @@ __device__ inline int block_excl_scan(int v, int32_t* wsum, int& total) {
 // Group g (expert g, or the shared expert as group E) owns rows
 // off[g] .. off[g+1] and is cut into ceil(rows / BM) tiles of at most BM rows;
 // with extra > 0, a group whose last tile would hold at most `extra` rows
-// merges them into its previous tile instead (that tile then holds up to
-// BM + extra rows).  Tiles are listed group by group, row-ascending.  `off`
-// may sit in global memory or LDS.  ntiles[0] gets the tile count,
-// ntiles[1 .. kSplitSlots] (the grouped GEMM's split counters) zero.
+// merges them into its previous tile instead, which then holds more than BM
+// rows (a heavy tile).  The heavy tiles come first, one per such group in
+// group order, then every other tile, group by group and row-ascending;
+// `first` and `count` of a tile give the group's run of tiles in that second
+// part (a heavy tile: its own index, 1).  `off` may sit in global memory or
+// LDS.  ntiles[0] gets the tile count, ntiles[1 .. kSplitSlots] (the grouped
+// GEMM's split counters) zero, ntiles[kSplitSlots + 1] the heavy tile count.
 __device__ inline void build_tile_list(const int32_t* off, int G, int BM, int extra,
                                        RowTile* __restrict__ tiles, int32_t* __restrict__ ntiles,
                                        int32_t* wsum) {
   const int g = threadIdx.x;
-  int rows = 0, m = 0;
+  int rows = 0, m = 0, h = 0;
   if (g < G) {
     rows = off[g + 1] - off[g];
     m = (rows + BM - 1) / BM;
-    if (extra > 0 && m >= 2 && rows - (m - 1) * BM <= extra) --m;
+    if (extra > 0 && m >= 2 && rows - (m - 1) * BM <= extra) {
+      --m;
+      h = 1;  // the last of the m tiles holds rows - (m - 1) BM > BM rows
+    }
   }
-  int total;
-  const int start = block_excl_scan(m, wsum, total);
+  int heavy, normal;
+  const int hstart = block_excl_scan(h, wsum, heavy);
+  const int start = heavy + block_excl_scan(m - h, wsum, normal);
   if (g < G) {
     const int r0 = off[g];
     for (int j = 0; j < m; ++j) {
@@ -56,13 +63,17 @@ __device__ inline void build_tile_list(const int32_t* off, int G, int BM, int ex
       t.group = g;
       t.row0 = r0 + j * BM;
       t.rows = j + 1 < m ? BM : rows - j * BM;
-      t.first = start;
-      t.count = m;
+      const bool hv = h && j + 1 == m;
+      t.first = hv ? hstart : start;
+      t.count = hv ? 1 : m - h;
       t.pad0 = t.pad1 = t.pad2 = 0;
-      tiles[start + j] = t;
+      tiles[hv ? hstart : start + j] = t;
     }
   }
-  if (g == 0) ntiles[0] = total;
+  if (g == 0) {
+    ntiles[0] = heavy + normal;
+    ntiles[kSplitSlots + 1] = heavy;
+  }
   // arrival counters of the grouped GEMM's K split start from zero
   for (int i = threadIdx.x; i < kSplitSlots; i += blockDim.x) ntiles[1 + i] = 0;
 }

@@ -147,15 +147,25 @@ __device__ __forceinline__ int xcd_order(int pid, int total) {
   return full + x * q + min(x, r) + local;  // bijection onto [full, total)
 }
 
-// Tile id -> (row tile, n tile), each XCD on a contiguous range of the tile list.
+// Tile id -> (row tile, n tile).  The first H row tiles of the list are heavy
+// (more rows than the tile height, at most one per group): their H * NT tiles
+// come first, each row tile's N tiles in a row, so the longest tiles start in
+// the first round and a CU gets at most one of them while there are fewer than
+// the CUs.  The other tiles follow group by group.
 template <bool CHUNKED = false>
-__device__ __forceinline__ void decode_tile(const GemmArgs& a, int pid, int total, int* rt,
-                                            int* nt) {
+__device__ __forceinline__ void decode_tile(const GemmArgs& a, int pid, int total, int H,
+                                            int* rt, int* nt) {
   const int NT = a.n_tiles_n;
-  const int v = xcd_order<CHUNKED>(pid, total);
-  const RowTile& t = a.tiles[v / NT];
+  int v = xcd_order<CHUNKED>(pid, total);
+  if (v < H * NT) {
+    *rt = v / NT;
+    *nt = v % NT;
+    return;
+  }
+  v -= H * NT;  // index among the other tiles, whose row tiles start at H
+  const RowTile& t = a.tiles[H + v / NT];
   const int m = t.count;
-  const int ve = v - t.first * NT;           // index inside the group
+  const int ve = v - (t.first - H) * NT;     // index inside the group
   const int band = ve / (m * kBand);
   const int rem = ve - band * m * kBand;
   *nt = band * kBand + rem / m;
@@ -188,7 +198,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
   const int total = *a.ntiles * a.n_tiles_n;
   if (static_cast<int>(blockIdx.x) >= total) return;
   int rt, nt;
-  decode_tile(a, blockIdx.x, total, &rt, &nt);
+  decode_tile(a, blockIdx.x, total, 0, &rt, &nt);
   const RowTile tile = a.tiles[rt];
   const int g = tile.group;
   const bool sh = (g == a.E);
@@ -468,6 +478,8 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
   __shared__ int split_last;
 
   const int total = MODE == kWgrad ? a.E * a.tiles_m * a.n_tiles_n : *a.ntiles * a.n_tiles_n;
+  // heavy row tiles lead the list (only lists built for heavy-tile kernels have any)
+  const int nheavy = XR > 0 ? a.ntiles[kSplitSlots + 1] : 0;
   int D = total, R = 0, S = 1;
   if constexpr (!PERSIST) split_plan(total, a.slots, a.smax, &D, &R, &S);
   int t = blockIdx.x;
@@ -537,7 +549,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
       return c;
     }
     int rt, nt;
-    decode_tile<(XR > 0)>(a, tt, total, &rt, &nt);  // heavy tiles: chunks across XCDs
+    decode_tile<(XR > 0)>(a, tt, total, nheavy, &rt, &nt);  // heavy: chunks across XCDs
     rt = __builtin_amdgcn_readfirstlane(rt);
     nt = __builtin_amdgcn_readfirstlane(nt);
     const RowTile& rtile = a.tiles[rt];
@@ -840,14 +852,14 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
                                            (static_cast<int64_t>(cur.row0) * a.ldo + cur.n0) * OE
                                      : nullptr;
       const uint32_t ldo = static_cast<uint32_t>(a.ldo);
-      // CHK: some columns of the tile lie past N.  Rows are checked per 32-row
-      // block, only in blocks that reach past the tile's rows.
+      // CHK: some rows or columns of the tile are missing; then rows are
+      // checked per 32-row block, only in blocks that reach past the tile's rows.
       auto epilogue = [&](auto checked, auto relu) {
         constexpr bool CHK = decltype(checked)::value;
         constexpr bool RELU = decltype(relu)::value;
 #pragma unroll
         for (int i = 0; i < MU; ++i) {
-          const bool rchk = arow_blk(i) + 32 > cur.rows;
+          const bool rchk = CHK && arow_blk(i) + 32 > cur.rows;
 #pragma unroll
          for (int qh = 0; qh < 16; qh += 8) {
           // kDz: eight rows' pre-activations are loaded before any of their
@@ -905,7 +917,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
       // A tile whose columns all lie past its group's N (the shared expert's
       // narrower projection) stores nothing; the clamps of the partial-tile
       // path assume at least one valid column.
-      const bool full = cur.n0 + BN <= cur.N;  // every column of the tile is stored
+      const bool full = cur.rows == MU * 32 * WM && cur.n0 + BN <= cur.N;
       if (cur.n0 >= cur.N) {
       } else if ((MD::fwd_act || MODE == kDz) && a.act == MOE_ACT_RELU) {
         if (full) epilogue(std::false_type{}, std::true_type{});

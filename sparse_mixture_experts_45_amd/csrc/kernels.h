@@ -91,7 +91,8 @@ struct FfnArgs {
   void* H;           // [rows_max, max(F, Fs)] in dtype
   float* y_rows;     // [rows_max, d]
   RowTile* tiles;    // [tiles_max]
-  int32_t* ntiles;   // [1 + kSplitSlots]: the tile count, then the split counters
+  int32_t* ntiles;   // [2 + kSplitSlots]: the tile count, the split counters, the
+                     // heavy tile count
   float* row_gate;   // [rows_max]
   int64_t rows_max;  // bound on the routed plus shared rows (grid of the tile-list kernel)
   int tiles_ready;   // tiles, ntiles and row_gate already written by the dispatch

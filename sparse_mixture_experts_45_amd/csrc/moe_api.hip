@@ -229,7 +229,7 @@ Layout layout(const moe_config* c, bool train = false) {
   L.row_slot = take(sizeof(int32_t) * (ec ? 0 : L.rows_max));
   L.inv = take(sizeof(int32_t) * (ec ? 0 : T * k));
   L.tiles = take(sizeof(RowTile) * L.gp.tiles_max);
-  L.ntiles = take(sizeof(int32_t) * (1 + kSplitSlots));  // count, split counters
+  L.ntiles = take(sizeof(int32_t) * (2 + kSplitSlots));  // count, split counters, heavy count
   L.row_gate = take(sizeof(float) * L.rows_max);
   L.probsT = take(sizeof(float) * (ec ? E * T : 0));
   L.sel = take(sizeof(uint32_t) * E * L.ec_W);
