@@ -414,6 +414,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until at most min(pending, P) stages of JPW loads each are still in
+// flight (pending <= 0: none); the loads issued before them have then landed.
+template <int NS, int JPW, int P = NS - 2>
+__device__ __forceinline__ void wait_stages(int pending) {
+  if constexpr (P <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (pending >= P) wait_vmcnt<P * JPW>();
+    else wait_stages<NS, JPW, P - 1>(pending);
+  }
+}
+
 // Scheduling hints for N k16 steps: each step's NM MFMAs (0x008) with the NR
 // fragment reads (0x100: DS reads) of the following step spread between them.
 template <int S, int N, int NR, int NM>
@@ -675,16 +687,8 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
           // tile's epilogue stores were issued after this tile's first stages)
           if (kt == 0) {
             wait_vmcnt<0>();
-          } else if (kt + NS - 2 < KT) {
-            wait_vmcnt<JPW * (NS - 2)>();
-          } else if constexpr (NS > 2) {
-            if (kt + 1 == KT) wait_vmcnt<0>();
-            else if constexpr (NS > 3) {
-              if (kt + 2 == KT) wait_vmcnt<JPW>();
-              else wait_vmcnt<0>();
-            } else {
-              wait_vmcnt<0>();
-            }
+          } else {
+            wait_stages<NS, JPW>(KT - 1 - kt);
           }
           // Every lane's loads of stage kt landed; every wave finished reading stage
           // kt - 1.  A plain s_barrier: a workgroup fence would also wait for the
