@@ -62,6 +62,9 @@ def parse():
                         "copy of known size, then moe_expert_ffn calls")
     p.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="turn the two probe databases into the stored traffic summary")
+    p.add_argument("--pmc-summarize", nargs=2, metavar=("RESULTS_DB", "PROBE_LOG"),
+                   help="turn a rocprofv3 --pmc (+ --kernel-trace) run of --traffic-probe into the "
+                        "stored matrix-core utilisation summary")
     p.add_argument("--trace-summarize", nargs=2, metavar=("RESULTS_DB", "BENCH_JSON"),
                    help="turn a rocprofv3 --kernel-trace --stats run of this bench (its "
                         "results database and the JSON line it printed) into the stored "
@@ -182,7 +185,12 @@ def traffic_probe(args):
     for _ in range(5):
         moe.moe_expert_ffn(*fargs)
     torch.cuda.synchronize()
-    print("traffic probe done:", shape.name, flush=True)
+    # the grouping of these calls (token choice: what moe_dispatch wrote)
+    offsets = fargs[3].cpu().numpy()
+    kept = np.diff(offsets[:shape.E + 1])
+    print(json.dumps({"probe": "expert FFN", "workload": shape.name,
+                      "kept_rows": int(kept.sum()), "experts_hit": int((kept > 0).sum())}),
+          flush=True)
 
 
 # epilogue mode of a grouped-GEMM kernel: its last integer template argument
@@ -190,9 +198,23 @@ def traffic_probe(args):
 GEMM_MODE_UP, GEMM_MODE_DOWN = 0, 1
 
 
+def _template_args(kernel_name):
+    return [x.strip() for x in kernel_name.split("<", 1)[1].split(">", 1)[0].split(",")]
+
+
 def gemm_mode(kernel_name):
-    args = [x.strip() for x in kernel_name.split("<", 1)[1].split(">", 1)[0].split(",")]
+    """Epilogue mode of a grouped-GEMM kernel: the LDS-DMA kernel's ninth template
+    argument (<BM, BN, BK, NS, WM, WN, OCC, PERSIST, MODE, BT, XR>), else the
+    register-staged kernel's last integer one (<T, BM, BN, BK, WM, WN, MODE, BT>)."""
+    args = _template_args(kernel_name)
+    if "grouped_gemm_dma_kernel" in kernel_name:
+        return int(args[8])
     return int([x for x in args if x.lstrip("-").isdigit()][-1])
+
+
+def gemm_bt(kernel_name):
+    """Whether a grouped-GEMM kernel reads B stored [K, N] (the input-gradient pass)."""
+    return "true" in _template_args(kernel_name)
 
 
 def _counter_rows(db, counter):
@@ -217,7 +239,7 @@ def traffic_summarize(args):
         rec[counter.lower() + "_factor"] = round(factor, 4)
         for tag, mode in (("up", GEMM_MODE_UP), ("down", GEMM_MODE_DOWN)):
             vals = [v for _, n, v in rows
-                    if "grouped_gemm" in n and gemm_mode(n) == mode and "true>" not in n]
+                    if "grouped_gemm" in n and gemm_mode(n) == mode and not gemm_bt(n)]
             if not vals:
                 sys.exit("no %s GEMM dispatches in %s" % (tag, db))
             kib[(tag, counter)] = (float(np.mean(vals)), len(vals), factor)
@@ -302,7 +324,7 @@ def trace_summarize(args):
     total = sum(sum(v) for v in durs.values())
     names = sorted(durs, key=lambda n: -sum(durs[n]))
     gemm = lambda mode: [n for n in names  # noqa: E731
-                         if "grouped_gemm" in n and gemm_mode(n) == mode]
+                         if "grouped_gemm" in n and gemm_mode(n) == mode and not gemm_bt(n)]
     up, dn = gemm(GEMM_MODE_UP), gemm(GEMM_MODE_DOWN)
     tl = [n for n in names if "build_tiles_kernel" in n]
     if len(up) != 1 or len(dn) != 1:
@@ -350,6 +372,101 @@ def trace_summarize(args):
                                             run["value"]),
               ""]
     with open(trace_path(s.name), "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+PMC_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES",
+                "SQ_BUSY_CU_CYCLES", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT",
+                "GRBM_GUI_ACTIVE"]
+N_SIMD = 1024        # 256 CUs x 4 SIMDs
+N_XCD = 8
+MFMA_CYCLES = 32     # v_mfma_f32_32x32x16_bf16: 32 cycles of one SIMD's matrix core
+MFMA_FLOP = 32 * 32 * 16 * 2
+
+
+def pmc_path(workload):
+    return os.path.join(ROOT, "profiles", "pmc_expert_gemm_%s.md" % workload)
+
+
+def pmc_summarize(args):
+    """Matrix-core utilisation of the up and down GEMMs of one workload from a
+    rocprofv3 --pmc run (with --kernel-trace for durations) of --traffic-probe:
+    per-dispatch averages of the counters, the engine clock they imply and the
+    MFMA busy fraction at that clock and at the 2.4 GHz the peak assumes."""
+    db, log = args.pmc_summarize
+    probe = json.loads([ln for ln in open(log) if ln.startswith('{"probe"')][-1])
+    from moe_synth import workload
+    shape = workload(probe["workload"])
+    con = sqlite3.connect(db)
+    rows = con.execute("select dispatch_id, kernel_name, counter_name, value from "
+                       "counters_collection").fetchall()
+    durs = dict(con.execute("select dispatch_id, duration from kernels").fetchall())
+    con.close()
+    per = {}
+    for did, name, cname, val in rows:
+        if "grouped_gemm" not in name or gemm_bt(name):
+            continue
+        tag = {GEMM_MODE_UP: "up", GEMM_MODE_DOWN: "down"}.get(gemm_mode(name))
+        if tag is None:
+            continue
+        d = per.setdefault(tag, {"name": name, "disp": {}})
+        d["disp"].setdefault(did, {})[cname] = d["disp"].get(did, {}).get(cname, 0.0) + float(val)
+    kept = probe["kept_rows"]
+    # MFMA instructions the kept rows need, per GEMM: rows x N x K / (32 x 32 x 16)
+    need = {"up": kept * shape.F * shape.d / 16384.0, "down": kept * shape.d * shape.F / 16384.0}
+    if shape.Fs:
+        need = {k: v + shape.T * shape.Fs * shape.d / 16384.0 for k, v in need.items()}
+    rel_db = os.path.relpath(os.path.abspath(db), ROOT)
+    rel_log = os.path.relpath(os.path.abspath(log), ROOT)
+    wl = shape.name
+    lines = ["# Matrix-core utilisation of the expert GEMMs: %s" % wl, "",
+             "One `rocprofv3 --pmc` pass (with `--kernel-trace` for durations) over `bench.py "
+             "--traffic-probe` (a 256 MiB copy, then five `moe_expert_ffn` calls); per-dispatch "
+             "averages.  Commands (from the repository root, on one MI355X; "
+             "`cd /tmp && export TMPDIR=/tmp` first):", "", "```",
+             "rocprofv3 --kernel-trace --pmc %s -d %s -o %s -- python3 bench.py --traffic-probe "
+             "--workload %s > %s" % (" ".join(PMC_COUNTERS), os.path.dirname(rel_db),
+                                     os.path.basename(rel_db)[:-len("_results.db")], wl, rel_log),
+             "python3 bench.py --pmc-summarize %s %s" % (rel_db, rel_log), "```", "",
+             "| counter | up-projection | down-projection |", "|---|---|---|"]
+    avg = {}
+    for tag in ("up", "down"):
+        if tag not in per:
+            sys.exit("no %s-projection dispatches with counters in %s" % (tag, db))
+        disp = per[tag]["disp"]
+        avg[tag] = {c: float(np.mean([v.get(c, 0.0) for v in disp.values()])) for c in PMC_COUNTERS}
+        avg[tag]["us"] = float(np.mean([durs[i] for i in disp if i in durs])) / 1e3
+        avg[tag]["n"] = len(disp)
+    for c in PMC_COUNTERS:
+        lines.append("| `%s` | %.4g | %.4g |" % (c, avg["up"][c], avg["down"][c]))
+    lines.append("| duration (us, under the profiler) | %.1f | %.1f |" % (avg["up"]["us"],
+                                                                         avg["down"]["us"]))
+    lines += ["", "Kernels: `%s` (up), `%s` (down)." % (per["up"]["name"], per["down"]["name"]),
+              "", "Derived (per dispatch):"]
+    for tag in ("up", "down"):
+        a = avg[tag]
+        cyc = a["GRBM_GUI_ACTIVE"] / N_XCD          # engine cycles over the kernel
+        clk = cyc / a["us"] if a["us"] else 0.0     # MHz
+        busy = a["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cyc) if cyc else 0.0
+        busy24 = (a["SQ_INSTS_MFMA"] * MFMA_CYCLES / N_SIMD) / (a["us"] * 2400.0)
+        lines.append(
+            "- %s: %.3g MFMA instructions (%.3g for the kept rows: %.1f %% on padding rows); "
+            "%.1f cycles per MFMA; engine clock %.0f MHz (`GRBM_GUI_ACTIVE` / %d XCDs / "
+            "duration); matrix cores busy %.1f %% of the cycles at that clock, %.1f %% of a "
+            "2.4 GHz kernel duration; waves waiting %.1f %% of their cycles (`SQ_WAIT_ANY` / "
+            "`SQ_WAVE_CYCLES`); executed %.0f TFLOP/s, useful %.0f TFLOP/s; LDS bank "
+            "conflicts %.3g." % (
+                tag, a["SQ_INSTS_MFMA"], need[tag],
+                100.0 * (a["SQ_INSTS_MFMA"] - need[tag]) / max(a["SQ_INSTS_MFMA"], 1.0),
+                a["SQ_VALU_MFMA_BUSY_CYCLES"] / max(a["SQ_INSTS_MFMA"], 1.0), clk, N_XCD,
+                100.0 * busy, 100.0 * busy24,
+                100.0 * a["SQ_WAIT_ANY"] / max(a["SQ_WAVE_CYCLES"], 1.0),
+                a["SQ_INSTS_MFMA"] * MFMA_FLOP / (a["us"] * 1e-6) / 1e12,
+                need[tag] * MFMA_FLOP / (a["us"] * 1e-6) / 1e12, a["SQ_LDS_BANK_CONFLICT"]))
+    lines += ["", "Grouping of the probed calls: %d kept routed rows, %d experts hit." % (
+        kept, probe["experts_hit"]), ""]
+    with open(pmc_path(wl), "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
 
@@ -615,6 +732,9 @@ def main():
         return
     if args.trace_summarize:
         trace_summarize(args)
+        return
+    if args.pmc_summarize:
+        pmc_summarize(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the MoE layer here is the data-parallel "

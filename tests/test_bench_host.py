@@ -59,13 +59,17 @@ def test_default_workloads():
     assert flop2 / nbytes2 < bench.RIDGE
 
 
-@pytest.mark.parametrize("name,mode", [
-    ("moe::grouped_gemm_dma_kernel<128, 128, 64, 2, 2, 4, 2, 0, 0, false>", 0),
-    ("void moe::grouped_gemm_dma_kernel<256, 256, 64, 2, 2, 4, 2, 0, 1, true>(moe::GemmArgs)", 1),
-    ("moe::grouped_gemm_kernel<float, 64, 64, 32, 2, 2, 3, false>", 3),
+@pytest.mark.parametrize("name,mode,bt", [
+    ("moe::grouped_gemm_dma_kernel<128, 128, 64, 2, 2, 4, 2, 0, 0, false, 0>", 0, False),
+    ("void moe::grouped_gemm_dma_kernel<256, 256, 64, 2, 2, 4, 2, 0, 1, true, 0>(moe::GemmArgs)",
+     1, True),
+    ("void moe::grouped_gemm_dma_kernel<256, 256, 64, 2, 2, 4, 2, 0, 1, false, 1>(moe::GemmArgs)",
+     1, False),
+    ("moe::grouped_gemm_kernel<float, 64, 64, 32, 2, 2, 3, false>", 3, False),
 ])
-def test_gemm_mode_of_kernel_name(name, mode):
+def test_gemm_mode_of_kernel_name(name, mode, bt):
     assert bench.gemm_mode(name) == mode
+    assert bench.gemm_bt(name) == bt
 
 
 def test_stored_traffic_summaries_parse():
