@@ -44,6 +44,9 @@ SMALL = [
     S("ec_many_experts", T=200, d=64, F=32, E=300, k=3, router_bias="none"),
     S("ec_uncached_keys", T=20000, d=64, F=64, E=8, k=1),
     S("ec_e64_router_fused", T=2048, d=256, F=128, E=64, k=2),
+    # 800 tokens per expert = 3 x 256 + 32: the 256-row tier with a heavy last
+    # tile per expert (288 rows), and a shared expert of 2000 rows (7 x 256 + 208)
+    S("ec_heavy_tiles", T=2000, d=192, F=256, E=3, k=1, capacity=800, Fs=128),
 ]
 
 
