@@ -488,8 +488,9 @@ def algorithmic(shape, kept_rows, hit_experts):
 
 def cpu_baseline(shape, inp, seconds):
     """The fp64 oracle on the host cores over a bounded sample of the batch: routing of
-    the whole batch, then expert MLPs + combine over tokens in batch order, repeating
-    the batch when one pass is shorter than `seconds`, until about `seconds` of work."""
+    the whole batch (timed once, prorated to the tokens processed), then expert MLPs
+    and combine over consecutive chunks of tokens in batch order (wrapping around
+    the batch), until about `seconds` of work."""
     import oracle
     t0 = time.perf_counter()
     if shape.routing == "expert":
@@ -499,29 +500,23 @@ def cpu_baseline(shape, inp, seconds):
         rt = oracle.route(shape, inp, with_probs=False)
         experts = lambda toks: oracle.experts(shape, inp, rt, toks)  # noqa: E731
     t_route = time.perf_counter() - t0
-    # calibrate on a few tokens, then size the sample to ~`seconds`
-    n0 = min(shape.T, 8)
-    t1 = time.perf_counter()
-    experts(np.arange(n0))
-    per_tok = (time.perf_counter() - t1) / max(n0, 1)
-    per_tok_all = per_tok + t_route / max(shape.T, 1)
-    # one pass over the whole batch when it fits the budget, else the prefix that does;
-    # passes repeat until the measured time reaches the budget
-    chunk = int(min(shape.T, max(n0, seconds / max(per_tok_all, 1e-9))))
-    t_exp, done = 0.0, 0
+    T = max(shape.T, 1)
+    # chunks of about a tenth of the budget, sized from the tokens already timed
+    n, t_exp, done = min(shape.T, 8), 0.0, 0
     while True:
-        toks = np.arange(chunk)
+        toks = (done + np.arange(n)) % T
         t2 = time.perf_counter()
         experts(toks)
         t_exp += time.perf_counter() - t2
-        done += chunk
-        if chunk < shape.T or t_exp + t_route * done / max(shape.T, 1) >= seconds:
+        done += n
+        dt = t_exp + t_route * done / T
+        if dt >= seconds or shape.T == 0:
             break
-    # routing is timed once per full batch and prorated to the tokens processed
-    dt = t_exp + t_route * done / max(shape.T, 1)
+        per_tok = dt / done
+        n = int(max(1, min(shape.T, (seconds - dt) / per_tok, 0.1 * seconds / per_tok + 1)))
     if done >= shape.T:
-        what = "%d tokens = %.2f passes over the %d-token %s batch" % (done, done / shape.T,
-                                                                      shape.T, shape.name)
+        what = "%d tokens = %.2f passes over the %d-token %s batch" % (done, done / T, shape.T,
+                                                                      shape.name)
     else:
         what = "the first %d tokens of the %d-token %s batch" % (done, shape.T, shape.name)
     return {"value": round(done / dt, 3), "unit": "tokens/s", "cores": oracle.threads(),
