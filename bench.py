@@ -610,9 +610,17 @@ def bench_backward(args):
     print(json.dumps(out), flush=True)
 
 
+def calls_per_graph(steps):
+    """Layer calls captured in one HIP graph: the largest of 10, 5, 4, 2, 1 that
+    divides `steps` (replays of a one-call graph left ~0.1 ms between replays
+    on the Mixtral-shaped layer that several calls per replay do not)."""
+    return next(n for n in (10, 5, 4, 2, 1) if steps % n == 0)
+
+
 def time_layer(moe, torch, shape, dev, steps, warmup, use_graph):
-    """moe_forward over `steps` calls (replayed from a HIP graph when use_graph),
-    bracketed by device synchronisation.  Returns (seconds, kept [E] counts)."""
+    """moe_forward over `steps` calls (replayed from a HIP graph of
+    calls_per_graph(steps) calls when use_graph), bracketed by device
+    synchronisation.  Returns (seconds, kept [E] counts)."""
     tdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
     cfg = layer_config(moe, torch, shape)
     ws = moe.workspace(cfg)
@@ -632,10 +640,12 @@ def time_layer(moe, torch, shape, dev, steps, warmup, use_graph):
         for _ in range(warmup):
             step()
     torch.cuda.synchronize()
+    per = calls_per_graph(steps)
     if use_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            step()
+            for _ in range(per):
+                step()
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             for _ in range(2):
@@ -646,10 +656,11 @@ def time_layer(moe, torch, shape, dev, steps, warmup, use_graph):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
-        for _ in range(steps):
-            if graph is not None:
+        if graph is not None:
+            for _ in range(steps // per):
                 graph.replay()
-            else:
+        else:
+            for _ in range(steps):
                 step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -771,6 +782,7 @@ def main():
                    "n_experts": E, "top_k": k, "capacity": shape.capacity,
                    "shared_d_ff": shape.Fs, "act": shape.act, "routing": shape.routing,
                    "hip_graph": bool(args.graph),
+                   "calls_per_graph": calls_per_graph(args.steps) if args.graph else 0,
                    "kept_rows": kept_rows, "experts_hit": hit},
         "layer_tflops": round(flop / (ms_per_step * 1e-3) / 1e12, 2),
         "roofline": roof,

@@ -40,6 +40,11 @@ def test_algorithmic_work_shared_expert():
     assert nbytes == w + 2 * 512 * 7168 * 2
 
 
+@pytest.mark.parametrize("steps,per", [(50, 10), (20, 10), (15, 5), (8, 4), (6, 2), (7, 1), (1, 1)])
+def test_calls_per_graph_divides_the_steps(steps, per):
+    assert bench.calls_per_graph(steps) == per and steps % per == 0
+
+
 def test_default_workloads():
     """The default bench line is the Mixtral-shaped layer (matrix-core bound) with
     the DeepSeek-shaped layer (weight streaming) as its second roofline."""

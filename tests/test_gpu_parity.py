@@ -50,7 +50,12 @@ SMALL = [
     S("bf16_no_expert_bias", T=150, d=128, F=128, E=8, k=2, expert_bias=False,
       router_bias="none"),
     # K multiples of 64: the LDS-DMA kernels; tile tier follows rows per expert
+    # 256-row tiles: 800 rows per expert leave 32 (a heavy tile whose extra
+    # rows need the first wave row only), 816 leave 48 (both wave rows), 790
+    # leave 22, with a shared expert's heavy tile too
     S("dma_large_ntail", T=800, d=192, F=320, E=2, k=2),
+    S("dma_large_heavy48", T=816, d=192, F=320, E=2, k=2),
+    S("dma_large_heavy_shared", T=790, d=128, F=256, E=2, k=2, Fs=192),
     S("dma_large_shared", T=900, d=256, F=256, E=2, k=2, Fs=192, act="relu"),
     S("dma_mid_ntail", T=600, d=192, F=320, E=4, k=2),
     S("dma_small_ragged", T=300, d=128, F=192, E=4, k=2),
