@@ -317,6 +317,8 @@ def trace_summarize(args):
     db, bench_json = args.trace_summarize
     line = [ln for ln in open(bench_json) if ln.lstrip().startswith("{")][-1]
     run = json.loads(line)
+    if "backward" in run:
+        return trace_summarize_backward(db, bench_json, run)
     from moe_synth import workload
     shape = workload(run["config"]["workload"])
     kept_rows, hit = run["config"]["kept_rows"], run["config"]["experts_hit"]
@@ -372,6 +374,42 @@ def trace_summarize(args):
                                             run["value"]),
               ""]
     with open(trace_path(s.name), "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def trace_summarize_backward(db, bench_json, run):
+    """Kernel-trace summary of one profiled `--backward` run: every kernel's
+    call count and durations, and the run's own training-step line."""
+    wl = run["config"]["workload"]
+    durs = _kernel_durations(db)
+    total = sum(sum(v) for v in durs.values())
+    names = sorted(durs, key=lambda n: -sum(durs[n]))
+    rel_db = os.path.relpath(os.path.abspath(db), ROOT)
+    rel_json = os.path.relpath(os.path.abspath(bench_json), ROOT)
+    b = run["backward"]
+    lines = [
+        "# Kernel trace: training step (moe_forward_train + moe_backward), %s" % wl, "",
+        "Commands (from the repository root, on one MI355X; `cd /tmp && export TMPDIR=/tmp` "
+        "first for the profiler's scratch files):", "", "```",
+        "rocprofv3 --kernel-trace --stats -d %s -o %s -- python3 bench.py --backward --workload %s "
+        "--steps %d --warmup %d > %s" % (os.path.dirname(rel_db),
+                                         os.path.basename(rel_db)[:-len("_results.db")], wl,
+                                         run["steps"], run["warmup"], rel_json),
+        "python3 bench.py --trace-summarize %s %s" % (rel_db, rel_json),
+        "```", "",
+        "| kernel | calls | avg (us) | min (us) | max (us) | share |",
+        "|---|---|---|---|---|---|"]
+    for n in names:
+        v = durs[n]
+        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %.1f %% |" % (
+            n, len(v), float(np.mean(v)) / 1e3, min(v) / 1e3, max(v) / 1e3,
+            100.0 * sum(v) / total))
+    lines += ["", "The profiled run's own bench line (under the profiler): training step %.4f ms, "
+              "backward %.4f ms (HIP events), backward GEMM work %.4g FLOP = %.1f TFLOP/s, %.4f "
+              "of the bf16 peak." % (run["ms_per_step"], b["ms"], b["gemm_flop"],
+                                     b["achieved_tflops"], b["frac"]), ""]
+    with open(os.path.join(ROOT, "profiles", "kernel_trace_backward_%s.md" % wl), "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
 
