@@ -203,3 +203,31 @@ def test_graph_replays_match_eager():
     oinp = device_inputs(make_inputs(other_shape, 2))
     step.__outs__ = dict(grads, y=y)
     _replays(step, eager, lambda: gpu_forward(other_shape, oinp))
+
+
+def test_graph_of_several_calls():
+    """Several moe_forward calls captured back to back in one HIP graph (as the
+    benchmark replays them), on the 256-row tier with heavy tiles and a K split
+    of the last round: the calls share one workspace, so each call's tile list
+    must leave the split counters ready for the next.  Each replay equals the
+    eager result bit for bit, and the oracle within tolerance."""
+    shape = LayerShape("graph_heavy", T=800, d=256, F=8192, E=2, k=2, dtype="bf16", Fs=8192,
+                       router_bias="normal")
+    say("case", shape)
+    inp = make_inputs(shape, 21)
+    dev = device_inputs(inp)
+    c = cfg_of(shape)
+    ws = moe.workspace(c)
+    y = torch.empty((shape.T, shape.d), dtype=torch.bfloat16, device="cuda")
+    moe.moe_forward(c, dev, dev["x"], y, None, ws)
+    torch.cuda.synchronize()
+    check_y(shape, y.float().cpu().numpy().astype(np.float64), oracle.forward(shape, inp)["y"])
+    eager = {"y": y.clone()}
+    other_shape = LayerShape("other", T=200, d=64, F=64, E=4, k=2, dtype="bf16")
+    oinp = device_inputs(make_inputs(other_shape, 2))
+
+    def capture():
+        for _ in range(3):
+            moe.moe_forward(c, dev, dev["x"], y, None, ws)
+    capture.__outs__ = {"y": y}
+    _replays(capture, eager, lambda: gpu_forward(other_shape, oinp))
