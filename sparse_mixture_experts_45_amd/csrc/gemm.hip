@@ -375,9 +375,12 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 
 // 16 bytes from global memory to LDS; the wave's 64 lanes fill 1 KB starting at
-// the wave-uniform address `lds` (lane L at lds + 16 L).
+// the wave-uniform address `lds` (lane L at lds + 16 L).  CPOL: the load's
+// cache-policy bits (0, or kCpolNT for data read once).
+constexpr int kCpolNT = 2;  // gfx950 `nt`: non-temporal
+template <int CPOL = 0>
 __device__ __forceinline__ void lds_dma16(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, CPOL);
 }
 
 // Chunk swizzle of tile row r.  gfx950 LDS has 64 four-byte banks (256 bytes
@@ -453,7 +456,7 @@ __device__ __forceinline__ void sched_steps() {
 // previous tile instead of giving them a tile of their own; tiles of at most
 // BM rows skip the extra block's loads and MFMAs.
 template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int MODE,
-          bool BT, int XR = 0>
+          bool BT, int XR = 0, int NTB = 0>
 __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(GemmArgs a) {
   using MD = ModeOf<MODE>;
   // BT: the group's B is stored [K, N] (row k holds N contiguous values), as
@@ -642,11 +645,15 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void grouped_gemm_dma_kernel(Gemm
   bool heavy = XR > 0 && cur.rows > BM;
   auto issue = [&](int stage, int k0) {
 #pragma unroll
-    for (int j = 0; j < JPW; ++j)
-      if (XR == 0 || heavy || j < JA - JX || j >= JA)
-        lds_dma16((j < JA ? abase : bbase) + src[j] +
-                      static_cast<uint32_t>(k0) * (j < JA ? 2u : bstep),
-                  smem + stage * STAGE + (wave + j * NW) * RPI * RB);
+    for (int j = 0; j < JPW; ++j) {
+      if (XR > 0 && !heavy && j >= JA - JX && j < JA) continue;
+      char* dst = smem + stage * STAGE + (wave + j * NW) * RPI * RB;
+      if (j < JA)
+        lds_dma16(abase + src[j] + static_cast<uint32_t>(k0) * 2u, dst);
+      else  // the weights (not the activations B holds in kWgrad)
+        lds_dma16<NTB && MODE != kWgrad ? kCpolNT : 0>(
+            bbase + src[j] + static_cast<uint32_t>(k0) * bstep, dst);
+    }
   };
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
@@ -1047,10 +1054,10 @@ static int cu_count() {
 // count; otherwise one block per tile, plus up to `slots` more for the K split
 // of a last round (split: partial tiles reserved, 0 for none).
 template <int BM, int BN, int BK, int NS, int WM, int WN, int OCC, int PERSIST, int MODE,
-          bool BT, int XR = 0>
+          bool BT, int XR = 0, int NTB = 0>
 static void launch_dma(GemmArgs g, int64_t tiles, int split, hipStream_t st) {
   if (tiles <= 0) return;
-  auto kern = grouped_gemm_dma_kernel<BM, BN, BK, NS, WM, WN, OCC, PERSIST, MODE, BT, XR>;
+  auto kern = grouped_gemm_dma_kernel<BM, BN, BK, NS, WM, WN, OCC, PERSIST, MODE, BT, XR, NTB>;
   const size_t lds = static_cast<size_t>(NS) * (BM + XR * WM * 32 + BN) * BK * 2;
   static int per_cu = [&] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1076,13 +1083,13 @@ static void launch_dma(GemmArgs g, int64_t tiles, int split, hipStream_t st) {
 }
 
 template <int BM, int BNU, int BND, int BK, int NS, int WM, int WN, int OCC, int PERSIST,
-          int WMD, int WND, int SPLIT, int M1, bool BT, int XR = 0>
+          int WMD, int WND, int SPLIT, int NTB, int M1, bool BT, int XR = 0>
 static void run_dma(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
   const GemmArgs u = up_args(f, BNU);
-  launch_dma<BM, BNU, BK, NS, WM, WN, OCC, PERSIST, M1, BT, XR>(u, gp.tiles_max * u.n_tiles_n,
-                                                                SPLIT, st);
+  launch_dma<BM, BNU, BK, NS, WM, WN, OCC, PERSIST, M1, BT, XR, NTB>(
+      u, gp.tiles_max * u.n_tiles_n, SPLIT, st);
   const GemmArgs dn = down_args(f, BND);
-  launch_dma<BM, BND, BK, NS, WMD, WND, OCC, PERSIST, kDown, BT, XR>(
+  launch_dma<BM, BND, BK, NS, WMD, WND, OCC, PERSIST, kDown, BT, XR, NTB>(
       dn, gp.tiles_max * dn.n_tiles_n, SPLIT, st);
 }
 
@@ -1097,7 +1104,7 @@ static void run_pass(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
     case kGemmBf16Small: run_generic<bf16, 32, 128, 128, 64, 1, 4, M1, BT>(gp, f, st); break;
 #define MOE_RUN_DMA(C)                                                                     \
   run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN, C.OCC, C.PERSIST, C.WMD, C.WND, C.SPLIT, \
-          M1, BT>(gp, f, st)
+          C.NTB, M1, BT>(gp, f, st)
     case kGemmDmaLarge:
       // the forward's tile list may hold heavy tiles (rows past BM)
       if constexpr (M1 == kUp && !BT) {
@@ -1105,7 +1112,7 @@ static void run_pass(const GemmPlan& gp, const FfnArgs& f, hipStream_t st) {
         static_assert(C.WM == C.WMD && C.NS == 2 && !C.PERSIST, "heavy tiles");
         if (gp.extra > 0) {
           run_dma<C.BM, C.BNU, C.BND, C.BK, C.NS, C.WM, C.WN, C.OCC, C.PERSIST, C.WMD, C.WND,
-                  C.SPLIT, M1, BT, 1>(gp, f, st);
+                  C.SPLIT, C.NTB, M1, BT, 1>(gp, f, st);
           break;
         }
       }

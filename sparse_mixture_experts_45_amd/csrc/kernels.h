@@ -37,16 +37,20 @@ struct DmaCfg {
   // per SIMD the register budget is sized for, whether blocks stay resident and
   // walk several tiles (1) or each block takes one tile (0), and the down
   // GEMM's wave grid; SPLIT: partial tiles reserved for the K split below (0:
-  // the tier never splits)
-  int BM, BNU, BND, BK, NS, WM, WN, OCC, PERSIST, WMD, WND, SPLIT;
+  // the tier never splits); NTB: the weight (B) tiles of the forward and
+  // input-gradient GEMMs are loaded with the non-temporal cache policy (1):
+  // measured faster where the layer's weights are streamed (the 32-, 192- and
+  // 256-row tiers), slower where they are read again from the caches (the
+  // 64- and 128-row tiers)
+  int BM, BNU, BND, BK, NS, WM, WN, OCC, PERSIST, WMD, WND, SPLIT, NTB;
 };
-constexpr DmaCfg kDmaLarge{256, 256, 256, 64, 2, 2, 4, 2, 0, 2, 4, 256};  // >= 768 rows per expert
-constexpr DmaCfg kDmaMid{128, 128, 128, 64, 2, 2, 4, 2, 0, 2, 4, 512};    // >= 256
-constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 3, 1, 4, 2, 1, 1, 4, 0};     // >= 48 (3 stages: 2 blocks per CU)
-constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 3, 1, 4, 2, 0, 1, 4, 0};    // fewer: weight streaming
+constexpr DmaCfg kDmaLarge{256, 256, 256, 64, 2, 2, 4, 2, 0, 2, 4, 256, 1};  // >= 768 rows per expert
+constexpr DmaCfg kDmaMid{128, 128, 128, 64, 2, 2, 4, 2, 0, 2, 4, 512, 0};    // >= 256
+constexpr DmaCfg kDmaSmall{64, 128, 128, 64, 3, 1, 4, 2, 1, 1, 4, 0, 0};     // >= 48 (3 stages: 2 blocks per CU)
+constexpr DmaCfg kDmaSkinny{32, 128, 128, 64, 3, 1, 4, 2, 0, 1, 4, 0, 1};    // fewer: weight streaming
 // 192-row tiles where an expert's rows (about 128-165) fit one: a quarter
 // fewer MFMAs on padding rows than 256
-constexpr DmaCfg kDmaTall{192, 256, 256, 64, 2, 2, 4, 2, 0, 2, 4, 256};
+constexpr DmaCfg kDmaTall{192, 256, 256, 64, 2, 2, 4, 2, 0, 2, 4, 256, 1};
 
 // K split of a last, partly filled round.  When a launch's tiles leave the
 // final round of resident blocks (`slots` of them) at most half full, each of
