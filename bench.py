@@ -782,7 +782,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the MoE layer here is the data-parallel "
-              "replica of one GPU; multi-GPU runs are not part of this build "
+              "replica of one GPU; this library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
