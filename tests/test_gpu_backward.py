@@ -160,12 +160,16 @@ def test_forward_train_output_equals_forward():
 
 
 @pytest.mark.parametrize("name,n_tok", [("page1_b4s512", 48), ("mixtral_t4096", 12),
-                                        ("deepseek_e256_top8", 12)])
+                                        ("deepseek_e256_top8", 12),
+                                        ("switch_e64_top1_cap", 24),
+                                        ("deepseek_ep8_rank", 12)])
 def test_backward_workload(name, n_tok):
     """Full-size shapes: dx on sampled tokens, entries of two experts' weight
     gradients (and the bias gradients at those entries), and, for page-1, the
     router gradients from every token's dl.  The DeepSeek shape (16 rows per
-    expert) runs the weight gradients with one or two K steps per tile."""
+    expert) runs the weight gradients with one or two K steps per tile; the
+    Switch shape (capacity 160, skewed router) has dropped tokens and experts
+    with few or no rows; the expert-parallel share takes 192-row tiles."""
     shape = workload(name)
     say("workload", shape)
     inp = make_inputs(shape, 0)
