@@ -6,6 +6,7 @@
 #include <mutex>
 
 #include "kernels.h"
+#include "router_tile.h"
 
 using namespace moe;
 
@@ -171,7 +172,7 @@ RoutePlan route_plan(const moe_config* c) {
   // keeping >= 2 K steps.  bf16 layers whose experts fit one score tile
   // (E <= 64) and that gain nothing from a split run the gate inside the score
   // kernel (one launch).
-  const int TE = c->n_experts <= 16 ? 16 : 64;
+  const int TE = router_tile(c->n_experts, c->dtype);
   const int QK = 16 / (TE / 16);
   const int64_t base_blocks = ceil_div(c->T, 64) * ceil_div(c->n_experts, TE);
   int S = static_cast<int>(std::max<int64_t>(1, ceil_div(256, std::max<int64_t>(1, base_blocks))));

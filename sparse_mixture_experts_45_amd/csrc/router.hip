@@ -7,6 +7,7 @@
 // of Experts", router formula Softmax(TopK(x W_g)) and "Tiny example";
 // botmartz "Load Balancing" (mean router probability per expert).
 #include "kernels.h"
+#include "router_tile.h"
 #include "block_ops.h"
 
 namespace moe {
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(256) void router_scores_f32_kernel(const float* __r
 // sum_k x w = S(hi) + S(mid + lo) is accumulated in fp32: the precision of an
 // fp32 dot product.
 //
-// Block = 16 waves over 64 tokens x TE experts (TE = 16 or 64) and one K chunk.
+// Block = 16 waves over 64 tokens x TE experts (TE = 16, 32 or 64) and one K chunk.
 // Wave w takes expert block w % (TE / 16) and K slice w / (TE / 16): the chunk's
 // 32-wide K steps are dealt round-robin to the slices.  A wave multiplies all
 // four 16-token row blocks with its 16 experts (v_mfma_f32_16x16x32_bf16: lane l
@@ -531,7 +532,8 @@ __global__ __launch_bounds__(1024) void router_stats_kernel(const double* __rest
 }
 
 // ------------------------------------------------------------------ launches
-// Fused score + gate kernels: TE = 16 (E <= 16) or 64 (E <= 64, VPL 2 or 4).
+// Fused score + gate kernels: TE = 16 (E <= 16), 32 (E <= 32, VPL 2) or 64 (E <= 64,
+// VPL 2 or 4).
 #define MOE_FUSED(TE_, VPL_)                                                                    \
   router_scores_bf16_kernel<TE_, true, 16, VPL_><<<g1, kRw * 64, 0, st>>>(                     \
       static_cast<const bf16*>(x), Wg, bg, p.T, p.d, p.E, p.kchunk, part, p.k, p.renorm,       \
@@ -542,18 +544,23 @@ hipError_t launch_router(const RoutePlan& p, const void* x, int dtype, const flo
                          float* probs, double* stat_part, int32_t* hist, float* mean_prob,
                          float* balance, hipStream_t st) {
   if (p.T > 0) {
-    const int TE = p.E <= 16 ? 16 : 64;
+    const int TE = router_tile(p.E, dtype);
     dim3 g1(static_cast<unsigned>(ceil_div(p.T, kRtM)), static_cast<unsigned>(ceil_div(p.E, TE)),
             static_cast<unsigned>(p.S));
     if (p.fused) {
       // one block holds every score of its 64 tokens: the gate runs in place
       if (TE == 16) MOE_FUSED(16, 1);
+      else if (TE == 32) MOE_FUSED(32, 2);
       else if (p.vpl <= 2) MOE_FUSED(64, 2);
       else MOE_FUSED(64, 4);
     } else {
       if (dtype == MOE_BF16) {
         if (TE == 16)
           router_scores_bf16_kernel<16, false, 16, 1><<<g1, kRw * 64, 0, st>>>(
+              static_cast<const bf16*>(x), Wg, bg, p.T, p.d, p.E, p.kchunk, part, p.k,
+              p.renorm, topk_idx, topk_w, probs, p.ps_t, p.ps_e, stat_part, hist);
+        else if (TE == 32)
+          router_scores_bf16_kernel<32, false, 16, 1><<<g1, kRw * 64, 0, st>>>(
               static_cast<const bf16*>(x), Wg, bg, p.T, p.d, p.E, p.kchunk, part, p.k,
               p.renorm, topk_idx, topk_w, probs, p.ps_t, p.ps_e, stat_part, hist);
         else
