@@ -231,11 +231,34 @@ __device__ __forceinline__ void scatter_block_few(int64_t b, const int (&mine)[K
   }
 }
 
-// Any k: slots rolled, each pair placed as soon as its rank is known (keeps the
-// registers few for large k).  Slot j of the block's token `lane` is read from
-// ids[lane * ids_stride + j] and its gate from gates[lane * ids_stride + j]
-// (gates only needed with row_gate): LDS copies of the block's ids and gates
-// when they fit, else topk_idx / topk_w themselves.
+// Slot i of every token of 64-token block b (one wave, lane = token): ranked
+// against all k slots of the lower lanes, then placed.  Slot j of the block's
+// token `lane` is read from ids[lane * ids_stride + j] and its gate from
+// gates[lane * ids_stride + j] (gates only needed with row_gate): LDS copies of
+// the block's ids and gates when they fit, else topk_idx / topk_w themselves.
+__device__ __forceinline__ void scatter_slot(int64_t b, int i, const int32_t* ids,
+                                             int ids_stride, const float* gates, int64_t T,
+                                             int k, int E, int nbits, const int32_t* base,
+                                             const int32_t* kept, const int32_t* offsets,
+                                             int32_t* __restrict__ row_token,
+                                             int32_t* __restrict__ row_slot,
+                                             int32_t* __restrict__ inv,
+                                             float* __restrict__ row_gate) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = b * kGateTokens + lane;
+  const bool valid = t < T;
+  const uint64_t live = __ballot(valid) & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)));
+  const int32_t* my = ids + lane * ids_stride;
+  const int ei = valid ? my[i] : 0;
+  int rank = 0;
+  for (int j = 0; j < k; ++j) rank += lower_matches(valid ? my[j] : 0, ei, nbits, live);
+  if (valid)
+    place_pair(t, i, k, ei, rank, E, base, kept, offsets,
+               gates ? gates[lane * ids_stride + i] : 0.f, row_token, row_slot, inv, row_gate);
+}
+
+// Any k on one wave: slots rolled, each pair placed as soon as its rank is known
+// (keeps the registers few for large k).
 __device__ __forceinline__ void scatter_block_any(int64_t b, const int32_t* ids, int ids_stride,
                                                   const float* gates, int64_t T,
                                                   int k, int E, int nbits, const int32_t* base,
@@ -244,21 +267,11 @@ __device__ __forceinline__ void scatter_block_any(int64_t b, const int32_t* ids,
                                                   int32_t* __restrict__ row_slot,
                                                   int32_t* __restrict__ inv,
                                                   float* __restrict__ row_gate) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = b * kGateTokens + lane;
-  const bool valid = t < T;
-  const uint64_t live = __ballot(valid) & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)));
-  const int32_t* my = ids + lane * ids_stride;
-  const float* myg = gates ? gates + lane * ids_stride : nullptr;
-  for (int i = 0; i < k; ++i) {
-    const int ei = valid ? my[i] : 0;
-    int rank = 0;
-    for (int j = 0; j < k; ++j) rank += lower_matches(valid ? my[j] : 0, ei, nbits, live);
-    if (valid)
-      place_pair(t, i, k, ei, rank, E, base, kept, offsets, myg ? myg[i] : 0.f, row_token,
+  for (int i = 0; i < k; ++i)
+    scatter_slot(b, i, ids, ids_stride, gates, T, k, E, nbits, base, kept, offsets, row_token,
                  row_slot, inv, row_gate);
-  }
-  if (valid && shared) place_shared(t, E, offsets, row_token, row_slot, row_gate);
+  const int64_t t = b * kGateTokens + (threadIdx.x & 63);
+  if (t < T && shared) place_shared(t, E, offsets, row_token, row_slot, row_gate);
 }
 
 // Copy the ids (and, with wdst set, the gates) of 64-token block b (64 x k,
@@ -292,8 +305,10 @@ __device__ __forceinline__ void stage_ids(int64_t b, const int32_t* __restrict__
   }
 }
 
+// One 64-token block per workgroup: one wave, or with more than 4 slots and at
+// most kIdsK of them, one wave per slot (ids staged in LDS by wave 0).
 template <int KM>
-__global__ __launch_bounds__(64) void dispatch_scatter_kernel(
+__global__ __launch_bounds__(KM <= 4 ? 64 : 64 * kIdsK) void dispatch_scatter_kernel(
     const int32_t* __restrict__ topk_idx, int64_t T, int k, int E, int nbits,
     const int32_t* __restrict__ base, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ offsets, int shared, int32_t* __restrict__ row_token,
@@ -308,9 +323,14 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(
   } else {
     __shared__ int32_t sids[kGateTokens * (kIdsK + 1)];
     if (k <= kIdsK) {
-      stage_ids(b, topk_idx, nullptr, T, k, sids, nullptr);
-      scatter_block_any(b, sids, kIdsK + 1, nullptr, T, k, E, nbits, base + b * E, kept,
-                        offsets, shared, row_token, row_slot, inv, nullptr);
+      const int wave = threadIdx.x >> 6;
+      if (wave == 0) stage_ids(b, topk_idx, nullptr, T, k, sids, nullptr);
+      __syncthreads();
+      if (wave < k)
+        scatter_slot(b, wave, sids, kIdsK + 1, nullptr, T, k, E, nbits, base + b * E, kept,
+                     offsets, row_token, row_slot, inv, nullptr);
+      const int64_t t = b * kGateTokens + (threadIdx.x & 63);
+      if (wave == 0 && shared && t < T) place_shared(t, E, offsets, row_token, row_slot, nullptr);
     } else {
       scatter_block_any(b, topk_idx + b * kGateTokens * k, k, nullptr, T, k, E, nbits,
                         base + b * E, kept, offsets, shared, row_token, row_slot, inv, nullptr);
@@ -402,16 +422,28 @@ __global__ __launch_bounds__(1024) void dispatch_blocks_kernel(DispatchArgs a) {
     if (a.cv2) counts_cv2(cnt, E, a.cv2, wsd);
     build_tile_list(soff, E + (a.shared ? 1 : 0), a.BM, a.extra, a.tiles, a.ntiles, wsum);
   }
-  if (!scatter) return;
+  if (b >= nb) return;
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
+  if constexpr (KM > 4) {
+    if (a.k <= kIdsK) {
+      // the block's ids and gates to LDS, then wave i ranks and places slot i
+      if (wave == 0) stage_ids(b, a.topk_idx, a.topk_w, a.T, a.k, sids, sgts);
+      __syncthreads();
+      if (wave < a.k)
+        scatter_slot(b, wave, sids, kIdsK + 1, sgts, a.T, a.k, E, nbits, sbase, skept, soff,
+                     a.row_token, a.row_slot, a.inv, a.row_gate);
+      if (wave == 0 && a.shared) {
+        const int64_t t = static_cast<int64_t>(b) * kGateTokens + (tid & 63);
+        if (t < a.T) place_shared(t, E, soff, a.row_token, a.row_slot, a.row_gate);
+      }
+      return;
+    }
+  }
+  if (!scatter) return;
   if constexpr (KM <= 4) {
     scatter_block_few<KP>(b, mine, wsel, a.T, a.k, E, nbits, sbase, skept, soff, a.shared,
                           a.row_token, a.row_slot, a.inv, a.row_gate);
-  } else if (a.k <= kIdsK) {
-    stage_ids(b, a.topk_idx, a.topk_w, a.T, a.k, sids, sgts);
-    scatter_block_any(b, sids, kIdsK + 1, sgts, a.T, a.k, E, nbits, sbase, skept, soff, a.shared,
-                      a.row_token, a.row_slot, a.inv, a.row_gate);
   } else {
     const int64_t f0 = static_cast<int64_t>(b) * kGateTokens * a.k;
     scatter_block_any(b, a.topk_idx + f0, a.k, a.topk_w + f0, a.T, a.k, E, nbits, sbase, skept,
@@ -440,9 +472,9 @@ hipError_t launch_dispatch(int64_t T, int E, int k, int capacity, int shared, in
   if (nb > 0) {
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
-#define MOE_SCAT(KM)                                                                          \
-  dispatch_scatter_kernel<KM><<<nb, 64, 0, st>>>(topk_idx, T, k, E, nbits, base, kept, offsets, \
-                                                 shared, row_token, row_slot, inv)
+#define MOE_SCAT(KM)                                                                 \
+  dispatch_scatter_kernel<KM><<<nb, KM > 4 && k <= kIdsK ? 64 * k : 64, 0, st>>>(     \
+      topk_idx, T, k, E, nbits, base, kept, offsets, shared, row_token, row_slot, inv)
     if (k <= 1) MOE_SCAT(1);
     else if (k <= 2) MOE_SCAT(2);
     else if (k <= 4) MOE_SCAT(4);

@@ -149,6 +149,10 @@ def test_route_stage(shape):
 @pytest.mark.parametrize("shape", [S("disp_cap", T=1000, E=16, k=3, capacity=150,
                                      router_bias="zipf1.1", Fs=64),
                                    S("disp_plain", T=333, E=5, k=2),
+                                   # 5-8 slots: one wave per slot in the scatter
+                                   S("disp_k8_shared", T=700, E=40, k=8, Fs=64),
+                                   S("disp_k5_cap", T=900, E=24, k=5, capacity=120,
+                                     router_bias="zipf1.1"),
                                    S("disp_e1024", T=70, d=64, E=1023, k=32, Fs=8,
                                      router_bias="none")],
                          ids=lambda s: s.name)
